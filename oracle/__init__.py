@@ -1,0 +1,226 @@
+"""CPU oracle for the accelerator linear layer -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the C-ABI library and
+its Python binding in ``quantized_weight_matmul_amd``) never imports, links or
+calls it, and the two share no code.
+
+What it computes: y[t][n_out] = x[t][n_in] * W^T (oxinfer 0.0.0 ``src/gpu.rs``
+page, doc comment of ``struct Job``) for W in one of the storage formats of
+``enum WeightRef`` on that page: each weight element is decoded to the f32
+value it denotes, products are formed exactly in f64 and summed in f64 in
+increasing k, and the sum is rounded once to f32.  ``bound`` is
+sum_k |x*w| in f64; the acceptance test is |y - y_ref| <= 4e-3 * bound per
+output element.  The arithmetic lives in ``il_oracle.c`` (plain C, gcc -O2);
+this module only marshals numpy arrays.
+
+Pins live in ``tests/oracle_pins.py`` (run by ``tests/test_oracle_pins.py``):
+exhaustive bf16 / f16 decode against library casts; exact-rational brute
+force on tiny shapes; closed forms (one-hot / identity W selects x columns,
+x = 1 gives row sums, all-zero codes give 0); Q8/Q4 round trips on
+representable values; hand-derived fixtures under ``tests/golden/``; numpy
+float64 matmul at full shapes.  ``tests/test_oracle_mutants.py`` plants
+mistakes in copies of ``il_oracle.c`` and checks that the pins catch each.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+BF16, Q8, Q4 = 0, 1, 2
+BLOCK = 32
+TOL = 4e-3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "il_oracle.c")
+SO = os.path.join(_HERE, "liboracle.so")
+
+_i64 = ctypes.c_int64
+_ptr = ctypes.c_void_p
+
+
+def compile_oracle(src: str, out: str, verbose: bool = False) -> str:
+    """gcc -O2 (no fast-math, no intrinsics) -fopenmp -> shared library."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
+           src, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = False, verbose: bool = False) -> str:
+    if force or not os.path.exists(SO) or os.path.getmtime(SO) < os.path.getmtime(SRC):
+        compile_oracle(SRC, SO, verbose)
+    return SO
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_ptr)
+
+
+def weight_bytes(fmt: int, n_out: int, n_in: int) -> int:
+    """Host-format size; -1 for a bad format or shape (mirrors the C rule)."""
+    if n_out <= 0 or n_in <= 0:
+        return -1
+    if fmt == BF16:
+        return 2 * n_out * n_in
+    if n_in % BLOCK:
+        return -1
+    if fmt == Q8:
+        return 36 * n_out * (n_in // BLOCK)
+    if fmt == Q4:
+        return 18 * n_out * (n_in // BLOCK)
+    return -1
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library (the real one, or a planted
+    mutant in the mutation tests)."""
+
+    def __init__(self, so_path: str):
+        lib = ctypes.CDLL(so_path)
+        lib.orc_bf16_value.restype = ctypes.c_double
+        lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
+        lib.orc_f16_value.restype = ctypes.c_double
+        lib.orc_f16_value.argtypes = [ctypes.c_uint16]
+        lib.orc_weight_bytes.restype = _i64
+        lib.orc_weight_bytes.argtypes = [ctypes.c_int, _i64, _i64]
+        lib.orc_dequant_row.restype = ctypes.c_int
+        lib.orc_dequant_row.argtypes = [_ptr, ctypes.c_int, _i64, _i64, _ptr]
+        lib.orc_matmul_rows.restype = ctypes.c_int
+        lib.orc_matmul_rows.argtypes = [_ptr, _i64, _i64, _ptr, ctypes.c_int, _i64, _i64, _i64,
+                                        _ptr, _ptr, ctypes.c_int]
+        lib.orc_matmul_points.restype = ctypes.c_int
+        lib.orc_matmul_points.argtypes = [_ptr, _i64, _i64, _ptr, ctypes.c_int, _i64, _i64,
+                                          _ptr, _ptr, _ptr, _ptr, ctypes.c_int]
+        lib.orc_check.restype = _i64
+        lib.orc_check.argtypes = [_ptr, _ptr, _ptr, _i64, ctypes.c_double,
+                                  ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]
+        self.lib = lib
+        self.path = so_path
+
+    # -- helpers ---------------------------------------------------------
+    def _host_weight(self, weight, fmt: int, n_out: int, n_in: int) -> np.ndarray:
+        w = np.ascontiguousarray(weight)
+        need = int(self.lib.orc_weight_bytes(fmt, n_out, n_in))
+        if need < 0:
+            raise ValueError("bad format or shape")
+        if w.nbytes != need:
+            raise ValueError(f"weight holds {w.nbytes} bytes, format needs {need}")
+        return w
+
+    # -- API -------------------------------------------------------------
+    def bf16_value(self, bits) -> np.ndarray:
+        """bfloat16 bit patterns -> float64, decoded from the format definition."""
+        b = np.asarray(bits, dtype=np.uint16)
+        f = self.lib.orc_bf16_value
+        return np.array([f(int(v)) for v in b.ravel()], dtype=np.float64).reshape(b.shape)
+
+    def f16_value(self, bits) -> np.ndarray:
+        """IEEE binary16 bit patterns -> float64, decoded from the format definition."""
+        b = np.asarray(bits, dtype=np.uint16)
+        f = self.lib.orc_f16_value
+        return np.array([f(int(v)) for v in b.ravel()], dtype=np.float64).reshape(b.shape)
+
+    def dequant(self, weight, fmt: int, n_out: int, n_in: int, rows=None) -> np.ndarray:
+        """Decoded f32 weight rows, [len(rows), n_in] (all rows by default)."""
+        w = self._host_weight(weight, fmt, n_out, n_in)
+        rows = range(n_out) if rows is None else rows
+        out = np.empty((len(rows), n_in), dtype=np.float32)
+        for j, r in enumerate(rows):
+            if not 0 <= r < n_out:
+                raise IndexError(r)
+            if self.lib.orc_dequant_row(_p(w), fmt, n_in, int(r), _p(out[j])) != 0:
+                raise ValueError("dequant failed")
+        return out
+
+    def matmul(self, x: np.ndarray, weight, fmt: int, n_out: int, r0: int = 0,
+               r1: int | None = None, threads: int = 0):
+        """(y_ref [t, r1-r0] f32, bound [t, r1-r0] f64) for output rows [r0, r1)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        if x.ndim != 2:
+            raise ValueError("x must be [t, n_in]")
+        t, n_in = x.shape
+        w = self._host_weight(weight, fmt, n_out, n_in)
+        r1 = n_out if r1 is None else r1
+        y = np.empty((t, r1 - r0), dtype=np.float32)
+        bound = np.empty((t, r1 - r0), dtype=np.float64)
+        if self.lib.orc_matmul_rows(_p(x), t, n_in, _p(w), fmt, n_out, r0, r1, _p(y), _p(bound),
+                                    int(threads)) != 0:
+            raise ValueError("oracle matmul failed")
+        return y, bound
+
+    def matmul_points(self, x: np.ndarray, weight, fmt: int, n_out: int, ii, rr,
+                      threads: int = 0):
+        """(y_ref[p], bound[p]) for the outputs (ii[p], rr[p])."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        t, n_in = x.shape
+        w = self._host_weight(weight, fmt, n_out, n_in)
+        ii = np.ascontiguousarray(ii, dtype=np.int64)
+        rr = np.ascontiguousarray(rr, dtype=np.int64)
+        if ii.shape != rr.shape:
+            raise ValueError("ii and rr differ in shape")
+        y = np.empty(ii.shape, dtype=np.float32)
+        bound = np.empty(ii.shape, dtype=np.float64)
+        if self.lib.orc_matmul_points(_p(x), t, n_in, _p(w), fmt, n_out, ii.size, _p(ii),
+                                      _p(rr), _p(y), _p(bound), int(threads)) != 0:
+            raise ValueError("oracle matmul_points failed")
+        return y, bound
+
+    def check(self, y, y_ref, bound, tol: float = TOL) -> dict:
+        """Element-wise |y - y_ref| <= tol * bound (NaN/Inf in y fail)."""
+        y = np.ascontiguousarray(y, dtype=np.float32)
+        y_ref = np.ascontiguousarray(y_ref, dtype=np.float32)
+        bound = np.ascontiguousarray(bound, dtype=np.float64)
+        if not (y.shape == y_ref.shape == bound.shape):
+            raise ValueError(f"shape mismatch {y.shape} {y_ref.shape} {bound.shape}")
+        first = _i64(-1)
+        worst = ctypes.c_double(0.0)
+        bad = self.lib.orc_check(_p(y), _p(y_ref), _p(bound), y.size, tol, ctypes.byref(first),
+                                 ctypes.byref(worst))
+        return {"n": int(y.size), "bad": int(bad), "first_bad": int(first.value),
+                "worst": float(worst.value), "ok": bad == 0}
+
+
+_default = None
+_lock = threading.Lock()
+
+
+def default() -> Oracle:
+    global _default
+    with _lock:
+        if _default is None:
+            build()
+            _default = Oracle(SO)
+    return _default
+
+
+def bf16_value(bits):
+    return default().bf16_value(bits)
+
+
+def f16_value(bits):
+    return default().f16_value(bits)
+
+
+def dequant(weight, fmt, n_out, n_in, rows=None):
+    return default().dequant(weight, fmt, n_out, n_in, rows)
+
+
+def matmul(x, weight, fmt, n_out, r0=0, r1=None, threads=0):
+    return default().matmul(x, weight, fmt, n_out, r0, r1, threads)
+
+
+def matmul_points(x, weight, fmt, n_out, ii, rr, threads=0):
+    return default().matmul_points(x, weight, fmt, n_out, ii, rr, threads)
+
+
+def check(y, y_ref, bound, tol=TOL):
+    return default().check(y, y_ref, bound, tol)

@@ -1,0 +1,275 @@
+/*
+ * il_oracle.c -- TEST INFRASTRUCTURE, not part of the product.
+ *
+ * A plain, slow, obviously correct CPU implementation of the accelerator
+ * linear layer: a batch of matmuls over one shared f32 input,
+ *
+ *     y[t][n_out] = x[t][n_in] * W^T                       (1)
+ *
+ * as stated in the doc comment of `struct Job` on the oxinfer 0.0.0
+ * `src/gpu.rs` page, with every weight W `[n_out, n_in]` row-major in one of
+ * the three storage formats of `enum WeightRef` on the same page (Bf16 as raw
+ * u16 bits, Q8, Q4).
+ *
+ * Only the test suite, the package's smoke check and the benchmark's CPU
+ * baseline leg may load this file's library.  Nothing in the product path
+ * links, imports or calls it, and it shares no source with the GPU path.
+ *
+ * Method: dequantise, then multiply.  Each weight element is decoded to the
+ * f32 value it denotes; each output is the sum over k of the exact f64
+ * products x*w in increasing k, rounded once to f32.  Beside it, the bound
+ * sum_k |x*w| (f64) that the tolerance check scales with.
+ *
+ * Host formats (the pages import QMatrix / Q4Matrix without showing their
+ * layout; these are this library's readings, listed with the others in the
+ * design notes):
+ *   BF16: uint16_t[n_out][n_in], raw bfloat16 bits.
+ *   Q8  : n_out * (n_in/32) packed 36-byte blocks, row-major by (row, block),
+ *         each { float32 scale (little-endian); int8 q[32]; };
+ *         w = (float)q * scale   -- one f32 multiply, round-to-nearest-even.
+ *   Q4  : n_out * (n_in/32) packed 18-byte blocks, row-major by (row, block),
+ *         each { uint16 f16 scale bits (little-endian); uint8 qs[16]; },
+ *         qs[j] holds element 2j in its low nibble, element 2j+1 in its high;
+ *         w = (code - 8) * f16(scale)  -- exact in f32.
+ *
+ * Built with plain `gcc -O2` (no -ffast-math, no intrinsics).  OpenMP, when
+ * enabled, splits rows between threads; every output is still summed
+ * serially, so the result does not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_BF16 = 0, ORC_Q8 = 1, ORC_Q4 = 2 };
+enum { ORC_BLOCK = 32, ORC_Q8_BLOCK_BYTES = 36, ORC_Q4_BLOCK_BYTES = 18 };
+
+/* bfloat16 -> double, from the format's definition: 1 sign bit, 8 exponent
+ * bits (bias 127), 7 fraction bits; exponent 0 is subnormal (f * 2^-133),
+ * exponent 255 is Inf (f == 0) or NaN. */
+double orc_bf16_value(uint16_t bits)
+{
+    int sign = bits >> 15;
+    int e = (bits >> 7) & 0xFF;
+    int f = bits & 0x7F;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -126 - 7);
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + f), e - 127 - 7);
+    return sign ? -v : v;
+}
+
+/* IEEE 754 binary16 -> double, from its definition: 1 sign bit, 5 exponent
+ * bits (bias 15), 10 fraction bits; exponent 0 is subnormal (f * 2^-24),
+ * exponent 31 is Inf (f == 0) or NaN. */
+double orc_f16_value(uint16_t bits)
+{
+    int sign = bits >> 15;
+    int e = (bits >> 10) & 0x1F;
+    int f = bits & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 15 - 10);
+    return sign ? -v : v;
+}
+
+static uint16_t rd_u16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+static float rd_f32(const uint8_t *p)
+{
+    uint32_t u = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) |
+                 ((uint32_t)p[3] << 24);
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Size in bytes of one weight in its host format (the storage that
+ * `WeightRef::bytes` counts); -1 on a bad format or shape. */
+int64_t orc_weight_bytes(int fmt, int64_t n_out, int64_t n_in)
+{
+    if (n_out <= 0 || n_in <= 0) return -1;
+    if (fmt == ORC_BF16) return n_out * n_in * 2;
+    if (n_in % ORC_BLOCK) return -1;
+    if (fmt == ORC_Q8) return n_out * (n_in / ORC_BLOCK) * ORC_Q8_BLOCK_BYTES;
+    if (fmt == ORC_Q4) return n_out * (n_in / ORC_BLOCK) * ORC_Q4_BLOCK_BYTES;
+    return -1;
+}
+
+/* Decode row `r` of a host-format weight to f32 values w[0..n_in). */
+int orc_dequant_row(const void *weight, int fmt, int64_t n_in, int64_t r, float *w)
+{
+    const uint8_t *base = (const uint8_t *)weight;
+    if (fmt == ORC_BF16) {
+        const uint8_t *row = base + (size_t)r * (size_t)n_in * 2;
+        for (int64_t k = 0; k < n_in; ++k)
+            w[k] = (float)orc_bf16_value(rd_u16(row + 2 * k));
+        return 0;
+    }
+    if (n_in % ORC_BLOCK) return -1;
+    int64_t nb = n_in / ORC_BLOCK;
+    if (fmt == ORC_Q8) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = base + ((size_t)r * (size_t)nb + (size_t)b) * ORC_Q8_BLOCK_BYTES;
+            float scale = rd_f32(blk);
+            for (int e = 0; e < ORC_BLOCK; ++e) {
+                float q = (float)(int8_t)blk[4 + e];
+                w[b * ORC_BLOCK + e] = q * scale; /* one f32 multiply */
+            }
+        }
+        return 0;
+    }
+    if (fmt == ORC_Q4) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = base + ((size_t)r * (size_t)nb + (size_t)b) * ORC_Q4_BLOCK_BYTES;
+            double scale = orc_f16_value(rd_u16(blk));
+            for (int e = 0; e < ORC_BLOCK; ++e) {
+                uint8_t byte = blk[2 + e / 2];
+                int code = (e % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+                w[b * ORC_BLOCK + e] = (float)((double)(code - 8) * scale);
+            }
+        }
+        return 0;
+    }
+    return -1;
+}
+
+/* Equation (1) for output rows [r0, r1) of one weight.  y and bound are
+ * [t][r1 - r0] row-major: y[i][j] = (float) sum_k x[i][k] * w[r0 + j][k] with
+ * f64 products and an f64 running sum in increasing k; bound[i][j] =
+ * sum_k |x[i][k] * w[r0 + j][k]| in f64.  Returns 0, or -1 on bad arguments. */
+int orc_matmul_rows(const float *x, int64_t t, int64_t n_in, const void *weight, int fmt,
+                    int64_t n_out, int64_t r0, int64_t r1, float *y, double *bound,
+                    int nthreads)
+{
+    if (t < 0 || n_in <= 0 || r0 < 0 || r1 > n_out || r0 > r1) return -1;
+    if (orc_weight_bytes(fmt, n_out, n_in) < 0) return -1;
+    int64_t nr = r1 - r0;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+#endif
+    {
+        float *w = (float *)malloc((size_t)n_in * sizeof(float));
+        if (!w) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+            for (int64_t j = 0; j < nr; ++j) {
+                if (orc_dequant_row(weight, fmt, n_in, r0 + j, w)) {
+                    failed = 1;
+                    continue;
+                }
+                for (int64_t i = 0; i < t; ++i) {
+                    const float *xi = x + (size_t)i * (size_t)n_in;
+                    double acc = 0.0, mag = 0.0;
+                    for (int64_t k = 0; k < n_in; ++k) {
+                        double p = (double)xi[k] * (double)w[k];
+                        acc += p;
+                        mag += fabs(p);
+                    }
+                    y[(size_t)i * (size_t)nr + (size_t)j] = (float)acc;
+                    bound[(size_t)i * (size_t)nr + (size_t)j] = mag;
+                }
+            }
+            free(w);
+        }
+    }
+    (void)nthreads;
+    return failed ? -1 : 0;
+}
+
+/* Equation (1) at chosen points only: y[p] = output (ii[p], rr[p]).  Used to
+ * check full-size GPU results on a sample the oracle computes one by one. */
+int orc_matmul_points(const float *x, int64_t t, int64_t n_in, const void *weight, int fmt,
+                      int64_t n_out, int64_t n_pts, const int64_t *ii, const int64_t *rr,
+                      float *y, double *bound, int nthreads)
+{
+    if (t < 0 || n_in <= 0 || n_pts < 0) return -1;
+    if (orc_weight_bytes(fmt, n_out, n_in) < 0) return -1;
+    for (int64_t p = 0; p < n_pts; ++p)
+        if (ii[p] < 0 || ii[p] >= t || rr[p] < 0 || rr[p] >= n_out) return -1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+#endif
+    {
+        float *w = (float *)malloc((size_t)n_in * sizeof(float));
+        if (!w) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+            for (int64_t p = 0; p < n_pts; ++p) {
+                if (orc_dequant_row(weight, fmt, n_in, rr[p], w)) {
+                    failed = 1;
+                    continue;
+                }
+                const float *xi = x + (size_t)ii[p] * (size_t)n_in;
+                double acc = 0.0, mag = 0.0;
+                for (int64_t k = 0; k < n_in; ++k) {
+                    double prod = (double)xi[k] * (double)w[k];
+                    acc += prod;
+                    mag += fabs(prod);
+                }
+                y[p] = (float)acc;
+                bound[p] = mag;
+            }
+            free(w);
+        }
+    }
+    (void)nthreads;
+    return failed ? -1 : 0;
+}
+
+/* The acceptance test on n outputs: |y - y_ref| <= tol * bound, element by
+ * element; a NaN or Inf in y always fails, and bound == 0 demands y == y_ref.
+ * Returns the number of failing elements; *first_bad is the first failing
+ * index (-1 if none) and *worst the largest |y - y_ref| / bound seen (an
+ * element with bound == 0 and y != y_ref counts as +Inf). */
+int64_t orc_check(const float *y, const float *y_ref, const double *bound, int64_t n,
+                  double tol, int64_t *first_bad, double *worst)
+{
+    int64_t bad = 0;
+    double wmax = 0.0;
+    if (first_bad) *first_bad = -1;
+    for (int64_t e = 0; e < n; ++e) {
+        double got = (double)y[e];
+        double want = (double)y_ref[e];
+        double err = fabs(got - want);
+        double ratio;
+        int ok;
+        if (isnan(got) || isinf(got)) {
+            ok = 0;
+            ratio = INFINITY;
+        } else if (bound[e] == 0.0) {
+            ok = (err == 0.0);
+            ratio = ok ? 0.0 : INFINITY;
+        } else {
+            ratio = err / bound[e];
+            ok = (err <= tol * bound[e]);
+        }
+        if (!(ratio <= wmax)) wmax = ratio;
+        if (!ok) {
+            if (bad == 0 && first_bad) *first_bad = e;
+            ++bad;
+        }
+    }
+    if (worst) *worst = wmax;
+    return bad;
+}

@@ -1,0 +1,389 @@
+"""Pins for the CPU oracle: checks of ``oracle`` against things other than itself.
+
+Every function takes an ``oracle.Oracle`` (the real library, or a planted
+mutant in ``test_oracle_mutants.py``) and raises AssertionError when the
+oracle disagrees with:
+
+* library casts (torch bfloat16, numpy float16/float32) on every bit pattern;
+* exact rational arithmetic (``fractions.Fraction``) on tiny shapes;
+* closed forms: one-hot / identity W selects columns of x, x = 1 gives row
+  sums, all-zero codes give 0, Q8/Q4 codes round-trip through dequantisation;
+* hand-derived fixtures in ``tests/golden`` (the storage-format readings);
+* numpy float64 ``x @ W.T`` on library-decoded weights at the workloads' shapes.
+
+The method pinned is y[t][n_out] = x[t][n_in] * W^T of the oxinfer 0.0.0
+``src/gpu.rs`` page (doc comment of ``struct Job``), with W stored in one of
+the formats of ``enum WeightRef`` on that page.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle as O_mod
+from quantized_weight_matmul_amd import workloads as wl
+
+BF16, Q8, Q4 = O_mod.BF16, O_mod.Q8, O_mod.Q4
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+FMTS = {"bf16": BF16, "q8": Q8, "q4": Q4}
+
+
+# ------------------------------------------------------------ library decodes
+def lib_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bits -> float64 via torch's bfloat16 dtype."""
+    import torch
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def lib_f16(bits: np.ndarray) -> np.ndarray:
+    """binary16 bits -> float64 via numpy's float16 dtype."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def lib_q8_values(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float32(q) * float32(scale) with numpy's IEEE f32 multiply."""
+    n_out, n_in = codes.shape
+    s = np.repeat(scales.astype(np.float32), wl.BLOCK, axis=1)
+    return codes.astype(np.float32) * s
+
+
+def lib_q4_values(codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    s = np.repeat(lib_f16(scale_bits), wl.BLOCK, axis=1)
+    return ((codes.astype(np.float64) - 8.0) * s).astype(np.float32)
+
+
+def _nan_equal(a, b):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    both_nan = np.isnan(a) & np.isnan(b)
+    same = (a == b) & (np.signbit(a) == np.signbit(b))
+    return bool(np.all(both_nan | same))
+
+
+# --------------------------------------------------------------- decoders
+def pin_bf16_exhaustive(O):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    assert _nan_equal(O.bf16_value(bits), lib_bf16(bits)), "bf16 decode disagrees with torch"
+
+
+def pin_f16_exhaustive(O):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    assert _nan_equal(O.f16_value(bits), lib_f16(bits)), "f16 decode disagrees with numpy"
+
+
+# ----------------------------------------------------------------- goldens
+def load_golden(path):
+    fields = {}
+    wb = []
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, _, val = line.partition(" ")
+            if key == "weight_bytes":
+                wb.append(val.replace(" ", ""))
+            else:
+                fields[key] = val.strip()
+    fmt = FMTS[fields["fmt"]]
+    n_out, n_in = int(fields["n_out"]), int(fields["n_in"])
+    if fmt == BF16:
+        weight = np.array([int(h, 16) for h in fields["weight_u16"].split()], dtype=np.uint16)
+    else:
+        weight = np.frombuffer(bytes.fromhex("".join(wb)), dtype=np.uint8).copy()
+    if fields["x"] == "ones":
+        x = np.ones((1, n_in), dtype=np.float32)
+    else:
+        x = np.array([[float(v) for v in row.split(",")] for row in fields["x"].split(";")],
+                     dtype=np.float32)
+    y = np.array([[float(v) for v in row.split(",")] for row in fields["y"].split(";")])
+    closed = np.array(eval(fields["closed_form"], {"__builtins__": {}},
+                           {"sum": sum, "range": range}), dtype=np.float64)
+    return fmt, n_out, n_in, weight, x, y, closed
+
+
+def golden_files():
+    return sorted(f for f in os.listdir(GOLDEN) if f.endswith(".txt"))
+
+
+def pin_goldens(O):
+    files = golden_files()
+    assert len(files) >= 7
+    for name in files:
+        fmt, n_out, n_in, weight, x, y, closed = load_golden(os.path.join(GOLDEN, name))
+        assert np.array_equal(y.ravel(), closed), f"{name}: stored y is not its closed form"
+        got, bound = O.matmul(x, weight, fmt, n_out)
+        assert got.shape == y.shape, name
+        assert np.array_equal(got.astype(np.float64), y), f"{name}: oracle {got} != {y}"
+
+
+# ------------------------------------------------------------ closed forms
+def _onehot_weight(fmt, n_out, n_in, cols):
+    """W[r][cols[r]] = 1, every other element 0, in each host format; built
+    from the encodings of 1 and 0 directly (no decoding involved)."""
+    if fmt == BF16:
+        w = np.zeros((n_out, n_in), dtype=np.uint16)
+        w[np.arange(n_out), cols] = 0x3F80  # 1.0
+        return w
+    nb = n_in // wl.BLOCK
+    if fmt == Q8:
+        codes = np.zeros((n_out, n_in), dtype=np.int8)
+        codes[np.arange(n_out), cols] = 64
+        scales = np.full((n_out, nb), 2.0 ** -6, dtype=np.float32)  # 64 * 2^-6 = 1
+        return wl.encode_q8(codes, scales)
+    codes = np.full((n_out, n_in), 8, dtype=np.uint8)  # code 8 -> value 0
+    codes[np.arange(n_out), cols] = 9  # (9 - 8) * 1.0
+    return wl.encode_q4(codes, np.full((n_out, nb), 0x3C00, dtype=np.uint16))
+
+
+def pin_onehot(O):
+    rng = np.random.default_rng(7)
+    n_out, n_in, t = 7, 64, 3
+    x = rng.standard_normal((t, n_in)).astype(np.float32)
+    for fmt in (BF16, Q8, Q4):
+        cols = rng.integers(0, n_in, n_out)
+        w = _onehot_weight(fmt, n_out, n_in, cols)
+        y, bound = O.matmul(x, w, fmt, n_out)
+        assert np.array_equal(y, x[:, cols]), f"one-hot fmt {fmt}"
+        assert np.array_equal(bound, np.abs(x[:, cols]).astype(np.float64)), f"one-hot bound {fmt}"
+
+
+def pin_identity(O):
+    rng = np.random.default_rng(8)
+    n = 64
+    x = rng.standard_normal((2, n)).astype(np.float32)
+    for fmt in (BF16, Q8, Q4):
+        y, _ = O.matmul(x, _onehot_weight(fmt, n, n, np.arange(n)), fmt, n)
+        assert np.array_equal(y, x), f"identity fmt {fmt}"
+
+
+def pin_row_sums(O):
+    """x = 1 gives y[r] = sum_k w[r][k]; codes chosen so the sums are closed forms."""
+    n_out, n_in = 5, 96
+    nb = n_in // wl.BLOCK
+    x = np.ones((1, n_in), dtype=np.float32)
+    k = np.arange(n_in)
+    # Q4: code k % 16 in every row; per block sum(code - 8) = 2 * (-8) = -16.
+    # Row r has scale 2^-r (f16 bits (15 - r) << 10), so y[r] = -16 * nb * 2^-r.
+    codes = np.tile((k % 16).astype(np.uint8), (n_out, 1))
+    sbits = np.array([[(15 - r) << 10] * nb for r in range(n_out)], dtype=np.uint16)
+    y, _ = O.matmul(x, wl.encode_q4(codes, sbits), Q4, n_out)
+    assert np.array_equal(y[0], np.array([-16.0 * nb * 2.0 ** -r for r in range(n_out)])), "q4 sums"
+    # Q8: code (k % 32) - 16 -> per block sum = -16; row scale r + 1 -> y = -16 nb (r + 1).
+    codes8 = np.tile(((k % 32) - 16).astype(np.int8), (n_out, 1))
+    sc = np.array([[r + 1.0] * nb for r in range(n_out)], dtype=np.float32)
+    y, _ = O.matmul(x, wl.encode_q8(codes8, sc), Q8, n_out)
+    assert np.array_equal(y[0], np.array([-16.0 * nb * (r + 1) for r in range(n_out)])), "q8 sums"
+    # bf16: w[r][k] = 2^-(k % 4) * (+1 if r even else -1); row sum = +-nb*32/4 * (1+.5+.25+.125)
+    vals = np.array([0x3F80, 0x3F00, 0x3E80, 0x3E00], dtype=np.uint16)  # 1, 1/2, 1/4, 1/8
+    w = np.tile(vals[k % 4], (n_out, 1))
+    w[1::2] |= 0x8000
+    y, _ = O.matmul(x, w, BF16, n_out)
+    want = np.array([(n_in // 4) * 1.875 * (1 if r % 2 == 0 else -1) for r in range(n_out)])
+    assert np.array_equal(y[0], want), "bf16 sums"
+
+
+def pin_zero_codes(O):
+    rng = np.random.default_rng(9)
+    n_out, n_in = 4, 64
+    nb = n_in // wl.BLOCK
+    x = rng.standard_normal((3, n_in)).astype(np.float32)
+    z4 = wl.encode_q4(np.full((n_out, n_in), 8, np.uint8),
+                      rng.integers(0x1000, 0x5000, (n_out, nb)).astype(np.uint16))
+    z8 = wl.encode_q8(np.zeros((n_out, n_in), np.int8),
+                      rng.uniform(0.1, 10, (n_out, nb)).astype(np.float32))
+    for fmt, w in ((Q4, z4), (Q8, z8)):
+        y, bound = O.matmul(x, w, fmt, n_out)
+        assert np.all(y == 0) and np.all(bound == 0), f"zero codes fmt {fmt}"
+
+
+def pin_roundtrip_q8(O):
+    """Every int8 code survives dequantisation: rint(w / s) == q, and for
+    power-of-two scales w == q * s exactly."""
+    codes_row = np.arange(-128, 128, dtype=np.int16).astype(np.int8)  # 256 = 8 blocks
+    pow2 = [2.0 ** e for e in range(-14, 1)]
+    rnd = list(np.random.default_rng(10).uniform(1e-4, 1e-3, 8))
+    scales = np.array(pow2 + rnd, dtype=np.float32)
+    n_out, n_in = len(scales), codes_row.size
+    codes = np.tile(codes_row, (n_out, 1))
+    w = O.dequant(wl.encode_q8(codes, np.repeat(scales[:, None], n_in // 32, 1)), Q8, n_out, n_in)
+    q_back = np.rint(w.astype(np.float64) / scales[:, None].astype(np.float64))
+    assert np.array_equal(q_back, codes.astype(np.float64)), "Q8 codes do not round-trip"
+    for r, e in enumerate(range(-14, 1)):
+        assert np.array_equal(w[r], np.ldexp(codes_row.astype(np.float64), e)), "Q8 pow2 scale"
+
+
+def pin_roundtrip_q4(O):
+    """Every 4-bit code survives: w / s + 8 == code exactly (f16 scales)."""
+    codes_row = np.tile(np.arange(16, dtype=np.uint8), 2)  # one block, each code twice
+    sbits = [(e + 15) << 10 for e in range(-14, 2)]  # powers of two 2^-14 .. 2^1
+    sbits += list(np.random.default_rng(11).integers(0x1400, 0x2400, 8))
+    sbits += [0x0001, 0x03FF]  # subnormal scales
+    sbits = np.array(sbits, dtype=np.uint16)
+    n_out = len(sbits)
+    codes = np.tile(codes_row, (n_out, 1))
+    w = O.dequant(wl.encode_q4(codes, sbits[:, None]), Q4, n_out, 32)
+    s = lib_f16(sbits)[:, None]
+    assert np.array_equal(w.astype(np.float64) / s + 8.0, codes.astype(np.float64)), "Q4 round trip"
+
+
+# -------------------------------------------------------------- brute force
+def _exact_values(fmt, parts):
+    """Exact rationals of every weight element, from library-decoded values."""
+    if fmt == BF16:
+        return [[Fraction(float(v)) for v in row] for row in lib_bf16(parts)]
+    if fmt == Q8:
+        return [[Fraction(float(v)) for v in row] for row in lib_q8_values(*parts)]
+    codes, sbits = parts
+    s = lib_f16(sbits)
+    return [[(int(c) - 8) * Fraction(float(s[r][k // 32])) for k, c in enumerate(row)]
+            for r, row in enumerate(codes)]
+
+
+def _random_parts(fmt, rng, n_out, n_in):
+    nb = n_in // 32
+    if fmt == BF16:
+        return wl.f32_to_bf16_bits(rng.standard_normal((n_out, n_in)).astype(np.float32))
+    if fmt == Q8:
+        return (rng.integers(-128, 128, (n_out, n_in)).astype(np.int8),
+                rng.uniform(1e-3, 1.0, (n_out, nb)).astype(np.float32))
+    return (rng.integers(0, 16, (n_out, n_in)).astype(np.uint8),
+            rng.uniform(1e-3, 1.0, (n_out, nb)).astype(np.float16).view(np.uint16))
+
+
+def _encode(fmt, parts):
+    if fmt == BF16:
+        return parts
+    return wl.encode_q8(*parts) if fmt == Q8 else wl.encode_q4(*parts)
+
+
+def _f32_neighbours(v: float):
+    f = np.float32(v)
+    return {f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))}
+
+
+def pin_bruteforce(O):
+    """Exact rational result on tiny shapes: the oracle is within one f32 ulp
+    of the correctly rounded value, and its bound matches sum |x w|."""
+    rng = np.random.default_rng(12)
+    for fmt in (BF16, Q8, Q4):
+        for t, n_out, n_in in ((1, 1, 32), (2, 3, 32), (3, 5, 64), (3, 4, 64)):
+            parts = _random_parts(fmt, rng, n_out, n_in)
+            x = rng.standard_normal((t, n_in)).astype(np.float32)
+            W = _exact_values(fmt, parts)
+            y, bound = O.matmul(x, _encode(fmt, parts), fmt, n_out)
+            for i in range(t):
+                xi = [Fraction(float(v)) for v in x[i]]
+                for r in range(n_out):
+                    exact = sum(a * b for a, b in zip(xi, W[r]))
+                    mag = sum(abs(a * b) for a, b in zip(xi, W[r]))
+                    assert y[i, r] in _f32_neighbours(float(exact)), (
+                        f"fmt {fmt} ({i},{r}): oracle {y[i, r]!r} vs exact {float(exact)!r}")
+                    assert math.isclose(bound[i, r], float(mag), rel_tol=1e-12), "bound"
+
+
+# --------------------------------------------------------- library routine
+def pin_numpy_matmul(O, rows_per_job: int = 64):
+    """numpy float64 x @ W.T on library-decoded weights, at the workloads'
+    shapes (row subsets of the large jobs keep the CPU time low)."""
+    seen = set()
+    for name, sub in wl.SUBMISSIONS.items():
+        x = wl.make_x(sub)
+        if sub.t > 8:
+            x = x[:16]
+        for j in sub.jobs:
+            if (sub.cfg, j.tensor_id) in seen:  # c4 repeats its weights at each t
+                continue
+            if sub.name.startswith("c4") and sub.t != 8:
+                continue
+            seen.add((sub.cfg, j.tensor_id))
+            n_rows = min(j.n_out, rows_per_job if sub.name != "c1" else j.n_out)
+            rows = np.unique(np.r_[0, j.n_out - 1,
+                                   np.random.default_rng(13).integers(0, j.n_out, n_rows)])
+            if j.fmt == BF16:
+                bits = wl.gen_bf16(sub.cfg, j.tensor_id, j.n_out, sub.n_in)
+                wd = lib_bf16(bits[rows])
+                host = bits
+            elif j.fmt == Q8:
+                codes, sc = wl.gen_q8_parts(sub.cfg, j.tensor_id, j.n_out, sub.n_in)
+                wd = lib_q8_values(codes[rows], sc[rows]).astype(np.float64)
+                host = wl.encode_q8(codes, sc)
+            else:
+                codes, sb = wl.gen_q4_parts(sub.cfg, j.tensor_id, j.n_out, sub.n_in)
+                wd = lib_q4_values(codes[rows], sb[rows]).astype(np.float64)
+                host = wl.encode_q4(codes, sb)
+            want = x.astype(np.float64) @ wd.T
+            mag = np.abs(x.astype(np.float64)) @ np.abs(wd).T
+            ii = np.repeat(np.arange(x.shape[0]), rows.size)
+            rr = np.tile(rows, x.shape[0])
+            got, bound = O.matmul_points(x, host, j.fmt, j.n_out, ii, rr)
+            got = got.reshape(x.shape[0], rows.size).astype(np.float64)
+            bound = bound.reshape(x.shape[0], rows.size)
+            err = np.abs(got - want)
+            # f32 rounding of the oracle's result plus summation-order noise
+            assert np.all(err <= np.abs(want) * 2.0 ** -23 + 1e-12 * mag), (
+                f"{name} job {j.tensor_id}: max err {err.max()}")
+            assert np.allclose(bound, mag, rtol=1e-12, atol=0), f"{name}: bound"
+
+
+# --------------------------------------------------------------- internals
+def pin_points_equal_rows(O):
+    rng = np.random.default_rng(14)
+    for fmt in (BF16, Q8, Q4):
+        parts = _random_parts(fmt, rng, 9, 96)
+        x = rng.standard_normal((3, 96)).astype(np.float32)
+        w = _encode(fmt, parts)
+        y, b = O.matmul(x, w, fmt, 9)
+        ii = np.repeat(np.arange(3), 9)
+        rr = np.tile(np.arange(9), 3)
+        yp, bp = O.matmul_points(x, w, fmt, 9, ii, rr)
+        assert np.array_equal(yp, y.ravel()) and np.array_equal(bp, b.ravel()), f"fmt {fmt}"
+        y2, b2 = O.matmul(x, w, fmt, 9, r0=3, r1=7)
+        assert np.array_equal(y2, y[:, 3:7]) and np.array_equal(b2, b[:, 3:7])
+
+
+def pin_thread_invariance(O):
+    rng = np.random.default_rng(15)
+    parts = _random_parts(Q4, rng, 64, 256)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    w = _encode(Q4, parts)
+    y1, b1 = O.matmul(x, w, Q4, 64, threads=1)
+    y8, b8 = O.matmul(x, w, Q4, 64, threads=8)
+    assert np.array_equal(y1, y8) and np.array_equal(b1, b8)
+
+
+def pin_check_rule(O):
+    yr = np.array([1.0, -2.0, 0.0, 5.0], np.float32)
+    bd = np.array([1.0, 2.0, 0.0, 10.0])
+    assert O.check(yr, yr, bd)["ok"]
+    ok_edge = yr + np.array([4e-3 * 0.999, 0, 0, 0], np.float32)
+    assert O.check(ok_edge, yr, bd)["ok"]
+    assert not O.check(yr + np.array([0, 0, 0, 0.05], np.float32), yr, bd)["ok"]
+    assert not O.check(np.array([1.0, -2.0, 1e-30, 5.0], np.float32), yr, bd)["ok"]
+    for bad in (np.nan, np.inf):
+        r = O.check(np.array([bad, -2.0, 0.0, 5.0], np.float32), yr, bd)
+        assert r["bad"] == 1 and r["first_bad"] == 0
+
+
+ALL_PINS = [
+    pin_bf16_exhaustive, pin_f16_exhaustive, pin_goldens, pin_onehot, pin_identity,
+    pin_row_sums, pin_zero_codes, pin_roundtrip_q8, pin_roundtrip_q4, pin_bruteforce,
+    pin_numpy_matmul, pin_points_equal_rows, pin_thread_invariance, pin_check_rule,
+]
+
+
+def run_all(O, quick: bool = False) -> list:
+    """Run every pin; returns the names of the pins that failed."""
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            if quick and pin is pin_numpy_matmul:
+                continue  # full-shape generation dominates the run time
+            pin(O)
+        except Exception as e:  # noqa: BLE001 -- a mutant may fail any way it likes
+            failed.append(f"{pin.__name__}: {type(e).__name__}: {str(e)[:200]}")
+    return failed
