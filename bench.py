@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the accelerator linear layer on one MI355X.
+
+One step = one il_matmul submission of the chosen workload (default: the
+fused bf16 decode, t = 1, three jobs [4096 | 1024 | 1024] x 4096 sharing one
+x).  Weights are uploaded once, off the timed path, as enough copies that one
+rotation through them exceeds 1 GiB, so every step streams its weights from
+HBM rather than from the 256 MiB last-level cache.  The K timed steps are
+captured in one HIP graph and replayed, bracketed by synchronisations, so the
+host's launch cost does not enter the per-step time.
+
+Prints one JSON line: the weight GB/s of the decode path (or TFLOP/s for the
+prefill workloads), a `roofline` object for the kernel (HIP-event timing of
+each launch on its stream, against the 8 TB/s HBM or 2.5 PFLOP/s bf16 MFMA
+peak) and a `cpu_baseline` object (the oracle on the host cores, on a bounded
+sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from quantized_weight_matmul_amd import workloads as wl  # noqa: E402
+
+METRIC = "weight GB/s (decode GEMV, % HBM peak); TFLOP/s (prefill GEMM, % MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk, dense
+ROTATE_BYTES = 1 << 30
+
+DESCRIPTIONS = {
+    "c1": "single bf16 job, t=1, [1024, 256]",
+    "c2": "fused bf16 decode, t=1, 3 jobs [4096|1024|1024] x 4096",
+    "c3a": "Q8 decode, t=1, 2 jobs [14336, 4096] (gate/up)",
+    "c3b": "Q8 decode, t=1, 1 job [4096, 14336] (down)",
+    "c4_t1": "Q4 verify, t=1, 2 jobs [17408, 5120]",
+    "c4_t2": "Q4 verify, t=2, 2 jobs [17408, 5120]",
+    "c4_t4": "Q4 verify, t=4, 2 jobs [17408, 5120]",
+    "c4_t8": "Q4 verify, t=8, 2 jobs [17408, 5120]",
+    "c5a": "bf16 prefill, t=2048, 2 jobs [4096|14336] x 4096",
+    "c5b": "Q4 prefill, t=512, 1 job [14336, 4096]",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(sub: wl.Submission, x, weights, budget_s: float) -> dict:
+    """The oracle, as it stands, on the host cores: a bounded sample of the
+    same workload (whole submissions for decode; a slice of x's rows for
+    prefill), scaled to the metric's unit."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    decode = sub.t <= 8
+    xs = x if decode else x[:16]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for j, w in zip(sub.jobs, weights):
+            oracle.matmul(xs, w, j.fmt, j.n_out, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (el > 0 and el / reps * (reps + 1) > budget_s * 2):
+            break
+    per = el / reps
+    if decode:
+        value = sub.weight_bytes / per / 1e9
+        unit = "GB/s"
+        sample = f"{reps} full oracle passes over the submission ({sub.weight_bytes / 1e6:.1f} MB of weights each)"
+    else:
+        flops = sum(2 * xs.shape[0] * j.n_out * sub.n_in for j in sub.jobs)
+        value = flops / per / 1e12
+        unit = "TFLOP/s"
+        sample = f"{reps} oracle passes over the first {xs.shape[0]} rows of x (all jobs)"
+    return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(el, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="c2", choices=sorted(wl.SUBMISSIONS))
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run it with --gpus 1.", file=sys.stderr)
+        return 2
+    import torch
+
+    import quantized_weight_matmul_amd as il
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    sub = wl.SUBMISSIONS[args.workload]
+    decode = sub.t <= 8
+    log(f"[bench] workload {sub.name}: {DESCRIPTIONS[sub.name]}")
+    x_np = wl.make_x(sub)
+    weights = wl.make_weights(sub)
+    per_set = sub.weight_bytes
+    n_sets = max(1, -(-ROTATE_BYTES // per_set)) if decode else 2
+    log(f"[bench] uploading {n_sets} weight sets x {per_set / 1e6:.1f} MB")
+    sets = []
+    for _ in range(n_sets):
+        hs = [il.il_upload(w, j.fmt, j.n_out, sub.n_in) for w, j in zip(weights, sub.jobs)]
+        if any(h is None for h in hs):
+            raise RuntimeError(il.il_last_error())
+        sets.append(hs)
+    x = torch.from_numpy(x_np).cuda()
+    ys = [torch.empty((sub.t, j.n_out), dtype=torch.float32, device="cuda") for j in sub.jobs]
+    stream = torch.cuda.Stream()  # default priority
+
+    def step(i, s):
+        hs = sets[i % n_sets]
+        rc = il.il_matmul(x, sub.t, sub.n_in, [(h, j.n_out, y) for h, j, y in zip(hs, sub.jobs, ys)], s)
+        if rc != 1:
+            raise RuntimeError(il.il_last_error())
+
+    # ---- per-launch kernel duration: HIP events around each launch ----
+    n_ev = min(args.steps, 200)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i, stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_ev)]
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            step(i, stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    kern_ms_mean = float(np.mean(launch_ms))
+    kern_ms_med = float(np.median(launch_ms))
+
+    # ---- whole-job throughput: K steps (one graph, replayed once) ----
+    if args.no_graph:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                step(i, stream)
+        torch.cuda.synchronize()
+        total_s = time.perf_counter() - t0
+    else:
+        g_warm = torch.cuda.CUDAGraph()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_warm, stream=stream, capture_error_mode="relaxed"):
+            for i in range(args.warmup):
+                step(i, torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=stream, capture_error_mode="relaxed"):
+            for i in range(args.steps):
+                step(i, torch.cuda.current_stream())
+        g_warm.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        total_s = time.perf_counter() - t0
+    ms_per_step = total_s * 1e3 / args.steps
+
+    if decode:
+        value = per_set / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = per_set / (kern_ms_mean * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        value = sub.flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = sub.flops / (kern_ms_mean * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roofline["kernel_ms_mean"] = round(kern_ms_mean, 5)
+    roofline["kernel_ms_median"] = round(kern_ms_med, 5)
+    roofline["launches_timed"] = n_ev
+    log(f"[bench] {ms_per_step * 1e3:.2f} us/step, {value:.1f} {unit}; per-launch events "
+        f"mean {kern_ms_mean * 1e3:.2f} us median {kern_ms_med * 1e3:.2f} us")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"[bench] oracle on the host cores for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(sub, x_np, weights, args.cpu_seconds)
+
+    fmts = sorted({wl.FMT_NAMES[j.fmt] for j in sub.jobs})
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if decode else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{sub.name}: {DESCRIPTIONS[sub.name]}",
+            "t": sub.t,
+            "n_in": sub.n_in,
+            "jobs": [[wl.FMT_NAMES[j.fmt], j.n_out] for j in sub.jobs],
+            "weight_formats": fmts,
+            "weight_bytes_per_step": per_set,
+            "flops_per_step": sub.flops,
+            "weight_sets_rotated": n_sets,
+            "timing": "eager" if args.no_graph else "hip-graph",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

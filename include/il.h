@@ -1,0 +1,135 @@
+/*
+ * il.h -- C ABI of the MI355X (gfx950) accelerator linear layer.
+ *
+ * One operation: a batch of matmuls that share one f32 input,
+ *
+ *     for every job j:   y_j[t][n_out_j] = x[t][n_in] * W_j^T
+ *
+ * (oxinfer 0.0.0 `src/gpu.rs` page: the doc comment of `struct Job` states
+ * the product; `trait Backend` gives the calls `wants`, `upload`, `matmul`,
+ * `name` and `stats` that the functions below follow).  Each W_j is
+ * `[n_out, n_in]` row-major, stored as bf16, Q8 or Q4 (`enum WeightRef` on
+ * the same page).  The pages do not show the Q8/Q4 layouts (`QMatrix`,
+ * `Q4Matrix` are imported but not printed), so this library fixes them as
+ * described at IL_Q8 / IL_Q4.
+ *
+ * Conventions for every function:
+ *   - sizes are int64_t; all multi-byte fields are little-endian;
+ *   - functions never print; on failure they set a thread-local message
+ *     readable with il_last_error();
+ *   - every function is thread-safe (`trait Backend: Send + Sync`).  The
+ *     device context is created once per process on first use, on the HIP
+ *     device current at that moment.
+ */
+#ifndef IL_H
+#define IL_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define IL_API __attribute__((visibility("default")))
+#else
+#define IL_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage format of a weight (`enum WeightRef`). */
+typedef enum {
+    /* uint16_t[n_out][n_in]: raw bfloat16 bits (WeightRef::Bf16(&[u16])). */
+    IL_BF16 = 0,
+    /* n_out * (n_in/32) packed 36-byte blocks, row-major by (row, block):
+     *   { float32 scale; int8 q[32]; }   value of element e = q[e] * scale
+     * (symmetric int8 with one f32 scale per 32-element block). */
+    IL_Q8 = 1,
+    /* n_out * (n_in/32) packed 18-byte blocks, row-major by (row, block):
+     *   { uint16 scale_f16_bits; uint8 qs[16]; }
+     * element 2j is the low nibble of qs[j], element 2j+1 the high nibble;
+     * value of element e = (code[e] - 8) * f16(scale)  (4-bit, offset 8). */
+    IL_Q4 = 2
+} il_fmt;
+
+/* Opaque device state of one uploaded weight (`type DeviceWeight`, "owned
+ * by the layer"): immutable after il_upload, so concurrent il_matmul calls
+ * may share it.  Freed with il_free. */
+typedef struct il_weight il_weight;
+
+/* One matmul of a batch (`struct Job`): y[t][n_out] = x[t][n_in] * W^T.
+ *   w     : handle from il_upload; its n_in must equal il_matmul's n_in.
+ *   n_out : must equal the handle's n_out.
+ *   y     : DEVICE pointer to float[t][n_out] row-major, written in full
+ *           (every element, once).  The y buffers of one call must not
+ *           overlap each other or x. */
+typedef struct {
+    const il_weight *w;
+    int64_t n_out;
+    float *y;
+} il_job;
+
+/* Backend::upload -- prepare device state for one weight.
+ *   weight : HOST pointer to the weight in format `fmt` (see il_fmt); it is
+ *            borrowed for the duration of the call and copied, so the caller
+ *            may free it on return.
+ *   n_out, n_in : the weight's shape; n_out >= 1, n_in >= 32 and
+ *            n_in % 32 == 0 (the Q8/Q4 block size; required for every
+ *            format).
+ * Copies the bytes to HBM and rearranges them into the device layout
+ * (code plane + scale plane for Q8/Q4).  Synchronous: the handle is ready on
+ * return.  Returns NULL on failure ("declined", the page's `None`): bad
+ * fmt or shape, null pointer, no HIP device, out of device memory; the
+ * reason is in il_last_error(). */
+IL_API il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in);
+
+/* Drops a handle and its device memory.  NULL is ignored.  The caller must
+ * make sure no il_matmul still using it is in flight (synchronize the
+ * streams it was used on first). */
+IL_API void il_free(il_weight *w);
+
+/* Backend::matmul -- run every job over the shared x in one submission.
+ *   x       : DEVICE pointer to float[t][n_in] row-major, 16-byte aligned.
+ *   t       : rows of x (tokens); t == 0 or n_jobs == 0 is a no-op.
+ *   n_in    : columns of x; must match every job's weight.
+ *   jobs    : HOST array of n_jobs job descriptors (read during the call).
+ *   hip_stream : hipStream_t to enqueue on (NULL = the null stream).
+ * Validates every job first; any invalid job fails the whole call before
+ * anything is enqueued (all or nothing).  t <= 8 runs the decode GEMV
+ * kernels, t > 8 the MFMA GEMM; all jobs of one format share one kernel
+ * launch.  Asynchronous: returns after enqueueing, results are valid once
+ * the stream has reached that point.
+ * Returns 1 on success, 0 if nothing was computed (the page's `false`: the
+ * caller then runs the whole batch elsewhere).  On a validation failure the
+ * y buffers are untouched; if a launch itself fails their contents are
+ * unspecified.  The reason is in il_last_error(). */
+IL_API int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64_t n_jobs,
+              void *hip_stream);
+
+/* Backend::wants -- whether a matmul of these dimensions is worth running on
+ * the GPU (the page: dispatch has a fixed cost, so small ops stay on the
+ * CPU).  A pure function of the sizes: 1 if 2 * n_out * n_in * t is at least
+ * the threshold (default 2^18 flops, IL_WANTS_MIN_FLOP in the environment
+ * overrides it), else 0.  Advisory only: il_matmul never consults it. */
+IL_API int il_wants(int64_t n_out, int64_t n_in, int64_t t);
+
+/* Backend::name -- a static string naming this backend. */
+IL_API const char *il_name(void);
+
+/* Backend::stats -- cumulative summary (calls, jobs and weight bytes per
+ * kernel path; device times when IL_TIMING=1 is set) written as text into
+ * buf (NUL-terminated, truncated to cap bytes).  Returns the length the full
+ * text needs, excluding the NUL; buf may be NULL when cap is 0. */
+IL_API int64_t il_stats(char *buf, int64_t cap);
+
+/* The weight's host-format size in bytes (`WeightRef::bytes`): bf16
+ * 2*n_out*n_in, Q8 36*n_out*n_in/32, Q4 18*n_out*n_in/32.  -1 for NULL. */
+IL_API int64_t il_weight_bytes(const il_weight *w);
+
+/* Message of the last failure on this thread ("" if none). */
+IL_API const char *il_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IL_H */

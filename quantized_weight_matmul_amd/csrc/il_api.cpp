@@ -1,0 +1,431 @@
+// il_api.cpp -- the C ABI (include/il.h): device context, weight handles,
+// argument validation, dispatch to the kernels, statistics, errors.
+//
+// The calls follow `trait Backend` on the oxinfer 0.0.0 src/gpu.rs page:
+// upload -> il_upload (NULL for the page's None), matmul -> il_matmul (0 for
+// false, "nothing was computed"), wants -> il_wants, name -> il_name,
+// stats -> il_stats; `type DeviceWeight` -> il_weight.  The page's process-wide
+// backend (`static ACTIVE: OnceLock`) becomes a lazily created per-device
+// context.
+#include "../../include/il.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cinttypes>
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "il_internal.h"
+
+using il::Weight;
+
+struct il_weight : Weight {};
+
+namespace {
+
+thread_local std::string g_err;
+
+void set_err(const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+}
+
+bool env_flag(const char *name, const char *value) {
+    const char *v = getenv(name);
+    if (!v) return false;
+    // comma-separated list, e.g. IL_FORCE_FAIL=upload,matmul
+    std::string s(v), want(value);
+    size_t pos = 0;
+    while (pos <= s.size()) {
+        size_t end = s.find(',', pos);
+        if (end == std::string::npos) end = s.size();
+        if (s.compare(pos, end - pos, want) == 0) return true;
+        pos = end + 1;
+    }
+    return false;
+}
+
+// ---------------------------------------------------------------- context
+constexpr int kMaxDevices = 64;
+
+struct DeviceCtx {
+    std::once_flag once;
+    bool ok = false;
+    std::string err;
+    int cu_count = 0;
+    hipStream_t upload_stream = nullptr;
+};
+
+DeviceCtx g_dev[kMaxDevices];
+
+DeviceCtx *context(int *device_out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) {
+        set_err("no HIP device available (%s)", hipGetErrorString(e));
+        return nullptr;
+    }
+    if (dev >= kMaxDevices) {
+        set_err("device index %d is beyond the supported %d", dev, kMaxDevices);
+        return nullptr;
+    }
+    DeviceCtx &c = g_dev[dev];
+    std::call_once(c.once, [&] {
+        hipDeviceProp_t prop;
+        hipError_t pe = hipGetDeviceProperties(&prop, dev);
+        if (pe != hipSuccess) {
+            c.err = std::string("hipGetDeviceProperties failed: ") + hipGetErrorString(pe);
+            return;
+        }
+        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+            c.err = std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950";
+            return;
+        }
+        c.cu_count = prop.multiProcessorCount;
+        pe = hipStreamCreateWithFlags(&c.upload_stream, hipStreamNonBlocking);
+        if (pe != hipSuccess) {
+            c.err = std::string("hipStreamCreate failed: ") + hipGetErrorString(pe);
+            return;
+        }
+        c.ok = true;
+    });
+    if (!c.ok) {
+        set_err("%s", c.err.c_str());
+        return nullptr;
+    }
+    if (device_out) *device_out = dev;
+    return &c;
+}
+
+// ------------------------------------------------------------------ stats
+struct PathStats {
+    std::atomic<uint64_t> calls{0}, launches{0}, jobs{0}, bytes{0}, flops{0}, timed_ns{0};
+};
+PathStats g_stats[2];  // 0: decode GEMV, 1: prefill GEMM
+std::atomic<uint64_t> g_uploads{0}, g_upload_bytes{0}, g_failed{0};
+
+int64_t host_bytes(int fmt, int64_t n_out, int64_t n_in) {
+    switch (fmt) {
+        case il::FMT_BF16: return 2 * n_out * n_in;
+        case il::FMT_Q8: return 36 * n_out * (n_in / il::kBlock);
+        case il::FMT_Q4: return 18 * n_out * (n_in / il::kBlock);
+        default: return -1;
+    }
+}
+
+// Device allocation containing [ptr, ptr + bytes)?  Guards the kernels
+// against host pointers and short buffers, which would fault the GPU.
+bool device_range_ok(const void *ptr, int64_t bytes, const char *what) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, ptr) != hipSuccess ||
+        (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)) {
+        (void)hipGetLastError();
+        set_err("%s is not a device pointer", what);
+        return false;
+    }
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        set_err("%s: cannot query its allocation", what);
+        return false;
+    }
+    const char *b = static_cast<const char *>(base);
+    const char *p = static_cast<const char *>(ptr);
+    if (p < b || p + bytes > b + size) {
+        set_err("%s: %" PRId64 " bytes from %p run past its allocation (%zu bytes at %p)", what,
+                bytes, ptr, size, base);
+        return false;
+    }
+    return true;
+}
+
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
+    const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+// ===================================================================== ABI
+extern "C" {
+
+il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in) {
+    g_err.clear();
+    if (!weight) {
+        set_err("il_upload: weight is NULL");
+        return nullptr;
+    }
+    if (fmt != IL_BF16 && fmt != IL_Q8 && fmt != IL_Q4) {
+        set_err("il_upload: unknown format %d", fmt);
+        return nullptr;
+    }
+    if (n_out < 1 || n_out > INT_MAX) {
+        set_err("il_upload: n_out = %" PRId64 " is outside [1, %d]", n_out, INT_MAX);
+        return nullptr;
+    }
+    if (n_in < il::kBlock || n_in % il::kBlock || n_in > INT_MAX) {
+        set_err("il_upload: n_in = %" PRId64 " must be a positive multiple of 32", n_in);
+        return nullptr;
+    }
+    if (env_flag("IL_FORCE_FAIL", "upload")) {
+        set_err("il_upload: failure injected by IL_FORCE_FAIL");
+        return nullptr;
+    }
+    int dev = -1;
+    DeviceCtx *ctx = context(&dev);
+    if (!ctx) return nullptr;
+
+    const int64_t nb = n_in / il::kBlock;
+    const int64_t hb = host_bytes(fmt, n_out, n_in);
+    int64_t code_bytes = 0, scale_bytes = 0;
+    if (fmt == IL_BF16) code_bytes = 2 * n_out * n_in;
+    if (fmt == IL_Q8) code_bytes = n_out * n_in, scale_bytes = 4 * n_out * nb;
+    if (fmt == IL_Q4) code_bytes = n_out * n_in / 2, scale_bytes = 2 * n_out * nb;
+    const int64_t code_alloc = (code_bytes + 255) / 256 * 256;
+
+    void *alloc = nullptr;
+    hipError_t e = hipMalloc(&alloc, (size_t)(code_alloc + scale_bytes));
+    if (e != hipSuccess) {
+        set_err("il_upload: hipMalloc(%" PRId64 ") failed: %s", code_alloc + scale_bytes,
+                hipGetErrorString(e));
+        return nullptr;
+    }
+    char *codes = static_cast<char *>(alloc);
+    char *scales = scale_bytes ? codes + code_alloc : nullptr;
+    hipStream_t s = ctx->upload_stream;
+    void *staging = nullptr;
+    if (fmt == IL_BF16) {
+        e = hipMemcpyAsync(codes, weight, (size_t)hb, hipMemcpyHostToDevice, s);
+    } else {
+        e = hipMalloc(&staging, (size_t)hb);
+        if (e == hipSuccess) e = hipMemcpyAsync(staging, weight, (size_t)hb, hipMemcpyHostToDevice, s);
+        if (e == hipSuccess && fmt == IL_Q8)
+            e = il::launch_repack_q8(static_cast<const uint8_t *>(staging), reinterpret_cast<int8_t *>(codes),
+                                     reinterpret_cast<float *>(scales), n_out, n_in, s);
+        if (e == hipSuccess && fmt == IL_Q4)
+            e = il::launch_repack_q4(static_cast<const uint8_t *>(staging), reinterpret_cast<uint8_t *>(codes),
+                                     reinterpret_cast<uint16_t *>(scales), n_out, n_in, s);
+    }
+    hipError_t se = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = se;
+    if (staging) (void)hipFree(staging);
+    if (e != hipSuccess) {
+        (void)hipFree(alloc);
+        set_err("il_upload: copy/repack failed: %s", hipGetErrorString(e));
+        return nullptr;
+    }
+    il_weight *w = new il_weight();
+    w->fmt = fmt;
+    w->device = dev;
+    w->n_out = n_out;
+    w->n_in = n_in;
+    w->host_bytes = hb;
+    w->alloc = alloc;
+    w->codes = codes;
+    w->scales = scales;
+    g_uploads++;
+    g_upload_bytes += (uint64_t)hb;
+    return w;
+}
+
+void il_free(il_weight *w) {
+    if (!w) return;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != w->device) (void)hipSetDevice(w->device);
+    (void)hipFree(w->alloc);
+    if (cur != w->device && cur >= 0) (void)hipSetDevice(cur);
+    delete w;
+}
+
+int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64_t n_jobs,
+              void *hip_stream) {
+    g_err.clear();
+    if (t < 0 || n_jobs < 0) {
+        set_err("il_matmul: negative t (%" PRId64 ") or n_jobs (%" PRId64 ")", t, n_jobs);
+        return 0;
+    }
+    if (t == 0 || n_jobs == 0) return 1;  // nothing to do
+    if (!jobs) {
+        set_err("il_matmul: jobs is NULL");
+        return 0;
+    }
+    if (!x) {
+        set_err("il_matmul: x is NULL");
+        return 0;
+    }
+    if (t > INT_MAX || n_in < il::kBlock || n_in % il::kBlock || n_in > INT_MAX) {
+        set_err("il_matmul: bad sizes t = %" PRId64 ", n_in = %" PRId64, t, n_in);
+        return 0;
+    }
+    if (reinterpret_cast<uintptr_t>(x) % 16) {
+        set_err("il_matmul: x must be 16-byte aligned");
+        return 0;
+    }
+    if (env_flag("IL_FORCE_FAIL", "matmul")) {
+        set_err("il_matmul: failure injected by IL_FORCE_FAIL");
+        return 0;
+    }
+    int dev = -1;
+    DeviceCtx *ctx = context(&dev);
+    if (!ctx) return 0;
+
+    // ---- validate everything before enqueueing anything ----
+    const int64_t x_bytes = t * n_in * (int64_t)sizeof(float);
+    if (!device_range_ok(x, x_bytes, "x")) return 0;
+    for (int64_t j = 0; j < n_jobs; ++j) {
+        const il_job &jb = jobs[j];
+        const il_weight *w = jb.w;
+        if (!w) {
+            set_err("il_matmul: job %" PRId64 " has no weight", j);
+            return 0;
+        }
+        if (w->n_in != n_in) {
+            set_err("il_matmul: job %" PRId64 ": weight n_in %" PRId64 " != %" PRId64, j, w->n_in, n_in);
+            return 0;
+        }
+        if (jb.n_out != w->n_out) {
+            set_err("il_matmul: job %" PRId64 ": n_out %" PRId64 " != weight's %" PRId64, j, jb.n_out,
+                    w->n_out);
+            return 0;
+        }
+        if (w->device != dev) {
+            set_err("il_matmul: job %" PRId64 ": weight lives on device %d, current is %d", j,
+                    w->device, dev);
+            return 0;
+        }
+        if (!jb.y || reinterpret_cast<uintptr_t>(jb.y) % 4) {
+            set_err("il_matmul: job %" PRId64 ": y is NULL or misaligned", j);
+            return 0;
+        }
+        char what[32];
+        snprintf(what, sizeof what, "job %" PRId64 " y", j);
+        const int64_t y_bytes = t * jb.n_out * (int64_t)sizeof(float);
+        if (!device_range_ok(jb.y, y_bytes, what)) return 0;
+        if (overlaps(jb.y, y_bytes, x, x_bytes)) {
+            set_err("il_matmul: job %" PRId64 ": y overlaps x", j);
+            return 0;
+        }
+        for (int64_t q = 0; q < j; ++q) {
+            if (overlaps(jb.y, y_bytes, jobs[q].y, t * jobs[q].n_out * (int64_t)sizeof(float))) {
+                set_err("il_matmul: jobs %" PRId64 " and %" PRId64 " write overlapping y", q, j);
+                return 0;
+            }
+        }
+    }
+
+    // ---- one launch per format present (kMaxJobs jobs per launch) ----
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const bool decode = t <= il::kGemvMaxT;
+    PathStats &st = g_stats[decode ? 0 : 1];
+    const bool timing = getenv("IL_TIMING") && strcmp(getenv("IL_TIMING"), "1") == 0;
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if (timing) {
+        (void)hipEventCreate(&ev0);
+        (void)hipEventCreate(&ev1);
+        (void)hipEventRecord(ev0, s);
+    }
+    uint64_t launches = 0, bytes = 0;
+    for (int fmt = 0; fmt < 3; ++fmt) {
+        std::vector<il::KJob> batch;
+        auto flush = [&]() -> bool {
+            if (batch.empty()) return true;
+            hipError_t e = decode ? il::launch_gemv(fmt, x, (int)t, (int)n_in, batch.data(),
+                                                    (int)batch.size(), ctx->cu_count, s)
+                                  : il::launch_gemm(fmt, x, (int)t, (int)n_in, batch.data(),
+                                                    (int)batch.size(), ctx->cu_count, s);
+            batch.clear();
+            if (e != hipSuccess) {
+                set_err("il_matmul: kernel launch failed: %s", hipGetErrorString(e));
+                return false;
+            }
+            ++launches;
+            return true;
+        };
+        for (int64_t j = 0; j < n_jobs; ++j) {
+            const il_weight *w = jobs[j].w;
+            if (w->fmt != fmt) continue;
+            batch.push_back(il::KJob{w->codes, w->scales, jobs[j].y, (int)w->n_out});
+            bytes += (uint64_t)w->host_bytes;
+            if ((int)batch.size() == il::kMaxJobs && !flush()) {
+                g_failed++;
+                return 0;
+            }
+        }
+        if (!flush()) {
+            g_failed++;
+            return 0;
+        }
+    }
+    if (timing) {
+        (void)hipEventRecord(ev1, s);
+        (void)hipEventSynchronize(ev1);
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, ev0, ev1) == hipSuccess) st.timed_ns += (uint64_t)(ms * 1e6);
+        (void)hipEventDestroy(ev0);
+        (void)hipEventDestroy(ev1);
+    }
+    uint64_t flops = 0;
+    for (int64_t j = 0; j < n_jobs; ++j) flops += 2ull * (uint64_t)t * (uint64_t)jobs[j].n_out * (uint64_t)n_in;
+    st.calls++;
+    st.launches += launches;
+    st.jobs += (uint64_t)n_jobs;
+    st.bytes += bytes;
+    st.flops += flops;
+    return 1;
+}
+
+int il_wants(int64_t n_out, int64_t n_in, int64_t t) {
+    if (n_out <= 0 || n_in <= 0 || t <= 0) return 0;
+    double min_flop = 262144.0;  // 2^18
+    if (const char *v = getenv("IL_WANTS_MIN_FLOP")) {
+        char *end = nullptr;
+        double d = strtod(v, &end);
+        if (end != v && d >= 0) min_flop = d;
+    }
+    return 2.0 * (double)n_out * (double)n_in * (double)t >= min_flop ? 1 : 0;
+}
+
+const char *il_name(void) { return "il-hip-gfx950"; }
+
+int64_t il_stats(char *buf, int64_t cap) {
+    std::string s;
+    char line[256];
+    const char *names[2] = {"decode_gemv", "prefill_gemm"};
+    for (int i = 0; i < 2; ++i) {
+        const PathStats &p = g_stats[i];
+        snprintf(line, sizeof line,
+                 "%s: calls=%" PRIu64 " launches=%" PRIu64 " jobs=%" PRIu64 " weight_bytes=%" PRIu64
+                 " flops=%" PRIu64 " device_ms=%.3f\n",
+                 names[i], (uint64_t)p.calls, (uint64_t)p.launches, (uint64_t)p.jobs,
+                 (uint64_t)p.bytes, (uint64_t)p.flops, (double)p.timed_ns / 1e6);
+        s += line;
+    }
+    snprintf(line, sizeof line, "uploads: count=%" PRIu64 " bytes=%" PRIu64 "\nfailed_calls: %" PRIu64 "\n",
+             (uint64_t)g_uploads, (uint64_t)g_upload_bytes, (uint64_t)g_failed);
+    s += line;
+    if (buf && cap > 0) {
+        size_t n = s.size() < (size_t)(cap - 1) ? s.size() : (size_t)(cap - 1);
+        memcpy(buf, s.data(), n);
+        buf[n] = '\0';
+    }
+    return (int64_t)s.size();
+}
+
+int64_t il_weight_bytes(const il_weight *w) { return w ? w->host_bytes : -1; }
+
+const char *il_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// il_internal.h -- declarations shared by the library's translation units.
+//
+// Device layouts (written by the upload/repack stage, read by every kernel):
+//   BF16 : codes  = uint16 [n_out][n_in]          (the host layout, row-major)
+//   Q8   : codes  = int8   [n_out][n_in]          (row-major, K contiguous)
+//          scales = float  [n_out][n_in/32]
+//   Q4   : codes  = uint8  [n_out][n_in/2]        (element 2j in the low nibble
+//                                                  of byte j, stored as
+//                                                  code ^ 8, i.e. the 4-bit
+//                                                  two's complement of code-8)
+//          scales = uint16 [n_out][n_in/32]       (f16 bits)
+// Every code row starts 16-byte aligned (n_in % 32 == 0), so one lane can
+// fetch 16 bytes of a row with a single global_load_dwordx4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace il {
+
+enum : int { FMT_BF16 = 0, FMT_Q8 = 1, FMT_Q4 = 2 };
+constexpr int kBlock = 32;     // quantisation block (elements)
+constexpr int kMaxJobs = 8;    // jobs per kernel launch (kernarg table)
+constexpr int kGemvMaxT = 8;   // t <= kGemvMaxT runs the decode kernels
+
+struct Weight {
+    int fmt;
+    int device;
+    int64_t n_out;
+    int64_t n_in;
+    int64_t host_bytes;  // WeightRef::bytes of the host format
+    void *alloc;         // single device allocation holding both planes
+    const void *codes;
+    const void *scales;  // nullptr for BF16
+};
+
+// One job as the kernels see it.
+struct KJob {
+    const void *codes;
+    const void *scales;
+    float *y;
+    int n_out;
+};
+
+// ---- upload / repack (il_repack.hip) ----
+hipError_t launch_repack_q8(const uint8_t *staging, int8_t *codes, float *scales, int64_t n_out,
+                            int64_t n_in, hipStream_t s);
+hipError_t launch_repack_q4(const uint8_t *staging, uint8_t *codes, uint16_t *scales,
+                            int64_t n_out, int64_t n_in, hipStream_t s);
+
+// ---- decode GEMV, t <= kGemvMaxT (il_gemv.hip) ----
+// All jobs share fmt, x and n_in; n_jobs <= kMaxJobs.
+hipError_t launch_gemv(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
+                       int cu_count, hipStream_t s);
+
+// ---- prefill GEMM, t > kGemvMaxT (il_gemm.hip) ----
+hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
+                       int cu_count, hipStream_t s);
+
+}  // namespace il

@@ -1,0 +1,162 @@
+"""ctypes binding of the C ABI in include/il.h, with the same names.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libil.so.  PyTorch supplies device memory and streams.  If the
+library is missing, the first call raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+IL_BF16, IL_Q8, IL_Q4 = 0, 1, 2
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libil.so")
+
+_lock = threading.Lock()
+_lib = None
+_i64 = ctypes.c_int64
+
+
+class il_job(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("n_out", ctypes.c_int64), ("y", ctypes.c_void_p)]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libil.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with __graft_entry__.build() or "
+                    "python -m quantized_weight_matmul_amd._build (there is no CPU fallback)")
+            L = ctypes.CDLL(LIB_PATH)
+            L.il_upload.restype = ctypes.c_void_p
+            L.il_upload.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64, _i64]
+            L.il_free.restype = None
+            L.il_free.argtypes = [ctypes.c_void_p]
+            L.il_matmul.restype = ctypes.c_int
+            L.il_matmul.argtypes = [ctypes.c_void_p, _i64, _i64, ctypes.POINTER(il_job), _i64,
+                                    ctypes.c_void_p]
+            L.il_wants.restype = ctypes.c_int
+            L.il_wants.argtypes = [_i64, _i64, _i64]
+            L.il_name.restype = ctypes.c_char_p
+            L.il_name.argtypes = []
+            L.il_stats.restype = _i64
+            L.il_stats.argtypes = [ctypes.c_char_p, _i64]
+            L.il_weight_bytes.restype = _i64
+            L.il_weight_bytes.argtypes = [ctypes.c_void_p]
+            L.il_last_error.restype = ctypes.c_char_p
+            L.il_last_error.argtypes = []
+            _lib = L
+    return _lib
+
+
+class Weight:
+    """An il_weight handle; il_free runs when the object is collected."""
+
+    __slots__ = ("handle", "fmt", "n_out", "n_in", "__weakref__")
+
+    def __init__(self, handle: int, fmt: int, n_out: int, n_in: int):
+        self.handle = handle
+        self.fmt = fmt
+        self.n_out = n_out
+        self.n_in = n_in
+
+    def free(self) -> None:
+        if self.handle:
+            lib().il_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    @property
+    def bytes(self) -> int:
+        return int(lib().il_weight_bytes(self.handle))
+
+
+def _ptr(a) -> int:
+    """Address of a torch tensor, numpy array, int address or None."""
+    if a is None:
+        return 0
+    if isinstance(a, int):
+        return a
+    if hasattr(a, "data_ptr"):
+        return int(a.data_ptr())
+    if isinstance(a, np.ndarray):
+        return int(a.ctypes.data)
+    raise TypeError(f"cannot take the address of {type(a).__name__}")
+
+
+def il_upload(weight, fmt: int, n_out: int, n_in: int):
+    """Copy a HOST weight (numpy array / bytes) to the device; None if declined."""
+    if isinstance(weight, (bytes, bytearray)):
+        weight = np.frombuffer(weight, dtype=np.uint8)
+    w = np.ascontiguousarray(weight)
+    h = lib().il_upload(ctypes.c_void_p(w.ctypes.data), int(fmt), int(n_out), int(n_in))
+    if not h:
+        return None
+    return Weight(h, int(fmt), int(n_out), int(n_in))
+
+
+def il_free(w: Weight) -> None:
+    w.free()
+
+
+def il_matmul(x, t: int, n_in: int, jobs, stream=None) -> int:
+    """Run every job over x in one submission.
+
+    x      : device tensor (or address) holding float32 [t, n_in]
+    jobs   : sequence of (Weight, n_out, y) with y a device tensor (or address)
+             holding float32 [t, n_out]
+    stream : torch.cuda.Stream, raw hipStream_t address, or None for torch's
+             current stream
+    Returns 1 on success, 0 if nothing was computed (see il_last_error()).
+    """
+    arr = (il_job * max(1, len(jobs)))()
+    keep = []
+    for i, (w, n_out, y) in enumerate(jobs):
+        if w is None or not isinstance(w, Weight):
+            arr[i].w = None
+        else:
+            arr[i].w = w.handle
+        arr[i].n_out = int(n_out)
+        arr[i].y = _ptr(y)
+        keep.append(y)
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    return int(lib().il_matmul(ctypes.c_void_p(_ptr(x)), int(t), int(n_in), arr, len(jobs),
+                               ctypes.c_void_p(int(stream))))
+
+
+def il_wants(n_out: int, n_in: int, t: int) -> int:
+    return int(lib().il_wants(int(n_out), int(n_in), int(t)))
+
+
+def il_name() -> str:
+    return lib().il_name().decode()
+
+
+def il_stats() -> str:
+    n = lib().il_stats(None, 0)
+    buf = ctypes.create_string_buffer(int(n) + 1)
+    lib().il_stats(buf, n + 1)
+    return buf.value.decode()
+
+
+def il_weight_bytes(w: Weight) -> int:
+    return int(lib().il_weight_bytes(w.handle if w else None))
+
+
+def il_last_error() -> str:
+    return lib().il_last_error().decode()

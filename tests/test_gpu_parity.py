@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: |y - y_ref| <= 4e-3 * sum_k |x_k w_k| for every output checked (the
+oracle computes y_ref and the bound), and the workload shapes checked at the
+launch configuration the benchmark times.  Plus device-side closed forms and
+invariants: one-hot / identity W, zero codes, determinism, batch-composition
+invariance, power-of-two scaling, full coverage of y, no writes outside y,
+and the validation paths that must leave y untouched.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_weight_matmul_amd as il
+from quantized_weight_matmul_amd import workloads as wl
+from conftest import gpu_available
+from gpu_util import check_full, check_sampled, run, say, submission_inputs, upload_all
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+BF16, Q8, Q4 = il.IL_BF16, il.IL_Q8, il.IL_Q4
+FMT_NAME = {BF16: "bf16", Q8: "q8", Q4: "q4"}
+
+
+def _bf16_rne(a):
+    """f32 -> nearest bf16 value (ties to even), as f32."""
+    bits = wl.f32_to_bf16_bits(a).astype(np.uint32) << 16
+    return bits.view(np.float32)
+
+
+# ------------------------------------------------------------- workloads
+@pytest.mark.parametrize("name", ["c1", "c2", "c3a", "c3b", "c4_t1", "c4_t2", "c4_t4", "c4_t8"])
+def test_workload_full(name):
+    sub = wl.SUBMISSIONS[name]
+    say(f"[parity] {name}: t={sub.t} n_in={sub.n_in} jobs={[(FMT_NAME[j.fmt], j.n_out) for j in sub.jobs]}")
+    x, ws = submission_inputs(sub)
+    hs = upload_all(ws, [j.fmt for j in sub.jobs], [j.n_out for j in sub.jobs], sub.n_in)
+    ys = run(x, hs, [j.n_out for j in sub.jobs])
+    for j, w, y in zip(sub.jobs, ws, ys):
+        r = check_full(y, x, w, j.fmt, j.n_out, what=f"{name} job {j.tensor_id}")
+        say(f"  job {j.tensor_id}: {r['n']} outputs ok, worst |err|/bound = {r['worst']:.2e}")
+
+
+@pytest.mark.parametrize("name", ["c5a", "c5b"])
+def test_workload_sampled(name):
+    sub = wl.SUBMISSIONS[name]
+    say(f"[parity] {name}: t={sub.t} n_in={sub.n_in} jobs={[(FMT_NAME[j.fmt], j.n_out) for j in sub.jobs]}")
+    x, ws = submission_inputs(sub)
+    hs = upload_all(ws, [j.fmt for j in sub.jobs], [j.n_out for j in sub.jobs], sub.n_in)
+    ys = run(x, hs, [j.n_out for j in sub.jobs])
+    for j, w, y in zip(sub.jobs, ws, ys):
+        r = check_sampled(y, x, w, j.fmt, j.n_out, n_pts=4096, what=f"{name} job {j.tensor_id}")
+        say(f"  job {j.tensor_id}: {r['n']} sampled outputs ok, worst {r['worst']:.2e}")
+
+
+# ---------------------------------------------------- odd shapes, all paths
+def _rand_weight(fmt, g, n_out, n_in):
+    nb = n_in // 32
+    if fmt == BF16:
+        return wl.f32_to_bf16_bits((g.standard_normal((n_out, n_in)) * 0.05).astype(np.float32))
+    if fmt == Q8:
+        return wl.encode_q8(g.integers(-128, 128, (n_out, n_in)).astype(np.int8),
+                            g.uniform(1e-3, 1e-2, (n_out, nb)).astype(np.float32))
+    return wl.encode_q4(g.integers(0, 16, (n_out, n_in)).astype(np.uint8),
+                        g.uniform(1e-3, 1e-1, (n_out, nb)).astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
+@pytest.mark.parametrize("t", [1, 2, 3, 5, 8, 9, 16, 33, 130, 257])
+def test_odd_shapes(fmt, t):
+    """Several tiles plus ragged tails in every dimension, three jobs per call."""
+    g = np.random.default_rng(1000 + 10 * t + fmt)
+    for n_in in (32, 288, 4160):
+        n_outs = [1, 17, 1000] if n_in < 4160 else [200, 129]
+        say(f"[odd] fmt={FMT_NAME[fmt]} t={t} n_in={n_in} n_outs={n_outs}")
+        x = g.standard_normal((t, n_in)).astype(np.float32)
+        ws = [_rand_weight(fmt, g, n, n_in) for n in n_outs]
+        hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
+        ys = run(x, hs, n_outs)
+        for w, n, y in zip(ws, n_outs, ys):
+            check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_in {n_in} n_out {n}")
+
+
+def test_mixed_formats_one_call():
+    g = np.random.default_rng(5)
+    n_in = 256
+    fmts = [Q4, BF16, Q8, BF16, Q4]
+    n_outs = [64, 33, 100, 7, 512]
+    for t in (1, 4, 40):
+        say(f"[mixed] t={t}")
+        x = g.standard_normal((t, n_in)).astype(np.float32)
+        ws = [_rand_weight(f, g, n, n_in) for f, n in zip(fmts, n_outs)]
+        hs = upload_all(ws, fmts, n_outs, n_in)
+        ys = run(x, hs, n_outs)
+        for f, w, n, y in zip(fmts, ws, n_outs, ys):
+            check_full(y, x, w, f, n, what=f"mixed t {t} fmt {f}")
+
+
+def test_many_jobs_one_call():
+    """More jobs than one launch's job table holds."""
+    g = np.random.default_rng(6)
+    n_in, t = 64, 2
+    n_outs = [3 + 5 * i for i in range(19)]
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    ws = [_rand_weight(BF16, g, n, n_in) for n in n_outs]
+    hs = upload_all(ws, [BF16] * len(ws), n_outs, n_in)
+    ys = run(x, hs, n_outs)
+    for w, n, y in zip(ws, n_outs, ys):
+        check_full(y, x, w, BF16, n, what=f"many jobs n_out {n}")
+
+
+# ----------------------------------------------------- closed forms on GPU
+def _onehot(fmt, n_out, n_in, cols):
+    if fmt == BF16:
+        w = np.zeros((n_out, n_in), np.uint16)
+        w[np.arange(n_out), cols] = 0x3F80
+        return w
+    nb = n_in // 32
+    if fmt == Q8:
+        c = np.zeros((n_out, n_in), np.int8)
+        c[np.arange(n_out), cols] = 1
+        return wl.encode_q8(c, np.ones((n_out, nb), np.float32))
+    c = np.full((n_out, n_in), 8, np.uint8)
+    c[np.arange(n_out), cols] = 9
+    return wl.encode_q4(c, np.full((n_out, nb), 0x3C00, np.uint16))
+
+
+@pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
+@pytest.mark.parametrize("t", [1, 3, 8, 9, 200])
+def test_onehot_selects_columns(fmt, t):
+    """One-hot W: y[:, r] = x[:, c_r] exactly on the f32 decode path, and
+    = bf16(x[:, c_r]) exactly on the MFMA path (x rounded to bf16)."""
+    g = np.random.default_rng(20 + t)
+    n_in, n_out = 320, 300
+    cols = g.integers(0, n_in, n_out)
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    (h,) = upload_all([_onehot(fmt, n_out, n_in, cols)], [fmt], [n_out], n_in)
+    (y,) = run(x, [h], [n_out])
+    want = x[:, cols] if t <= 8 else _bf16_rne(x)[:, cols]
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("t", [2, 64])
+def test_identity(t):
+    g = np.random.default_rng(30)
+    n = 256
+    x = g.standard_normal((t, n)).astype(np.float32)
+    for fmt in (BF16, Q8, Q4):
+        (h,) = upload_all([_onehot(fmt, n, n, np.arange(n))], [fmt], [n], n)
+        (y,) = run(x, [h], [n])
+        assert np.array_equal(y, x if t <= 8 else _bf16_rne(x)), f"identity fmt {fmt}"
+
+
+@pytest.mark.parametrize("t", [1, 5, 70])
+def test_zero_codes_give_exact_zeros(t):
+    g = np.random.default_rng(40)
+    n_out, n_in = 96, 512
+    nb = n_in // 32
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    z4 = wl.encode_q4(np.full((n_out, n_in), 8, np.uint8),
+                      g.integers(0x1000, 0x5000, (n_out, nb)).astype(np.uint16))
+    z8 = wl.encode_q8(np.zeros((n_out, n_in), np.int8), g.uniform(0.1, 10, (n_out, nb)).astype(np.float32))
+    hs = upload_all([z4, z8], [Q4, Q8], [n_out, n_out], n_in)
+    for y in run(x, hs, [n_out, n_out]):
+        assert np.all(y == 0)
+
+
+def test_row_sums_with_x_one():
+    """x = 1: y[r] = sum_k w[r][k]; Q4 codes k % 16 give -16 per block."""
+    n_out, n_in = 40, 1024
+    nb = n_in // 32
+    k = np.arange(n_in)
+    codes = np.tile((k % 16).astype(np.uint8), (n_out, 1))
+    sbits = np.array([[(15 - (r % 10)) << 10] * nb for r in range(n_out)], np.uint16)
+    (h,) = upload_all([wl.encode_q4(codes, sbits)], [Q4], [n_out], n_in)
+    for t in (1, 16):
+        (y,) = run(np.ones((t, n_in), np.float32), [h], [n_out])
+        want = np.array([-16.0 * nb * 2.0 ** -(r % 10) for r in range(n_out)], np.float32)
+        assert np.array_equal(y, np.tile(want, (t, 1)))
+
+
+# ------------------------------------------------------------- invariants
+@pytest.mark.parametrize("t", [1, 4, 8, 24, 300])
+def test_deterministic_and_batch_invariant(t):
+    g = np.random.default_rng(50 + t)
+    n_in = 1024
+    n_outs = [512, 130, 96]
+    fmts = [Q4, Q4, Q8]
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    ws = [_rand_weight(f, g, n, n_in) for f, n in zip(fmts, n_outs)]
+    hs = upload_all(ws, fmts, n_outs, n_in)
+    a = run(x, hs, n_outs)
+    b = run(x, hs, n_outs)
+    alone = run(x, hs[:1], n_outs[:1])
+    for ya, yb in zip(a, b):
+        assert np.array_equal(ya, yb), "not bitwise reproducible"
+    assert np.array_equal(a[0], alone[0]), "result depends on the other jobs in the batch"
+
+
+@pytest.mark.parametrize("t", [2, 96])
+def test_power_of_two_scaling(t):
+    g = np.random.default_rng(60)
+    n_in, n_out = 512, 256
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    for fmt in (BF16, Q8, Q4):
+        (h,) = upload_all([_rand_weight(fmt, g, n_out, n_in)], [fmt], [n_out], n_in)
+        (y1,) = run(x, [h], [n_out])
+        (y2,) = run(x * np.float32(8.0), [h], [n_out])
+        assert np.array_equal(y2, y1 * np.float32(8.0)), f"fmt {fmt}"
+
+
+@pytest.mark.parametrize("t", [3, 20])
+def test_writes_exactly_y(t):
+    """Every y element is written (NaN sentinel gone) and nothing around y is
+    (guard bands of a larger buffer keep their canary value)."""
+    import torch
+    g = np.random.default_rng(70)
+    n_in, n_out = 256, 333
+    x_np = g.standard_normal((t, n_in)).astype(np.float32)
+    (h,) = upload_all([_rand_weight(Q4, g, n_out, n_in)], [Q4], [n_out], n_in)
+    pad = 4096
+    buf = torch.full((pad + t * n_out + pad,), 12345.0, dtype=torch.float32, device="cuda")
+    y = buf[pad:pad + t * n_out]
+    y.fill_(float("nan"))
+    x = torch.from_numpy(x_np).cuda()
+    assert il.il_matmul(x, t, n_in, [(h, n_out, y)]) == 1, il.il_last_error()
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(b[:pad] == 12345.0) and np.all(b[pad + t * n_out:] == 12345.0)
+    assert np.all(np.isfinite(b[pad:pad + t * n_out]))
+
+
+# -------------------------------------------------------- validation on GPU
+def test_validation_leaves_y_untouched():
+    import torch
+    g = np.random.default_rng(80)
+    n_in, n_out, t = 64, 32, 2
+    (h,) = upload_all([_rand_weight(BF16, g, n_out, n_in)], [BF16], [n_out], n_in)
+    (h2,) = upload_all([_rand_weight(BF16, g, n_out, 96)], [BF16], [n_out], 96)
+    x_host = g.standard_normal((t, n_in)).astype(np.float32)
+    x = torch.from_numpy(x_host).cuda()
+    y = torch.full((t, n_out), 7.0, device="cuda")
+    y2 = torch.full((t, n_out), 7.0, device="cuda")
+    cases = {
+        "host x": (x_host.ctypes.data, [(h, n_out, y)]),
+        "wrong n_in": (x, [(h2, n_out, y)]),
+        "wrong n_out": (x, [(h, n_out + 1, y)]),
+        "null weight": (x, [(None, n_out, y)]),
+        "overlapping y": (x, [(h, n_out, y), (h, n_out, y)]),
+        "y is x": (x, [(h, n_out, x)]),
+        "bad second job": (x, [(h, n_out, y), (h2, n_out, y2)]),
+    }
+    for what, (xx, jobs) in cases.items():
+        say(f"[validation] {what}")
+        assert il.il_matmul(xx, t, n_in, jobs) == 0, what
+        assert il.il_last_error(), what
+        torch.cuda.synchronize()
+        assert torch.all(y == 7.0) and torch.all(y2 == 7.0), f"{what}: y was written"
+
+
+def test_upload_roundtrip_is_handle_metadata():
+    g = np.random.default_rng(90)
+    for fmt, n_out, n_in in ((BF16, 10, 64), (Q8, 7, 96), (Q4, 5, 128)):
+        w = _rand_weight(fmt, g, n_out, n_in)
+        (h,) = upload_all([w], [fmt], [n_out], n_in)
+        assert h.bytes == wl.weight_bytes(fmt, n_out, n_in) == w.nbytes
