@@ -267,6 +267,248 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming variant, used whenever all of x fits in LDS.  Each wave owns R
+// rows and keeps P steps x R rows of 16-byte weight loads in flight in a
+// register ring: a slot is refilled with the load P steps ahead as soon as it
+// has been consumed, so HBM sees a continuous stream of requests.  All global
+// reads are buffer loads whose descriptor spans exactly one row (or x):
+// reads past the end return 0 without touching memory, so the main loop has
+// no branches around loads and the in-order vector-memory counter lets the
+// whole ring stay in flight.  x goes straight from L2 to LDS (buffer loads
+// with the LDS bit, issued before the first weight loads; padding slots past
+// n_in read as zeros), so staging x overlaps the start of the weight stream.
+constexpr int kStreamWaves = 8;
+constexpr int kStreamThreads = 64 * kStreamWaves;
+constexpr int kStreamMaxLds = 160 * 1024;     // gfx950 LDS per workgroup
+constexpr uint32_t kBufFlags = 0x00020000u;   // gfx9 raw buffer: 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufFlags);
+}
+
+// bit-cast whole vectors: clang 22 turns bit casts of single ext_vector
+// elements into copies of element 0
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <int FMT>
+__device__ __forceinline__ float buf_scale(__amdgpu_buffer_rsrc_t r, uint32_t blk) {
+    if constexpr (FMT == FMT_Q8) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, blk * 4u, 0, 0));
+    } else {
+        const uint16_t bits = __builtin_amdgcn_raw_buffer_load_b16(r, blk * 2u, 0, 0);
+        return (float)__builtin_bit_cast(_Float16, bits) * 0.0625f;  // Q4 values carry *16
+    }
+}
+
+// Sum over the 64 lanes of a wave, result in every lane: DPP within each row
+// of 16 lanes, then two cross-row exchanges.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));  // row_mirror
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Steps (of 64*E elements) per x row in LDS: n_in rounded up to whole rings.
+template <int FMT, int P>
+__host__ __device__ constexpr int stream_steps(int n_in) {
+    constexpr int STEP = 64 * FmtTraits<FMT>::E;
+    return (n_in + STEP * P - 1) / (STEP * P) * P;
+}
+
+template <int FMT, int T, int R, int P>
+__global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvParams p) {
+    constexpr int E = FmtTraits<FMT>::E;
+    constexpr int STEP = 64 * E;
+    constexpr int G = E / 4;
+    constexpr int SLOTS_PER_STEP = STEP / 4;  // float4 slots per step per x row
+    constexpr int LOG_SPS = (E == 8) ? 7 : (E == 16) ? 8 : 9;
+    static_assert((1 << LOG_SPS) == SLOTS_PER_STEP, "slot math");
+    extern __shared__ float4 xs[];  // [T][steps_pad * SLOTS_PER_STEP]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_in = p.n_in;
+    const int steps_pad = stream_steps<FMT, P>(n_in);
+    const int xrow4 = steps_pad * SLOTS_PER_STEP;
+    const int n_slots = T * xrow4;
+    const int nb = n_in / kBlock;
+
+    // ---- 1. x: L2 -> LDS, one 1 KiB wave access per instruction ----
+    // slot q (float4) = row i, step s, group g4, lane l, holding
+    // x[i][s*STEP + l*E + 4*g4 .. +4]; slots past n_in read zeros.
+    {
+        const __amdgpu_buffer_rsrc_t xrs = make_rsrc(p.x, (uint32_t)(T * n_in * 4));
+        for (int q0 = wave * 64; q0 < n_slots; q0 += kStreamThreads) {
+            const int q = q0 + lane;
+            int i = 0, rem = q;
+#pragma unroll
+            for (int ii = 1; ii < T; ++ii)
+                if (rem >= xrow4) rem -= xrow4, ++i;
+            const int s = rem >> LOG_SPS;
+            const int g4 = (rem & (SLOTS_PER_STEP - 1)) >> 6;
+            const int k = s * STEP + (rem & 63) * E + g4 * 4;
+            const uint32_t off = (k < n_in) ? (uint32_t)((i * n_in + k) * 4) : 0x7FFFFFF0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xrs, (__attribute__((address_space(3))) void *)(xs + q0), 16, off, 0, 0, 0);
+        }
+    }
+
+    // ---- 2. this wave's rows: one buffer descriptor per row ----
+    __amdgpu_buffer_rsrc_t crs[R], srs[R];
+    float *yrow[R];
+    int ystride[R];
+    bool valid[R];
+    const int row_base = ((int)blockIdx.x * kStreamWaves + wave) * R;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int g = row_base + r;
+        valid[r] = g < p.total_rows;
+        int j = 0;
+#pragma unroll
+        for (int q = 1; q < kMaxJobs; ++q)
+            if (q < p.n_jobs && g >= p.row0[q]) j = q;
+        const int local = valid[r] ? g - p.row0[j] : 0;
+        const uint32_t rb = valid[r] ? (uint32_t)row_bytes<FMT>(n_in) : 0u;
+        crs[r] = make_rsrc(static_cast<const uint8_t *>(p.job[j].codes) + (int64_t)local * row_bytes<FMT>(n_in), rb);
+        if constexpr (FMT == FMT_Q8)
+            srs[r] = make_rsrc(static_cast<const float *>(p.job[j].scales) + (int64_t)local * nb,
+                               valid[r] ? (uint32_t)(nb * 4) : 0u);
+        else if constexpr (FMT == FMT_Q4)
+            srs[r] = make_rsrc(static_cast<const uint16_t *>(p.job[j].scales) + (int64_t)local * nb,
+                               valid[r] ? (uint32_t)(nb * 2) : 0u);
+        else
+            srs[r] = crs[r];
+        yrow[r] = p.job[j].y + local;
+        ystride[r] = p.job[j].n_out;
+    }
+
+    // ---- 3. prologue: P steps of weight (and scale) loads in flight ----
+    uint4 buf[P][R];
+    float sbuf[P][R];
+    auto issue = [&](int u, int s) {
+        const int k = s * STEP + lane * E;  // reads at k >= n_in return zeros
+        const uint32_t off = (uint32_t)code_byte<FMT>(k);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            buf[u][r] = buf_load16(crs[r], off);
+            if constexpr (FMT != FMT_BF16) sbuf[u][r] = buf_scale<FMT>(srs[r], (uint32_t)(k / kBlock));
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < P; ++u) issue(u, u);
+    __syncthreads();  // x is in LDS (the compiler waits for the LDS loads only)
+
+    // ---- 4. main loop: ring of P slots, no branches around loads ----
+    float acc[R][T];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < T; ++i) acc[r][i] = 0.f;
+
+    for (int s0 = 0; s0 < steps_pad; s0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int s = s0 + u;
+            float part[R][T];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int i = 0; i < T; ++i) part[r][i] = 0.f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float w[R][4];
+#pragma unroll
+                for (int r = 0; r < R; ++r) dequant4<FMT>(buf[u][r], g, w[r]);
+#pragma unroll
+                for (int i = 0; i < T; ++i) {
+                    const float4 xv = xs[i * xrow4 + (s * G + g) * 64 + lane];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        part[r][i] = fmaf(w[r][0], xv.x, part[r][i]);
+                        part[r][i] = fmaf(w[r][1], xv.y, part[r][i]);
+                        part[r][i] = fmaf(w[r][2], xv.z, part[r][i]);
+                        part[r][i] = fmaf(w[r][3], xv.w, part[r][i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int i = 0; i < T; ++i) {
+                    if constexpr (FMT == FMT_BF16)
+                        acc[r][i] += part[r][i];
+                    else
+                        acc[r][i] = fmaf(sbuf[u][r], part[r][i], acc[r][i]);
+                }
+            issue(u, s + P);  // refill this slot P steps ahead
+        }
+    }
+
+    // ---- 5. wave reductions; lane 0 stores ----
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int i = 0; i < T; ++i) {
+            const float v = wave_sum_dpp(acc[r][i]);
+            if (lane == 0 && valid[r]) yrow[r][(int64_t)i * ystride[r]] = v;
+        }
+    }
+}
+
+template <int FMT, int P>
+size_t stream_lds_bytes(int t, int n_in) {
+    constexpr int STEP = 64 * FmtTraits<FMT>::E;
+    return (size_t)t * stream_steps<FMT, P>(n_in) * STEP * sizeof(float);
+}
+
+template <int FMT, int T, int R, int P>
+hipError_t launch_stream(const GemvParams &p, hipStream_t s) {
+    const size_t lds = stream_lds_bytes<FMT, P>(T, p.n_in);
+    auto kern = gemv_stream_kernel<FMT, T, R, P>;
+    if (lds > 64 * 1024) {
+        static bool raised = false;  // benign race: the attribute is idempotent
+        if (!raised) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, kStreamMaxLds);
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+    }
+    const int rows_per_block = kStreamWaves * R;
+    const int grid = (p.total_rows + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kStreamThreads), lds, s, p);
+    return hipGetLastError();
+}
+
+// Ring depth for a row of `steps` 16-byte lane loads.
+inline int stream_ring(int steps) { return steps >= 5 ? 8 : steps >= 3 ? 4 : 2; }
+
+template <int FMT, int T>
+hipError_t try_stream(const GemvParams &p, hipStream_t s, bool *taken) {
+    constexpr int STEP = 64 * FmtTraits<FMT>::E;
+    const int steps = (p.n_in + STEP - 1) / STEP;
+    const int P = stream_ring(steps);
+    // bytes of every buffer descriptor (x and one row) stay far below 2^31
+    *taken = (int64_t)T * p.n_in * 4 < (1ll << 31);
+    // rows per wave: enough weight bytes per workgroup next to its copy of x
+    constexpr int R = (FMT == FMT_Q4) ? 4 : (FMT == FMT_Q8) ? 2 : 1;
+    if (P == 8 && *taken && stream_lds_bytes<FMT, 8>(T, p.n_in) <= kStreamMaxLds)
+        return launch_stream<FMT, T, R, 8>(p, s);
+    if (P == 4 && *taken && stream_lds_bytes<FMT, 4>(T, p.n_in) <= kStreamMaxLds)
+        return launch_stream<FMT, T, R, 4>(p, s);
+    if (P == 2 && *taken && stream_lds_bytes<FMT, 2>(T, p.n_in) <= kStreamMaxLds)
+        return launch_stream<FMT, T, R, 2>(p, s);
+    *taken = false;
+    return hipSuccess;
+}
+
 template <int FMT, int T>
 hipError_t launch_t(const GemvParams &p, int cu_count, hipStream_t s) {
     constexpr int R = (T <= 2) ? 4 : 2;
@@ -284,6 +526,22 @@ hipError_t launch_t(const GemvParams &p, int cu_count, hipStream_t s) {
 template <int FMT>
 hipError_t launch_fmt(GemvParams &p, int cu_count, hipStream_t s) {
     constexpr int STEP = 64 * FmtTraits<FMT>::E;
+    {
+        bool taken = false;
+        hipError_t e = hipSuccess;
+        switch (p.t) {
+            case 1: e = try_stream<FMT, 1>(p, s, &taken); break;
+            case 2: e = try_stream<FMT, 2>(p, s, &taken); break;
+            case 3: e = try_stream<FMT, 3>(p, s, &taken); break;
+            case 4: e = try_stream<FMT, 4>(p, s, &taken); break;
+            case 5: e = try_stream<FMT, 5>(p, s, &taken); break;
+            case 6: e = try_stream<FMT, 6>(p, s, &taken); break;
+            case 7: e = try_stream<FMT, 7>(p, s, &taken); break;
+            case 8: e = try_stream<FMT, 8>(p, s, &taken); break;
+            default: break;
+        }
+        if (taken || e != hipSuccess) return e;
+    }
     // K chunk: as much of x as the LDS budget allows, in whole steps.
     int kc = kXLdsBytes / (int)(p.t * sizeof(float));
     kc = (kc / STEP) * STEP;
