@@ -3,15 +3,27 @@
 // Computes y[t][n_out] = bf16(x)[t][n_in] * W^T with f32 accumulation for
 // every job of one format in one launch (the batch of `struct Job`s over one
 // shared x that Backend::matmul on the oxinfer 0.0.0 src/gpu.rs page submits
-// at once).  x is rounded to bf16 (round-to-nearest-even); bf16 weights are
-// used as stored; Q8/Q4 weights are dequantised to their exact f32 value
-// (Q8: q*scale rounded to f32, Q4: (code-8)*scale, exact) and then rounded to
-// bf16 as they are written to LDS, ahead of the MFMAs.
+// at once).  x is rounded to bf16 (round-to-nearest-even) by a pre-pass into
+// a stream-ordered scratch buffer; bf16 weights are used as stored; Q8/Q4
+// weights are dequantised to their exact f32 value (Q8: q*scale rounded to
+// f32, Q4: (code-8)*scale, exact) and rounded to bf16 as they are written to
+// LDS, ahead of the MFMAs.
 //
-// Tiling: a workgroup owns a BM x BN output tile (BM tokens x BN weight rows)
-// of one job and walks K in BK steps.  Four waves in a 2 x 2 grid each own a
-// 64 x 64 sub-tile = 4 x 4 MFMA 16x16x32 tiles.  Global tiles for step k+1 are
-// fetched into registers while step k runs from LDS.
+// Tiling: a workgroup of 8 waves (two per SIMD) owns a 256 x 256 output tile
+// (256 tokens x 256 weight rows) of one job and walks K in steps of 64.  The
+// waves form a 2 x 4 grid; each owns 128 x 64 = 4 x 2 MFMA 32x32x16 tiles
+// (128 f32 accumulators per lane).  The 32x32x16 bf16 MFMA is used because
+// one wave issuing it keeps the matrix core near its peak, which 16x16x32
+// does not; two waves per SIMD let one wave's MFMAs cover the other's waits.
+// Each K step's operand tiles are fetched into registers one step ahead
+// (Q8/Q4 codes are dequantised there), then written to the LDS stage the
+// MFMAs are not reading: two 64 KiB stages, one barrier per step.  Rows of 64
+// bf16 (8 chunks of 16 bytes) are stored with the chunk index XOR-swizzled by
+// the row, so that both the staging writes and the MFMA fragment reads are
+// free of LDS bank conflicts.  Workgroups are mapped to tiles XCD by XCD
+// (consecutive workgroup ids go to different XCDs), so that each XCD works on
+// one contiguous range of weight-row tiles and its L2 holds the operand slices
+// its workgroups share.
 #include "il_internal.h"
 
 namespace il {
@@ -21,205 +33,231 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (pad: no bank conflicts)
-constexpr int kThreads = 256;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kXcds = 8;
+constexpr int kChunks = BM * BK / 8 / kThreads;  // 16-byte chunks per thread per operand tile
+constexpr uint32_t kBufFlags = 0x00020000u;
+constexpr uint32_t kOut = 0x7FFFFFF0u;  // a buffer offset past every range: reads 0
 
 struct GemmParams {
-    const float *x;
+    const uint16_t *xb;  // bf16 x [t][n_in]
     int t;
     int n_in;
     int n_jobs;
     int tiles_m;
+    int tiles_total;
+    int tiles_per_xcd;
     KJob job[kMaxJobs];
-    int tile0[kMaxJobs + 1];  // prefix sums of tiles_m * tiles_n per job
+    int tn0[kMaxJobs + 1];  // prefix sums of n-tiles per job
 };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufFlags);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     f32x2 v = {a, b};
-    bf16x2 h = __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32: RNE
-    return __builtin_bit_cast(uint32_t, h);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));  // RNE
 }
 
-// Weight tile staging: each thread owns one row (n) and one 32-element half
-// (h) of the BN x BK tile: 32 elements -> 4 x 16 bytes of bf16.
-template <int FMT>
-struct BStage {
-    uint4 raw[4];  // bf16 uses all four, Q8 two, Q4 one
-    float scale;
-};
+// Swizzle of the 16-byte chunk index within an LDS row of 64 bf16.  Rows r
+// and the 8 chunks c: slot = c ^ ((r & 7) ^ ((r >> 3) & 1)).  Any 16
+// consecutive rows read at one chunk land in 16 distinct (bank-half, slot)
+// pairs (64-bank LDS), and any 8 in 8 distinct slots (32-bank LDS).
+__device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int FMT>
-__device__ __forceinline__ void load_b(BStage<FMT> &st, const KJob &jb, int n_in, int n, int k) {
-    // k: first element of this thread's 32-element half (a block boundary)
-    const bool ok = n < jb.n_out;
-    if constexpr (FMT == FMT_BF16) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            static_cast<const uint16_t *>(jb.codes) + (int64_t)n * n_in + k);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st.raw[i] = ok ? src[i] : make_uint4(0, 0, 0, 0);
-    } else if constexpr (FMT == FMT_Q8) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            static_cast<const int8_t *>(jb.codes) + (int64_t)n * n_in + k);
-        st.raw[0] = ok ? src[0] : make_uint4(0, 0, 0, 0);
-        st.raw[1] = ok ? src[1] : make_uint4(0, 0, 0, 0);
-        st.scale = ok ? static_cast<const float *>(jb.scales)[(int64_t)n * (n_in / kBlock) + k / kBlock]
-                      : 0.f;
-    } else {
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            static_cast<const uint8_t *>(jb.codes) + (int64_t)n * (n_in / 2) + k / 2);
-        st.raw[0] = ok ? src[0] : make_uint4(0, 0, 0, 0);
-        uint16_t bits = ok ? static_cast<const uint16_t *>(jb.scales)[(int64_t)n * (n_in / kBlock) + k / kBlock]
-                           : (uint16_t)0;
-        st.scale = (float)__builtin_bit_cast(_Float16, bits) * 0.0625f;  // values carry *16
-    }
-}
-
-// Convert the staged half-row to 32 bf16 and store at dst (16-byte aligned).
-template <int FMT>
-__device__ __forceinline__ void store_b(const BStage<FMT> &st, uint16_t *dst) {
-    uint4 *d = reinterpret_cast<uint4 *>(dst);
-    if constexpr (FMT == FMT_BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = st.raw[i];
-    } else if constexpr (FMT == FMT_Q8) {
-        const uint32_t w[8] = {st.raw[0].x, st.raw[0].y, st.raw[0].z, st.raw[0].w,
-                               st.raw[1].x, st.raw[1].y, st.raw[1].z, st.raw[1].w};
-        uint32_t o[16];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float a = (float)(int8_t)(w[i]) * st.scale;
-            float b = (float)(int8_t)(w[i] >> 8) * st.scale;
-            float c = (float)(int8_t)(w[i] >> 16) * st.scale;
-            float e = (float)(int8_t)(w[i] >> 24) * st.scale;
-            o[2 * i] = pack_bf16(a, b);
-            o[2 * i + 1] = pack_bf16(c, e);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-    } else {
-        const uint32_t w[4] = {st.raw[0].x, st.raw[0].y, st.raw[0].z, st.raw[0].w};
-        uint32_t o[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // word i holds elements 8i..8i+7; nibbles stored code ^ 8
-            uint32_t lo = (w[i] << 4) & 0xF0F0F0F0u;  // elements 0, 2, 4, 6
-            uint32_t hi = w[i] & 0xF0F0F0F0u;         // elements 1, 3, 5, 7
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                float ev = (float)(int8_t)(lo >> (8 * b)) * st.scale;
-                float od = (float)(int8_t)(hi >> (8 * b)) * st.scale;
-                o[4 * i + b] = pack_bf16(ev, od);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-    }
+// x f32 -> bf16 (RNE) pre-pass: 8 elements per thread.
+__global__ __launch_bounds__(256) void x_to_bf16_kernel(const float *__restrict__ x, uint4 *__restrict__ xb,
+                                                        int64_t n8) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const float4 a = reinterpret_cast<const float4 *>(x)[2 * i];
+    const float4 b = reinterpret_cast<const float4 *>(x)[2 * i + 1];
+    xb[i] = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
 }
 
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_STRIDE];
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][BM * BK];  // [stage][A|B]
 
-    // ---- tile -> (job, m tile, n tile) ----
-    const int tile = blockIdx.x;
+    // ---- workgroup -> tile, XCD by XCD ----
+    const int b = blockIdx.x;
+    const int tile = (b % kXcds) * p.tiles_per_xcd + b / kXcds;
+    if (tile >= p.tiles_total) return;
+    const int tn_all = tile / p.tiles_m;
+    const int tm = tile - tn_all * p.tiles_m;
     int j = 0;
 #pragma unroll
     for (int q = 1; q < kMaxJobs; ++q)
-        if (q < p.n_jobs && tile >= p.tile0[q]) j = q;
+        if (q < p.n_jobs && tn_all >= p.tn0[q]) j = q;
     const KJob jb = p.job[j];
-    const int local = tile - p.tile0[j];
-    const int tm = local % p.tiles_m;
-    const int tn = local / p.tiles_m;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * BM;
+    const int n0 = (tn_all - p.tn0[j]) * BN;
     const int n_in = p.n_in;
+    const int nb = n_in / kBlock;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 wave grid, 128 x 64 per wave
 
-    // staging roles: thread -> (row, 32-element half) of the A and B tiles
-    const int sr = tid >> 1, sh = tid & 1;
-    const int am = m0 + sr;
-    const bool a_ok = am < p.t;
-    const float *arow = p.x + (int64_t)(a_ok ? am : 0) * n_in + sh * 32;
+    // ---- operand descriptors: exactly the tile's valid rows ----
+    const int a_rows = min(BM, p.t - m0);
+    const int b_rows = min(BN, jb.n_out - n0);
+    const uint32_t row2 = (uint32_t)n_in * 2u;
+    const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.xb + (int64_t)m0 * n_in, (uint32_t)a_rows * row2);
+    __amdgpu_buffer_rsrc_t brs, bss;
+    if constexpr (FMT == FMT_BF16) {
+        brs = make_rsrc(static_cast<const uint16_t *>(jb.codes) + (int64_t)n0 * n_in, (uint32_t)b_rows * row2);
+        bss = brs;
+    } else if constexpr (FMT == FMT_Q8) {
+        brs = make_rsrc(static_cast<const int8_t *>(jb.codes) + (int64_t)n0 * n_in,
+                        (uint32_t)b_rows * (uint32_t)n_in);
+        bss = make_rsrc(static_cast<const float *>(jb.scales) + (int64_t)n0 * nb,
+                        (uint32_t)b_rows * (uint32_t)nb * 4u);
+    } else {
+        brs = make_rsrc(static_cast<const uint8_t *>(jb.codes) + (int64_t)n0 * (n_in / 2),
+                        (uint32_t)b_rows * (uint32_t)(n_in / 2));
+        bss = make_rsrc(static_cast<const uint16_t *>(jb.scales) + (int64_t)n0 * nb,
+                        (uint32_t)b_rows * (uint32_t)nb * 2u);
+    }
 
-    f32x4 acc[4][4];
+    // bf16 staging: chunk i of this thread is row crow0 + 64 i, 16-byte chunk
+    // cc, so 8 consecutive threads read one 128-byte row segment.  Q8/Q4
+    // staging: this thread owns row tid / 2, elements 32 (tid % 2) .. +31 of
+    // the step (one quantisation block).
+    const int crow0 = tid >> 3, cc = tid & 7;
+    const int cslot = cc ^ swz_key(crow0);  // rows crow0 + 64 i share the key
+    const int qr = tid >> 1, qh = tid & 1;
+    const int qkey = swz_key(qr);
+
+    uint4 sa[kChunks];
+    uint4 sb[FMT == FMT_BF16 ? kChunks : (FMT == FMT_Q8 ? 2 : 1)];
+    float ssc = 0.f;
+    auto fetch = [&](int k0) {
+        const int k = k0 + cc * 8;
+        const bool kok = k < n_in;
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            const uint32_t off = kok ? (uint32_t)(crow0 + (kThreads / 8) * i) * row2 + (uint32_t)k * 2u : kOut;
+            sa[i] = bload16(ars, off);
+            if constexpr (FMT == FMT_BF16) sb[i] = bload16(brs, off);
+        }
+        if constexpr (FMT != FMT_BF16) {
+            const int kh = k0 + 32 * qh;
+            const bool ok = kh < n_in;
+            if constexpr (FMT == FMT_Q8) {
+                const uint32_t off = ok ? (uint32_t)qr * (uint32_t)n_in + (uint32_t)kh : kOut;
+                sb[0] = bload16(brs, off);
+                sb[1] = bload16(brs, ok ? off + 16u : kOut);
+                ssc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                    bss, ok ? ((uint32_t)qr * nb + kh / kBlock) * 4u : kOut, 0, 0));
+            } else {
+                sb[0] = bload16(brs, ok ? (uint32_t)qr * (uint32_t)(n_in / 2) + (uint32_t)(kh / 2) : kOut);
+                const uint16_t bits = __builtin_amdgcn_raw_buffer_load_b16(
+                    bss, ok ? ((uint32_t)qr * nb + kh / kBlock) * 2u : kOut, 0, 0);
+                ssc = (float)__builtin_bit_cast(_Float16, bits) * 0.0625f;  // values carry *16
+            }
+        }
+    };
+    auto store = [&](uint16_t *As, uint16_t *Bs) {
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            const int off = (crow0 + (kThreads / 8) * i) * BK + cslot * 8;
+            *reinterpret_cast<uint4 *>(As + off) = sa[i];
+            if constexpr (FMT == FMT_BF16) *reinterpret_cast<uint4 *>(Bs + off) = sb[i];
+        }
+        if constexpr (FMT != FMT_BF16) {
+            uint32_t o[16];
+            if constexpr (FMT == FMT_Q8) {
+                const uint32_t w[8] = {sb[0].x, sb[0].y, sb[0].z, sb[0].w, sb[1].x, sb[1].y, sb[1].z, sb[1].w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    o[2 * i] = pack_bf16((float)(int8_t)(w[i]) * ssc, (float)(int8_t)(w[i] >> 8) * ssc);
+                    o[2 * i + 1] = pack_bf16((float)(int8_t)(w[i] >> 16) * ssc, (float)(int8_t)(w[i] >> 24) * ssc);
+                }
+            } else {
+                const uint32_t w[4] = {sb[0].x, sb[0].y, sb[0].z, sb[0].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t lo = (w[i] << 4) & 0xF0F0F0F0u;  // elements 0, 2, 4, 6 (code ^ 8)
+                    const uint32_t hi = w[i] & 0xF0F0F0F0u;         // elements 1, 3, 5, 7
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[4 * i + e] = pack_bf16((float)(int8_t)(lo >> (8 * e)) * ssc, (float)(int8_t)(hi >> (8 * e)) * ssc);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint4 *>(Bs + qr * BK + ((4 * qh + i) ^ qkey) * 8) =
+                    make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+        }
+    };
+
+    f32x16 acc[4][2];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < 2; ++n) acc[a][n] = (f32x16){};
 
-    float4 areg[8];
-    BStage<FMT> breg;
-    // Fetch this thread's halves of the A and B tiles at K offset k0; a half
-    // that lies past n_in (n_in % 64 == 32 on the last step) is zero-filled.
-    auto load_tiles = [&](int k0) {
-        const bool k_ok = k0 + sh * 32 < n_in;
-        const float4 *src = reinterpret_cast<const float4 *>(arow + k0);
+    // 32x32x16 fragments: lane reads row (lane & 31) of a 32-row tile, 16-byte
+    // chunk 2 kk + lane / 32; every fragment row of this lane shares one
+    // swizzle key because tile offsets are multiples of 32
+    const int frow = lane & 31;
+    const int fkey = swz_key(frow);
+    const int a_base = (wm * 128 + frow) * BK;
+    const int b_base = (wn * 64 + frow) * BK;
+    auto compute = [&](const uint16_t *As, const uint16_t *Bs) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            areg[i] = (a_ok && k_ok) ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        if (k_ok) {
-            load_b<FMT>(breg, jb, n_in, n0 + sr, k0 + sh * 32);
-        } else {
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int slot = (kk * 2 + (lane >> 5)) ^ fkey;
+            bf16x8 fa[4], fb[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) breg.raw[i] = make_uint4(0, 0, 0, 0);
-            breg.scale = 0.f;
-        }
-    };
-    auto store_tiles = [&]() {
-        uint4 *ad = reinterpret_cast<uint4 *>(As + sr * LDS_STRIDE + sh * 32);
+            for (int a = 0; a < 4; ++a) fa[a] = *reinterpret_cast<const bf16x8 *>(As + a_base + a * 32 * BK + slot * 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 u = areg[2 * i], v = areg[2 * i + 1];
-            ad[i] = make_uint4(pack_bf16(u.x, u.y), pack_bf16(u.z, u.w), pack_bf16(v.x, v.y),
-                               pack_bf16(v.z, v.w));
-        }
-        store_b<FMT>(breg, Bs + sr * LDS_STRIDE + sh * 32);
-    };
-
-    const int ksteps = n_in / BK + ((n_in % BK) ? 1 : 0);
-    load_tiles(0);
-    for (int ks = 0; ks < ksteps; ++ks) {
-        __syncthreads();  // previous step's MFMAs are done reading LDS
-        store_tiles();
-        __syncthreads();
-        if (ks + 1 < ksteps) load_tiles((ks + 1) * BK);
-#pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-            bf16x8 af[4], bfr[4];
-            const int kcol = kk * 32 + (lane >> 4) * 8;
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int row = wm * 64 + a * 16 + (lane & 15);
-                af[a] = *reinterpret_cast<const bf16x8 *>(As + row * LDS_STRIDE + kcol);
-            }
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int row = wn * 64 + b * 16 + (lane & 15);
-                bfr[b] = *reinterpret_cast<const bf16x8 *>(Bs + row * LDS_STRIDE + kcol);
-            }
+            for (int n = 0; n < 2; ++n) fb[n] = *reinterpret_cast<const bf16x8 *>(Bs + b_base + n * 32 * BK + slot * 8);
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+                for (int n = 0; n < 2; ++n)
+                    acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[n], acc[a][n], 0, 0, 0);
         }
+    };
+
+    const int nk = (n_in + BK - 1) / BK;
+    fetch(0);
+    store(lds[0][0], lds[0][1]);
+    if (nk > 1) fetch(BK);
+    __syncthreads();
+    for (int ks = 0; ks < nk; ++ks) {
+        const int cur = ks & 1;
+        compute(lds[cur][0], lds[cur][1]);
+        if (ks + 1 < nk) {
+            store(lds[cur ^ 1][0], lds[cur ^ 1][1]);  // step ks+1 (its loads were in flight)
+            if (ks + 2 < nk) fetch((ks + 2) * BK);
+        }
+        __syncthreads();
     }
 
-    // ---- epilogue: lane holds rows 4*(lane/16)+e of column lane%16 ----
+    // ---- epilogue: 32x32 tile, lane holds rows 8 (i / 4) + 4 (lane / 32) + i % 4
+    //      of column lane % 32 ----
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int n = n0 + wn * 64 + b * 16 + (lane & 15);
+        for (int n = 0; n < 2; ++n) {
+            const int col = n0 + wn * 64 + n * 32 + (lane & 31);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = m0 + wm * 64 + a * 16 + (lane >> 4) * 4 + e;
-                if (m < p.t && n < jb.n_out) jb.y[(int64_t)m * jb.n_out + n] = acc[a][b][e];
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * 128 + a * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+                if (row < p.t && col < jb.n_out) jb.y[(int64_t)row * jb.n_out + col] = acc[a][n][i];
             }
         }
     }
@@ -231,26 +269,44 @@ hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *job
                        int cu_count, hipStream_t s) {
     (void)cu_count;
     if (t < 1 || n_jobs < 1 || n_jobs > kMaxJobs || n_in % kBlock) return hipErrorInvalidValue;
+    // every buffer descriptor (256 rows of x or of a weight) must stay below 2^31 bytes
+    if ((int64_t)BM * n_in * 2 >= (1ll << 31)) return hipErrorInvalidValue;
     GemmParams p{};
-    p.x = x;
     p.t = t;
     p.n_in = n_in;
     p.n_jobs = n_jobs;
     p.tiles_m = (t + BM - 1) / BM;
-    int tiles = 0;
+    int tn = 0;
     for (int j = 0; j < n_jobs; ++j) {
         p.job[j] = jobs[j];
-        p.tile0[j] = tiles;
-        tiles += p.tiles_m * ((jobs[j].n_out + BN - 1) / BN);
+        p.tn0[j] = tn;
+        tn += (jobs[j].n_out + BN - 1) / BN;
     }
-    for (int j = n_jobs; j <= kMaxJobs; ++j) p.tile0[j] = tiles;
-    switch (fmt) {
-        case FMT_BF16: hipLaunchKernelGGL(gemm_kernel<FMT_BF16>, dim3(tiles), dim3(kThreads), 0, s, p); break;
-        case FMT_Q8: hipLaunchKernelGGL(gemm_kernel<FMT_Q8>, dim3(tiles), dim3(kThreads), 0, s, p); break;
-        case FMT_Q4: hipLaunchKernelGGL(gemm_kernel<FMT_Q4>, dim3(tiles), dim3(kThreads), 0, s, p); break;
-        default: return hipErrorInvalidValue;
+    for (int j = n_jobs; j <= kMaxJobs; ++j) p.tn0[j] = tn;
+    p.tiles_total = p.tiles_m * tn;
+    p.tiles_per_xcd = (p.tiles_total + kXcds - 1) / kXcds;
+
+    // x -> bf16 into stream-ordered scratch, freed after the GEMM on the same stream
+    const int64_t n8 = (int64_t)t * n_in / 8;
+    void *xb = nullptr;
+    hipError_t e = hipMallocAsync(&xb, (size_t)n8 * 16, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(x_to_bf16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x,
+                       static_cast<uint4 *>(xb), n8);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+        p.xb = static_cast<const uint16_t *>(xb);
+        const dim3 grid(kXcds * p.tiles_per_xcd);
+        switch (fmt) {
+            case FMT_BF16: hipLaunchKernelGGL(gemm_kernel<FMT_BF16>, grid, dim3(kThreads), 0, s, p); break;
+            case FMT_Q8: hipLaunchKernelGGL(gemm_kernel<FMT_Q8>, grid, dim3(kThreads), 0, s, p); break;
+            case FMT_Q4: hipLaunchKernelGGL(gemm_kernel<FMT_Q4>, grid, dim3(kThreads), 0, s, p); break;
+            default: e = hipErrorInvalidValue;
+        }
+        if (e == hipSuccess) e = hipGetLastError();
     }
-    return hipGetLastError();
+    hipError_t fe = hipFreeAsync(xb, s);
+    return e != hipSuccess ? e : fe;
 }
 
 }  // namespace il
