@@ -53,6 +53,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = {True: "il_gemv.hip", False: "il_gemm.hip"}  # decode?, prefill
+
+
+def kernel_source_sha(decode: bool) -> str:
+    import hashlib
+    path = os.path.join(ROOT, "quantized_weight_matmul_amd", "csrc", KERNEL_SOURCES[decode])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, decode: bool):
+    """HBM bytes per launch of the workload's kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (profiles/traffic.json), scaled by
+    the same counters on a plain copy of known size; None when absent or when
+    the kernel source changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha(decode):
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
 def cpu_baseline(sub: wl.Submission, x, weights, budget_s: float) -> dict:
     """The oracle, as it stands, on the host cores: a bounded sample of the
     same workload (whole submissions for decode; a slice of x's rows for
@@ -92,7 +118,21 @@ def main() -> int:
     ap.add_argument("--workload", default="c2", choices=sorted(wl.SUBMISSIONS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (the "
+                         "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.ones(n, device="cuda")
+        b = torch.empty(n, device="cuda")
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.calibrate_copy} MiB five times")
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -191,6 +231,7 @@ def main() -> int:
         achieved = sub.flops / launches_per_step / (kern_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roofline["traffic"] = measured_traffic(sub.name, decode)
     roofline["kernel_ms"] = round(kern_ms, 6)
     roofline["timing"] = "HIP events on the launch stream around the timed region / launches"
     roofline["event_pair_ms_median"] = round(pair_ms, 6)
