@@ -53,17 +53,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = {True: "il_gemv.hip", False: "il_gemm.hip"}  # decode?, prefill
-
-
-def kernel_source_sha(decode: bool) -> str:
+def kernel_source_sha(name: str) -> str:
     import hashlib
-    path = os.path.join(ROOT, "quantized_weight_matmul_amd", "csrc", KERNEL_SOURCES[decode])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    path = os.path.join(ROOT, "quantized_weight_matmul_amd", "csrc", name)
+    try:
+        with open(path, "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()[:16]
+    except OSError:
+        return ""
 
 
-def measured_traffic(workload: str, decode: bool):
+def measured_traffic(workload: str):
     """HBM bytes per launch of the workload's kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE runs (profiles/traffic.json), scaled by
     the same counters on a plain copy of known size; None when absent or when
@@ -74,7 +74,7 @@ def measured_traffic(workload: str, decode: bool):
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_source_sha") != kernel_source_sha(decode):
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha(rec.get("kernel_source", "")):
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -231,7 +231,7 @@ def main() -> int:
         achieved = sub.flops / launches_per_step / (kern_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
-    roofline["traffic"] = measured_traffic(sub.name, decode)
+    roofline["traffic"] = measured_traffic(sub.name)
     roofline["kernel_ms"] = round(kern_ms, 6)
     roofline["timing"] = "HIP events on the launch stream around the timed region / launches"
     roofline["event_pair_ms_median"] = round(pair_ms, 6)

@@ -24,6 +24,9 @@
 //     are bitwise reproducible.
 #include "il_internal.h"
 
+#include <cstdlib>
+#include <cstring>
+
 namespace il {
 namespace {
 
@@ -564,9 +567,22 @@ hipError_t launch_fmt(GemvParams &p, int cu_count, hipStream_t s) {
 
 }  // namespace
 
+// Smallest t at which the matrix-core decode kernel beats the streaming
+// kernel for a format: where the f32 vector work per weight byte (2t flops
+// per element plus the dequantisation) stops fitting under the HBM time.
+static int mfma_min_t(int fmt) { return fmt == FMT_Q4 ? 2 : fmt == FMT_Q8 ? 5 : kGemvMaxT + 1; }
+
 hipError_t launch_gemv(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
                        int cu_count, hipStream_t s) {
     if (t < 1 || t > kGemvMaxT || n_jobs < 1 || n_jobs > kMaxJobs) return hipErrorInvalidValue;
+    // IL_DECODE=valu|mfma pins the kernel family (both compute the same sums)
+    bool use_mfma = t >= mfma_min_t(fmt);
+    if (const char *force = getenv("IL_DECODE")) {
+        if (!strcmp(force, "mfma")) use_mfma = true;
+        if (!strcmp(force, "valu")) use_mfma = false;
+    }
+    if (use_mfma && gemv_mfma_fits(fmt, t, n_in, jobs, n_jobs))
+        return launch_gemv_mfma(fmt, x, t, n_in, jobs, n_jobs, cu_count, s);
     GemvParams p{};
     p.x = x;
     p.t = t;

@@ -1,0 +1,459 @@
+// il_gemv_mfma.hip -- decode GEMV on the bf16 matrix cores (small t > 1).
+//
+// Computes the same sums as the streaming decode kernel,
+//   y[i][r] = sum_b s_rb * sum_{k in block b} (q_rk - z) * x_ik
+// (bf16: s = 1, z = 0, q = w; Q8: z = 0; Q4: z = 8), i.e. the matmul of the
+// `struct Job` doc comment (oxinfer 0.0.0 src/gpu.rs page) for every job of
+// one format over the shared x of one submission (Backend::matmul on the
+// same page).  With t tokens every weight element feeds 2t flops; once that
+// outgrows the f32 vector units' budget per byte of Q4/Q8 weights, the
+// contraction is moved onto v_mfma_f32_16x16x32_bf16, while HBM streaming of
+// the weights stays the bound.
+//
+// Operands of one MFMA (16 x 16 output, K = 32 = one quantisation block):
+//   * B = 16 weight rows x one block, as exact bf16 values: bf16 weights as
+//     stored; Q8 codes converted through f32 (|q| <= 127 is exact in bf16);
+//     Q4 nibbles (stored as the 4-bit two's complement of code - 8) moved to
+//     the top of a byte are the signed value 16 * (code - 8), converted the
+//     same way (the factor 16 is removed from the result, exactly).  No
+//     offset is folded out of a sum, so every product of A and B is exact
+//     and the rounding of a result is relative to the sum of |x * w|.
+//   * A = x as 16 rows: row i < 8 holds bf16(x_i) ("hi"), row 8 + i holds
+//     bf16(x_i - hi) ("lo"), so hi + lo carries 16 significant bits of x and
+//     each product of A and B is exact in f32.  Rows of tokens >= t read
+//     zeros.  Each wave builds these operands itself from x (f32, a few KiB
+//     that stay in L2), one step ahead, in the per-lane order of the MFMA.
+//   * The per-block scale multiplies the 16 x 16 f32 result (one FMA per
+//     accumulator element), so no rounding of a dequantised weight occurs.
+//
+// Loads: a wave fetches 16 bytes per lane, 64 bytes of each of 16 rows (one
+// bf16 block, two Q8 blocks or four Q4 blocks per row: one "step").  Lane
+// group g (lanes 16g..16g+15) holds row bytes [16g, 16g + 16) of the step;
+// the MFMA wants lane group g to hold the g-th quarter of each block, which
+// for Q8/Q4 is a 4 x 4 transpose of dwords across the lane groups (two
+// permlane32 and two permlane16 swaps).  The K order inside a block that
+// results is mirrored in the layout of the A operand, so A and B agree slot
+// by slot.
+//
+// Work split: a workgroup of 8 waves owns a contiguous range of 16-row tiles
+// (an equal share of all jobs' tiles), taken in chunks of up to 9 tiles of
+// one job whose accumulators stay in registers.  Wave w streams steps w,
+// w + 8, w + 16, ... of every tile of the chunk, so the workgroup reads 512
+// contiguous bytes of each row at a time.  Each tile has its own register
+// slot, refilled with the next step's 16 bytes as soon as it has been
+// consumed, so a whole step of loads stays in flight.  At the end of a chunk
+// the eight partial 16 x 16 results per tile are summed through LDS in a
+// fixed order, so results are bitwise reproducible (no atomics).
+#include "il_internal.h"
+
+namespace il {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 16;                    // weight rows per MFMA tile
+constexpr int kChunk = 9;                    // tiles accumulated in registers at once
+constexpr uint32_t kBufFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
+constexpr uint32_t kOut = 0x7FFFFFF0u;       // a buffer offset past every range: reads 0
+
+// Blocks of one row covered by a wave's 16-byte-per-lane step (64 bytes/row).
+template <int FMT>
+struct Mfma;
+template <>
+struct Mfma<FMT_BF16> {
+    static constexpr int BPS = 1;
+    static constexpr int ROW_BYTES_PER_K = 2;
+};
+template <>
+struct Mfma<FMT_Q8> {
+    static constexpr int BPS = 2;
+    static constexpr int ROW_BYTES_PER_K = 1;
+};
+template <>
+struct Mfma<FMT_Q4> {
+    static constexpr int BPS = 4;
+    static constexpr int ROW_BYTES_PER_K = 0;  // half a byte: handled explicitly
+};
+
+template <int FMT>
+__host__ __device__ constexpr int64_t mfma_row_bytes(int64_t n_in) {
+    return FMT == FMT_Q4 ? n_in / 2 : n_in * Mfma<FMT>::ROW_BYTES_PER_K;
+}
+
+// Index within its block of the code that MFMA operand slot j (0..7) of lane
+// group g holds after the loads, transposes and conversions below.
+template <int FMT>
+__device__ __forceinline__ int slot_code(int g, int j) {
+    if constexpr (FMT == FMT_BF16) {
+        return 8 * g + j;
+    } else if constexpr (FMT == FMT_Q8) {
+        return (j < 4) ? 4 * g + j : 16 + 4 * g + (j - 4);
+    } else {
+        return 8 * g + j;
+    }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufFlags);
+}
+
+// bit-cast whole vectors: clang 22 turns bit casts of single ext_vector
+// elements into copies of element 0
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));  // RNE
+}
+
+__device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// Dword d of lane group m -> dword m of lane group d (lanes keep l % 16).
+__device__ __forceinline__ void xpose4(uint32_t &d0, uint32_t &d1, uint32_t &d2, uint32_t &d3) {
+    // lanes 32..63 of the first operand trade places with lanes 0..31 of the second
+    const auto a = __builtin_amdgcn_permlane32_swap(d0, d2, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(d1, d3, false, false);
+    // odd 16-lane rows of the first operand trade places with even rows of the second
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    d0 = c[0];
+    d1 = c[1];
+    d2 = e[0];
+    d3 = e[1];
+}
+
+// 8 Q4 codes of one dword (stored as code ^ 8, element 2i in the low nibble
+// of byte i) -> 8 exact bf16 values 16 * (code - 8), in order.
+__device__ __forceinline__ bf16x8 q4_to_bf16(uint32_t d) {
+    const uint32_t lo = (d << 4) & 0xF0F0F0F0u;  // elements 0, 2, 4, 6 as signed bytes
+    const uint32_t hi = d & 0xF0F0F0F0u;         // elements 1, 3, 5, 7
+    uint4 o;
+    o.x = pack_bf16((float)(int8_t)lo, (float)(int8_t)hi);
+    o.y = pack_bf16((float)(int8_t)(lo >> 8), (float)(int8_t)(hi >> 8));
+    o.z = pack_bf16((float)(int8_t)(lo >> 16), (float)(int8_t)(hi >> 16));
+    o.w = pack_bf16((float)(int8_t)(lo >> 24), (float)(int8_t)(hi >> 24));
+    return __builtin_bit_cast(bf16x8, o);
+}
+
+// 8 signed Q8 codes (4 per dword) -> 8 exact bf16 values, in order.
+__device__ __forceinline__ bf16x8 q8_to_bf16(uint32_t a, uint32_t b) {
+    uint4 o;
+    o.x = pack_bf16((float)(int8_t)a, (float)(int8_t)(a >> 8));
+    o.y = pack_bf16((float)(int8_t)(a >> 16), (float)(int8_t)(a >> 24));
+    o.z = pack_bf16((float)(int8_t)b, (float)(int8_t)(b >> 8));
+    o.w = pack_bf16((float)(int8_t)(b >> 16), (float)(int8_t)(b >> 24));
+    return __builtin_bit_cast(bf16x8, o);
+}
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+
+// A operand of one block for this lane from its 8 x values (two 16-byte
+// loads): hi lanes (lo_mask 0) take bf16(x), lo lanes (lo_mask ~0) take
+// bf16(x - bf16(x)).  Whole-vector bit casts (see bload16).
+__device__ __forceinline__ bf16x8 x_frag(const uint4 &p, const uint4 &q, uint32_t lo_mask) {
+    const f32x4 a = __builtin_bit_cast(f32x4, p);
+    const f32x4 b = __builtin_bit_cast(f32x4, q);
+    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t hm = pack_bf16(v[2 * k], v[2 * k + 1]) & lo_mask;
+        w[k] = pack_bf16(v[2 * k] - bf16_lo_f32(hm), v[2 * k + 1] - bf16_hi_f32(hm));
+    }
+    return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+struct MfmaParams {
+    const float *x;  // [t][n_in]
+    int t;
+    int n_in;
+    int nb;     // blocks per row
+    int steps;  // ceil(nb / BPS)
+    int n_jobs;
+    int tiles_total;
+    KJob job[kMaxJobs];
+    int tile0[kMaxJobs + 1];  // prefix sums of 16-row tiles per job
+};
+
+// A run of at most TC consecutive tiles of one job: the unit of register
+// accumulation and of the LDS reduction.
+struct Chunk {
+    int start;  // first tile (global index); >= the workgroup's end: none
+    int cnt;    // tiles in the chunk (0: none)
+    int j;      // job
+    int lrow0;  // job-local row of the chunk's first row
+};
+
+template <int FMT, int TC>
+__global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
+    constexpr int BPS = Mfma<FMT>::BPS;
+    __shared__ f32x4 red[kWaves][TC][32];
+
+    const int lane = (int)threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int n = lane & 15;  // weight row within the tile (B column) = A row
+    const int g = lane >> 4;  // lane group: quarter of the K slice
+    const int t = p.t, nb = p.nb, n_in = p.n_in;
+    const int64_t row_bytes = mfma_row_bytes<FMT>(n_in);
+
+    // A operand row n: hi of token n (n < 8) or lo of token n - 8; rows of
+    // tokens >= t read zeros
+    const int tok = n & 7;
+    const uint32_t lo_mask = n >= 8 ? 0xFFFFFFFFu : 0u;
+    const bool xrow_ok = tok < t;
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(p.x, (uint32_t)(t * n_in * 4));
+    const uint32_t xoff0 = (uint32_t)((tok * n_in + slot_code<FMT>(g, 0)) * 4);
+    const uint32_t xoff1 = (uint32_t)((tok * n_in + slot_code<FMT>(g, 4)) * 4);
+
+    // this workgroup's tiles and this wave's K steps
+    const int T = p.tiles_total, G = (int)gridDim.x;
+    const int ta = (int)((int64_t)blockIdx.x * T / G);
+    const int tb = (int)((int64_t)(blockIdx.x + 1) * T / G);
+    // wave w takes steps w, w + 8, ...: at any time the workgroup reads 8
+    // consecutive 64-byte steps (512 contiguous bytes) of every row, so the
+    // two halves of a 128-byte line are requested together
+    const int S = p.steps;
+    const int Sw = wave < S ? (S - wave + kWaves - 1) / kWaves : 0;
+
+    auto chunk_at = [&](int start) {
+        Chunk c;
+        c.start = start;
+        c.j = 0;
+#pragma unroll
+        for (int q = 1; q < kMaxJobs; ++q)
+            if (q < p.n_jobs && start >= p.tile0[q]) c.j = q;
+        c.cnt = start < tb ? min(TC, min(tb, p.tile0[c.j + 1]) - start) : 0;
+        c.lrow0 = (start - p.tile0[c.j]) * kTile;
+        return c;
+    };
+
+    // ---- register ring: one step of every tile of a chunk, plus x ----
+    uint4 wc[TC];
+    uint32_t ws[TC];
+    uint4 xr[BPS][2];
+
+    // issue side: chunk, step and the chunk's buffer descriptors
+    Chunk ic = chunk_at(ta);
+    int is = wave;
+    __amdgpu_buffer_rsrc_t crs, srs;
+    int ic_nout;  // rows of the issue chunk's job
+    auto set_rsrc = [&]() {
+        const KJob &jb = p.job[ic.j];
+        ic_nout = jb.n_out;
+        const int64_t rows = ic.cnt > 0 ? jb.n_out : 0;
+        crs = make_rsrc(jb.codes, (uint32_t)(rows * row_bytes));
+        srs = make_rsrc(jb.scales, (uint32_t)(rows * nb * (FMT == FMT_Q8 ? 4 : 2)));
+    };
+    set_rsrc();
+    auto issue_x = [&]() {
+#pragma unroll
+        for (int jb = 0; jb < BPS; ++jb) {
+            const int b = BPS * is + jb;
+            const bool ok = xrow_ok && ic.cnt > 0 && b < nb;
+            xr[jb][0] = bload16(xrs, ok ? xoff0 + (uint32_t)b * 128u : kOut);
+            xr[jb][1] = bload16(xrs, ok ? xoff1 + (uint32_t)b * 128u : kOut);
+        }
+    };
+    auto issue_w = [&](int r) {
+        const int kb = 4 * is + g;  // 16-byte chunk of the row this lane fetches
+        const int row = ic.lrow0 + kTile * r + n;
+        const bool row_ok = r < ic.cnt && row < ic_nout;
+        const bool ok = row_ok && (int64_t)kb * 16 < row_bytes;
+        wc[r] = bload16(crs, ok ? (uint32_t)(row * row_bytes + kb * 16) : kOut);
+        if constexpr (FMT == FMT_Q4) {
+            // this lane's 16 bytes are block kb
+            ws[r] = __builtin_amdgcn_raw_buffer_load_b16(srs, ok ? (uint32_t)((row * nb + kb) * 2) : kOut, 0, 0);
+        } else if constexpr (FMT == FMT_Q8) {
+            // this lane's 16 bytes are half of block 2s + g/2
+            const int blk = 2 * is + (g >> 1);
+            ws[r] = __builtin_amdgcn_raw_buffer_load_b32(srs, row_ok && blk < nb ? (uint32_t)((row * nb + blk) * 4) : kOut,
+                                                         0, 0);
+        }
+    };
+    auto advance = [&](Chunk &c, int &s) {
+        s += kWaves;
+        if (s >= S) {
+            s = wave;
+            c = chunk_at(c.start + max(c.cnt, 1));
+        }
+    };
+
+    f32x4 acc[TC];
+#pragma unroll
+    for (int r = 0; r < TC; ++r) acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // ---- end of a chunk: sum the 8 waves' partials per tile through LDS ----
+    auto reduce = [&](const Chunk &c) {
+#pragma unroll
+        for (int r = 0; r < TC; ++r) {
+            if (r < c.cnt) {
+                // rows 8..15 (lo) of lanes 32..63 onto rows 0..7 of lanes 0..31
+                // (whole-vector bit casts only, see bload16)
+                const uint4 ai = __builtin_bit_cast(uint4, acc[r]);
+                const uint32_t av[4] = {ai.x, ai.y, ai.z, ai.w};
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const auto h = __builtin_amdgcn_permlane32_swap(av[e], av[e], false, false);
+                    const f32x2 hf = __builtin_bit_cast(f32x2, h);
+                    v[e] = hf[0] + hf[1];
+                }
+                if (lane < 32) red[wave][r][lane] = v;
+            }
+            acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();
+        const float *redf = reinterpret_cast<const float *>(&red[0][0][0]);
+        const KJob &jb = p.job[c.j];
+        for (int r = wave; r < c.cnt; r += kWaves) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i = 4 * h + (lane >> 4);  // token
+                const int row = c.lrow0 + kTile * r + n;
+                if (i < t && row < jb.n_out) {
+                    // token i, row n sits in lane 16 * (i / 4) + n, element i % 4
+                    const int slot = 16 * (i >> 2) + n, e = i & 3;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int w = 0; w < kWaves; ++w) sum += redf[((w * TC + r) * 32 + slot) * 4 + e];
+                    // Q4 codes entered the MFMAs multiplied by 16
+                    jb.y[(int64_t)i * jb.n_out + row] = FMT == FMT_Q4 ? sum * 0.0625f : sum;
+                }
+            }
+        }
+        __syncthreads();  // red is rewritten by the next chunk
+    };
+
+    // ---- one step of one tile ----
+    auto consume = [&](int r, const bf16x8 (&a)[BPS]) {
+        if constexpr (FMT == FMT_BF16) {
+            acc[r] = mfma(a[0], __builtin_bit_cast(bf16x8, wc[r]), acc[r]);
+        } else if constexpr (FMT == FMT_Q8) {
+            uint32_t d0 = wc[r].x, d1 = wc[r].y, d2 = wc[r].z, d3 = wc[r].w;
+            xpose4(d0, d1, d2, d3);
+            // lane groups 0,1 hold block 2s's scale, groups 2,3 block 2s+1's
+            const auto sc = __builtin_amdgcn_permlane32_swap(ws[r], ws[r], false, false);
+            const f32x2 scf = __builtin_bit_cast(f32x2, sc);  // whole-vector cast (see bload16)
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 p0 = mfma(a[0], q8_to_bf16(d0, d1), z);
+            const f32x4 p1 = mfma(a[1], q8_to_bf16(d2, d3), z);
+            // both MFMAs issue before the first read of a result
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(scf[1], p1[e], fmaf(scf[0], p0[e], acc[r][e]));
+        } else {
+            uint32_t d[4] = {wc[r].x, wc[r].y, wc[r].z, wc[r].w};
+            xpose4(d[0], d[1], d[2], d[3]);
+            // every lane gets the scales of blocks 4s..4s+3 of its row
+            const auto x32 = __builtin_amdgcn_permlane32_swap(ws[r], ws[r], false, false);
+            const auto y0 = __builtin_amdgcn_permlane16_swap(x32[0], x32[0], false, false);
+            const auto y1 = __builtin_amdgcn_permlane16_swap(x32[1], x32[1], false, false);
+            const uint32_t sb[4] = {y0[0], y0[1], y1[0], y1[1]};
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4 pj[4];
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) pj[jb] = mfma(a[jb], q4_to_bf16(d[jb]), z);
+            // all four MFMAs issue before the first read of a result, so the
+            // scaling of block 0 overlaps the matrix core's work on 1..3
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[jb]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(sf, pj[jb][e], acc[r][e]);
+            }
+        }
+    };
+
+    if (Sw == 0) {
+        for (Chunk c = chunk_at(ta); c.cnt > 0; c = chunk_at(c.start + c.cnt)) reduce(c);
+        return;
+    }
+
+    // Units (chunk, step) in order; the loads of the next unit are issued
+    // while the current one is consumed: x first, then each tile's weights
+    // right after that tile's registers are consumed.  No branch surrounds a
+    // load, so the in-order vector-memory counter keeps a whole step of
+    // loads in flight.
+    issue_x();
+#pragma unroll
+    for (int r = 0; r < TC; ++r) issue_w(r);
+    Chunk cc = ic;
+    int cs = is;
+    advance(ic, is);
+    set_rsrc();
+    while (cc.cnt > 0) {
+        bf16x8 a[BPS];
+#pragma unroll
+        for (int jb = 0; jb < BPS; ++jb) a[jb] = x_frag(xr[jb][0], xr[jb][1], lo_mask);
+        issue_x();
+#pragma unroll
+        for (int r = 0; r < TC; ++r) {
+            if (r < cc.cnt) consume(r, a);
+            issue_w(r);
+        }
+        const bool chunk_end = cs + kWaves >= S;
+        if (chunk_end) reduce(cc);
+        cc = ic;
+        cs = is;
+        advance(ic, is);
+        set_rsrc();
+    }
+}
+
+}  // namespace
+
+bool gemv_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
+    if (t < 1 || t > kGemvMaxT || n_in <= 0 || n_in % kBlock) return false;
+    const int64_t rb = fmt == FMT_BF16 ? 2ll * n_in : fmt == FMT_Q8 ? (int64_t)n_in : n_in / 2;
+    const int64_t sb = fmt == FMT_Q8 ? 4 : 2;
+    if (4ll * t * n_in >= (1ll << 31)) return false;
+    // every buffer offset a lane forms stays below 2^31
+    for (int j = 0; j < n_jobs; ++j)
+        if ((int64_t)jobs[j].n_out * rb >= (1ll << 31) || (int64_t)jobs[j].n_out * (n_in / kBlock) * sb >= (1ll << 31))
+            return false;
+    return true;
+}
+
+hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
+                            int cu_count, hipStream_t s) {
+    if (!gemv_mfma_fits(fmt, t, n_in, jobs, n_jobs) || n_jobs < 1 || n_jobs > kMaxJobs) return hipErrorInvalidValue;
+    MfmaParams p{};
+    p.x = x;
+    p.t = t;
+    p.n_in = n_in;
+    p.nb = n_in / kBlock;
+    const int bps = fmt == FMT_BF16 ? 1 : fmt == FMT_Q8 ? 2 : 4;
+    p.steps = (p.nb + bps - 1) / bps;
+    p.n_jobs = n_jobs;
+    int tiles = 0;
+    for (int j = 0; j < n_jobs; ++j) {
+        p.job[j] = jobs[j];
+        p.tile0[j] = tiles;
+        tiles += (jobs[j].n_out + kTile - 1) / kTile;
+    }
+    for (int j = n_jobs; j <= kMaxJobs; ++j) p.tile0[j] = tiles;
+    p.tiles_total = tiles;
+    if (tiles == 0) return hipSuccess;
+    // one workgroup per compute unit at most, each an equal share of the tiles
+    const int grid = tiles < cu_count ? tiles : cu_count;
+    switch (fmt) {
+        case FMT_BF16: hipLaunchKernelGGL((gemv_mfma_kernel<FMT_BF16, kChunk>), dim3(grid), dim3(kThreads), 0, s, p); break;
+        case FMT_Q8: hipLaunchKernelGGL((gemv_mfma_kernel<FMT_Q8, kChunk>), dim3(grid), dim3(kThreads), 0, s, p); break;
+        default: hipLaunchKernelGGL((gemv_mfma_kernel<FMT_Q4, kChunk>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace il

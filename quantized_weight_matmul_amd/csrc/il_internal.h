@@ -54,6 +54,13 @@ hipError_t launch_repack_q4(const uint8_t *staging, uint8_t *codes, uint16_t *sc
 hipError_t launch_gemv(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
                        int cu_count, hipStream_t s);
 
+// ---- decode GEMV on the bf16 matrix cores, t <= kGemvMaxT (il_gemv_mfma.hip) ----
+// Same contract as launch_gemv.  gemv_mfma_fits says whether the kernel's
+// 32-bit buffer offsets cover x and every job's weight planes.
+bool gemv_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs);
+hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
+                            int cu_count, hipStream_t s);
+
 // ---- prefill GEMM, t > kGemvMaxT (il_gemm.hip) ----
 hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
                        int cu_count, hipStream_t s);

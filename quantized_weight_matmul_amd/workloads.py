@@ -52,8 +52,9 @@ def rng_for(cfg: int, tensor_id: int) -> np.random.Generator:
 # ----------------------------------------------------------------- encoders
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round finite f32 values to bfloat16 bit patterns (nearest, ties to even)."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    # finite patterns stay below 2^32 after the rounding increment
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return u.astype(np.uint16)
 
 

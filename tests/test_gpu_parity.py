@@ -6,6 +6,10 @@ launch configuration the benchmark times.  Plus device-side closed forms and
 invariants: one-hot / identity W, zero codes, determinism, batch-composition
 invariance, power-of-two scaling, full coverage of y, no writes outside y,
 and the validation paths that must leave y untouched.
+
+Decode (t <= 8) has two kernel families, the f32 streaming kernel ("valu")
+and the matrix-core kernel ("mfma"); the library picks one per format and t,
+and IL_DECODE pins it, so decode cases run under both.
 """
 import numpy as np
 import pytest
@@ -27,6 +31,29 @@ def _bf16_rne(a):
     """f32 -> nearest bf16 value (ties to even), as f32."""
     bits = wl.f32_to_bf16_bits(a).astype(np.uint32) << 16
     return bits.view(np.float32)
+
+
+def _hi_lo(a):
+    """The x the matrix-core decode kernel multiplies: bf16(x) + bf16(x - bf16(x)), in f32."""
+    hi = _bf16_rne(a)
+    return (hi + _bf16_rne((a - hi).astype(np.float32))).astype(np.float32)
+
+
+def _decode_cases(ts):
+    """(t, path) pairs: both decode families for t <= 8, the GEMM beyond."""
+    return [(t, p) for t in ts for p in (("valu", "mfma") if t <= 8 else ("gemm",))]
+
+
+def _pin(monkeypatch, path):
+    if path in ("valu", "mfma"):
+        monkeypatch.setenv("IL_DECODE", path)
+
+
+def _selected(x, path):
+    """What a one-hot weight row returns for x on each path."""
+    if path == "valu":
+        return x
+    return _hi_lo(x) if path == "mfma" else _bf16_rne(x)
 
 
 # ------------------------------------------------------------- workloads
@@ -67,13 +94,14 @@ def _rand_weight(fmt, g, n_out, n_in):
 
 
 @pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
-@pytest.mark.parametrize("t", [1, 2, 3, 5, 8, 9, 16, 33, 130, 257])
-def test_odd_shapes(fmt, t):
+@pytest.mark.parametrize("t,path", _decode_cases([1, 2, 3, 5, 8, 9, 16, 33, 130, 257]))
+def test_odd_shapes(fmt, t, path, monkeypatch):
     """Several tiles plus ragged tails in every dimension, three jobs per call."""
+    _pin(monkeypatch, path)
     g = np.random.default_rng(1000 + 10 * t + fmt)
     for n_in in (32, 288, 4160):
         n_outs = [1, 17, 1000] if n_in < 4160 else [200, 129]
-        say(f"[odd] fmt={FMT_NAME[fmt]} t={t} n_in={n_in} n_outs={n_outs}")
+        say(f"[odd] fmt={FMT_NAME[fmt]} t={t} path={path} n_in={n_in} n_outs={n_outs}")
         x = g.standard_normal((t, n_in)).astype(np.float32)
         ws = [_rand_weight(fmt, g, n, n_in) for n in n_outs]
         hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
@@ -97,8 +125,10 @@ def test_mixed_formats_one_call():
             check_full(y, x, w, f, n, what=f"mixed t {t} fmt {f}")
 
 
-def test_many_jobs_one_call():
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_many_jobs_one_call(path, monkeypatch):
     """More jobs than one launch's job table holds."""
+    _pin(monkeypatch, path)
     g = np.random.default_rng(6)
     n_in, t = 64, 2
     n_outs = [3 + 5 * i for i in range(19)]
@@ -108,6 +138,25 @@ def test_many_jobs_one_call():
     ys = run(x, hs, n_outs)
     for w, n, y in zip(ws, n_outs, ys):
         check_full(y, x, w, BF16, n, what=f"many jobs n_out {n}")
+
+
+@pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
+@pytest.mark.parametrize("t", [2, 5, 8])
+def test_mfma_decode_many_tiles(fmt, t, monkeypatch):
+    """More 16-row tiles than workgroups (several tile groups per workgroup),
+    a workgroup's tile range crossing from one job into the next, a ragged
+    last tile, and a K range (33 blocks) that splits unevenly over the waves."""
+    _pin(monkeypatch, "mfma")
+    g = np.random.default_rng(1500 + 10 * t + fmt)
+    n_in = 1056
+    n_outs = [20000, 777, 31]
+    say(f"[mfma tiles] fmt={FMT_NAME[fmt]} t={t} n_in={n_in} n_outs={n_outs}")
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    ws = [_rand_weight(fmt, g, n, n_in) for n in n_outs]
+    hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
+    ys = run(x, hs, n_outs)
+    for w, n, y in zip(ws, n_outs, ys):
+        check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_out {n}")
 
 
 # ----------------------------------------------------- closed forms on GPU
@@ -127,33 +176,36 @@ def _onehot(fmt, n_out, n_in, cols):
 
 
 @pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
-@pytest.mark.parametrize("t", [1, 3, 8, 9, 200])
-def test_onehot_selects_columns(fmt, t):
-    """One-hot W: y[:, r] = x[:, c_r] exactly on the f32 decode path, and
-    = bf16(x[:, c_r]) exactly on the MFMA path (x rounded to bf16)."""
+@pytest.mark.parametrize("t,path", _decode_cases([1, 3, 8, 9, 200]))
+def test_onehot_selects_columns(fmt, t, path, monkeypatch):
+    """One-hot W: y[:, r] = x[:, c_r] exactly on the f32 decode path, the
+    bf16 hi + lo split of it on the matrix-core decode path, and bf16(x)
+    on the GEMM path."""
+    _pin(monkeypatch, path)
     g = np.random.default_rng(20 + t)
     n_in, n_out = 320, 300
     cols = g.integers(0, n_in, n_out)
     x = g.standard_normal((t, n_in)).astype(np.float32)
     (h,) = upload_all([_onehot(fmt, n_out, n_in, cols)], [fmt], [n_out], n_in)
     (y,) = run(x, [h], [n_out])
-    want = x[:, cols] if t <= 8 else _bf16_rne(x)[:, cols]
-    assert np.array_equal(y, want)
+    assert np.array_equal(y, _selected(x, path)[:, cols])
 
 
-@pytest.mark.parametrize("t", [2, 64])
-def test_identity(t):
+@pytest.mark.parametrize("t,path", _decode_cases([2, 64]))
+def test_identity(t, path, monkeypatch):
+    _pin(monkeypatch, path)
     g = np.random.default_rng(30)
     n = 256
     x = g.standard_normal((t, n)).astype(np.float32)
     for fmt in (BF16, Q8, Q4):
         (h,) = upload_all([_onehot(fmt, n, n, np.arange(n))], [fmt], [n], n)
         (y,) = run(x, [h], [n])
-        assert np.array_equal(y, x if t <= 8 else _bf16_rne(x)), f"identity fmt {fmt}"
+        assert np.array_equal(y, _selected(x, path)), f"identity fmt {fmt}"
 
 
-@pytest.mark.parametrize("t", [1, 5, 70])
-def test_zero_codes_give_exact_zeros(t):
+@pytest.mark.parametrize("t,path", _decode_cases([1, 5, 70]))
+def test_zero_codes_give_exact_zeros(t, path, monkeypatch):
+    _pin(monkeypatch, path)
     g = np.random.default_rng(40)
     n_out, n_in = 96, 512
     nb = n_in // 32
@@ -166,8 +218,10 @@ def test_zero_codes_give_exact_zeros(t):
         assert np.all(y == 0)
 
 
-def test_row_sums_with_x_one():
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_row_sums_with_x_one(path, monkeypatch):
     """x = 1: y[r] = sum_k w[r][k]; Q4 codes k % 16 give -16 per block."""
+    _pin(monkeypatch, path)
     n_out, n_in = 40, 1024
     nb = n_in // 32
     k = np.arange(n_in)
@@ -181,8 +235,9 @@ def test_row_sums_with_x_one():
 
 
 # ------------------------------------------------------------- invariants
-@pytest.mark.parametrize("t", [1, 4, 8, 24, 300])
-def test_deterministic_and_batch_invariant(t):
+@pytest.mark.parametrize("t,path", _decode_cases([1, 4, 8, 24, 300]))
+def test_deterministic_and_batch_invariant(t, path, monkeypatch):
+    _pin(monkeypatch, path)
     g = np.random.default_rng(50 + t)
     n_in = 1024
     n_outs = [512, 130, 96]
@@ -198,8 +253,9 @@ def test_deterministic_and_batch_invariant(t):
     assert np.array_equal(a[0], alone[0]), "result depends on the other jobs in the batch"
 
 
-@pytest.mark.parametrize("t", [2, 96])
-def test_power_of_two_scaling(t):
+@pytest.mark.parametrize("t,path", _decode_cases([2, 96]))
+def test_power_of_two_scaling(t, path, monkeypatch):
+    _pin(monkeypatch, path)
     g = np.random.default_rng(60)
     n_in, n_out = 512, 256
     x = g.standard_normal((t, n_in)).astype(np.float32)
@@ -210,11 +266,12 @@ def test_power_of_two_scaling(t):
         assert np.array_equal(y2, y1 * np.float32(8.0)), f"fmt {fmt}"
 
 
-@pytest.mark.parametrize("t", [3, 20])
-def test_writes_exactly_y(t):
+@pytest.mark.parametrize("t,path", _decode_cases([3, 20]))
+def test_writes_exactly_y(t, path, monkeypatch):
     """Every y element is written (NaN sentinel gone) and nothing around y is
     (guard bands of a larger buffer keep their canary value)."""
     import torch
+    _pin(monkeypatch, path)
     g = np.random.default_rng(70)
     n_in, n_out = 256, 333
     x_np = g.standard_normal((t, n_in)).astype(np.float32)
