@@ -35,24 +35,26 @@ typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kBig = 256;  // side of the work tiles the job table is cut into
+constexpr int BK = 64;
 constexpr int kXcds = 8;
-constexpr int kChunks = BM * BK / 8 / kThreads;  // 16-byte chunks per thread per operand tile
 constexpr uint32_t kBufFlags = 0x00020000u;
 constexpr uint32_t kOut = 0x7FFFFFF0u;  // a buffer offset past every range: reads 0
 
+// One launch covers big tiles [tile_lo, tile_lo + n_units) of the
+// kBig x kBig tile grid (tile = tn * tiles_m + tm), or, for the 128 x 128
+// kernel, the four quarters of each of them (unit = 4 * tile + quarter).
 struct GemmParams {
     const uint16_t *xb;  // bf16 x [t][n_in]
     int t;
     int n_in;
     int n_jobs;
-    int tiles_m;
-    int tiles_total;
-    int tiles_per_xcd;
+    int tiles_m;        // kBig-row tiles of x
+    int tile_lo;        // first big tile of this launch
+    int n_units;        // work units (workgroups with work) of this launch
+    int units_per_xcd;  // ceil(n_units / kXcds)
     KJob job[kMaxJobs];
-    int tn0[kMaxJobs + 1];  // prefix sums of n-tiles per job
+    int tn0[kMaxJobs + 1];  // prefix sums of kBig-column tiles per job
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -84,30 +86,40 @@ __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float *__restrict_
     xb[i] = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
 }
 
-template <int FMT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][BM * BK];  // [stage][A|B]
+template <int FMT, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
+    constexpr int kThreads = 64 * WM * WN;
+    constexpr int kChunksA = BM * BK / 8 / kThreads;  // 16-byte chunks per thread, A tile
+    constexpr int kChunksB = BN * BK / 8 / kThreads;  // same, bf16 B tile
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
+    constexpr bool kQuarter = BM < kBig;
+    static_assert(kThreads == 2 * BN, "Q8/Q4 staging: two threads per B row");
+    static_assert(kChunksA >= 1 && kChunksB >= 1 && (kThreads / 8) % 16 == 0, "staging shape");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][(BM > BN ? BM : BN) * BK];  // [stage][A|B]
 
-    // ---- workgroup -> tile, XCD by XCD ----
+    // ---- workgroup -> work unit, XCD by XCD ----
     const int b = blockIdx.x;
-    const int tile = (b % kXcds) * p.tiles_per_xcd + b / kXcds;
-    if (tile >= p.tiles_total) return;
+    const int unit = (b % kXcds) * p.units_per_xcd + b / kXcds;
+    if (unit >= p.n_units) return;
+    const int tile = p.tile_lo + (kQuarter ? unit >> 2 : unit);
+    const int q = kQuarter ? unit & 3 : 0;
     const int tn_all = tile / p.tiles_m;
     const int tm = tile - tn_all * p.tiles_m;
     int j = 0;
 #pragma unroll
-    for (int q = 1; q < kMaxJobs; ++q)
-        if (q < p.n_jobs && tn_all >= p.tn0[q]) j = q;
+    for (int jj = 1; jj < kMaxJobs; ++jj)
+        if (jj < p.n_jobs && tn_all >= p.tn0[jj]) j = jj;
     const KJob jb = p.job[j];
-    const int m0 = tm * BM;
-    const int n0 = (tn_all - p.tn0[j]) * BN;
+    const int m0 = tm * kBig + (q >> 1) * BM;
+    const int n0 = (tn_all - p.tn0[j]) * kBig + (q & 1) * BN;
+    if (m0 >= p.t || n0 >= jb.n_out) return;  // a quarter past the edge of x or W
     const int n_in = p.n_in;
     const int nb = n_in / kBlock;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 wave grid, 128 x 64 per wave
+    const int wm = wave / WN, wn = wave % WN;  // WM x WN wave grid
 
     // ---- operand descriptors: exactly the tile's valid rows ----
     const int a_rows = min(BM, p.t - m0);
@@ -130,26 +142,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                         (uint32_t)b_rows * (uint32_t)nb * 2u);
     }
 
-    // bf16 staging: chunk i of this thread is row crow0 + 64 i, 16-byte chunk
-    // cc, so 8 consecutive threads read one 128-byte row segment.  Q8/Q4
+    // bf16 staging: chunk i of this thread is row crow0 + (threads / 8) i,
+    // 16-byte chunk cc, so 8 consecutive threads read one 128-byte row
+    // segment.  Q8/Q4
     // staging: this thread owns row tid / 2, elements 32 (tid % 2) .. +31 of
     // the step (one quantisation block).
     const int crow0 = tid >> 3, cc = tid & 7;
-    const int cslot = cc ^ swz_key(crow0);  // rows crow0 + 64 i share the key
+    const int cslot = cc ^ swz_key(crow0);  // rows crow0 + (threads / 8) i share the key
     const int qr = tid >> 1, qh = tid & 1;
     const int qkey = swz_key(qr);
 
-    uint4 sa[kChunks];
-    uint4 sb[FMT == FMT_BF16 ? kChunks : (FMT == FMT_Q8 ? 2 : 1)];
+    uint4 sa[kChunksA];
+    uint4 sb[FMT == FMT_BF16 ? kChunksB : (FMT == FMT_Q8 ? 2 : 1)];
     float ssc = 0.f;
     auto fetch = [&](int k0) {
         const int k = k0 + cc * 8;
         const bool kok = k < n_in;
 #pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const uint32_t off = kok ? (uint32_t)(crow0 + (kThreads / 8) * i) * row2 + (uint32_t)k * 2u : kOut;
-            sa[i] = bload16(ars, off);
-            if constexpr (FMT == FMT_BF16) sb[i] = bload16(brs, off);
+        for (int i = 0; i < kChunksA; ++i)
+            sa[i] = bload16(ars, kok ? (uint32_t)(crow0 + (kThreads / 8) * i) * row2 + (uint32_t)k * 2u : kOut);
+        if constexpr (FMT == FMT_BF16) {
+#pragma unroll
+            for (int i = 0; i < kChunksB; ++i)
+                sb[i] = bload16(brs, kok ? (uint32_t)(crow0 + (kThreads / 8) * i) * row2 + (uint32_t)k * 2u : kOut);
         }
         if constexpr (FMT != FMT_BF16) {
             const int kh = k0 + 32 * qh;
@@ -170,10 +185,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     };
     auto store = [&](uint16_t *As, uint16_t *Bs) {
 #pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int off = (crow0 + (kThreads / 8) * i) * BK + cslot * 8;
-            *reinterpret_cast<uint4 *>(As + off) = sa[i];
-            if constexpr (FMT == FMT_BF16) *reinterpret_cast<uint4 *>(Bs + off) = sb[i];
+        for (int i = 0; i < kChunksA; ++i)
+            *reinterpret_cast<uint4 *>(As + (crow0 + (kThreads / 8) * i) * BK + cslot * 8) = sa[i];
+        if constexpr (FMT == FMT_BF16) {
+#pragma unroll
+            for (int i = 0; i < kChunksB; ++i)
+                *reinterpret_cast<uint4 *>(Bs + (crow0 + (kThreads / 8) * i) * BK + cslot * 8) = sb[i];
         }
         if constexpr (FMT != FMT_BF16) {
             uint32_t o[16];
@@ -202,32 +219,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         }
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int n = 0; n < 2; ++n) acc[a][n] = (f32x16){};
+        for (int n = 0; n < TN; ++n) acc[a][n] = (f32x16){};
 
     // 32x32x16 fragments: lane reads row (lane & 31) of a 32-row tile, 16-byte
     // chunk 2 kk + lane / 32; every fragment row of this lane shares one
     // swizzle key because tile offsets are multiples of 32
     const int frow = lane & 31;
     const int fkey = swz_key(frow);
-    const int a_base = (wm * 128 + frow) * BK;
-    const int b_base = (wn * 64 + frow) * BK;
+    const int a_base = (wm * (BM / WM) + frow) * BK;
+    const int b_base = (wn * (BN / WN) + frow) * BK;
     auto compute = [&](const uint16_t *As, const uint16_t *Bs) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             const int slot = (kk * 2 + (lane >> 5)) ^ fkey;
-            bf16x8 fa[4], fb[2];
+            bf16x8 fa[TM], fb[TN];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) fa[a] = *reinterpret_cast<const bf16x8 *>(As + a_base + a * 32 * BK + slot * 8);
+            for (int a = 0; a < TM; ++a) fa[a] = *reinterpret_cast<const bf16x8 *>(As + a_base + a * 32 * BK + slot * 8);
 #pragma unroll
-            for (int n = 0; n < 2; ++n) fb[n] = *reinterpret_cast<const bf16x8 *>(Bs + b_base + n * 32 * BK + slot * 8);
+            for (int n = 0; n < TN; ++n) fb[n] = *reinterpret_cast<const bf16x8 *>(Bs + b_base + n * 32 * BK + slot * 8);
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < TM; ++a)
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
+                for (int n = 0; n < TN; ++n)
                     acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[n], acc[a][n], 0, 0, 0);
         }
     };
@@ -250,41 +267,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     // ---- epilogue: 32x32 tile, lane holds rows 8 (i / 4) + 4 (lane / 32) + i % 4
     //      of column lane % 32 ----
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < TM; ++a) {
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int col = n0 + wn * 64 + n * 32 + (lane & 31);
+        for (int n = 0; n < TN; ++n) {
+            const int col = n0 + wn * (BN / WN) + n * 32 + (lane & 31);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int row = m0 + wm * 128 + a * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+                const int row = m0 + wm * (BM / WM) + a * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
                 if (row < p.t && col < jb.n_out) jb.y[(int64_t)row * jb.n_out + col] = acc[a][n][i];
             }
         }
     }
 }
 
+template <int FMT>
+hipError_t launch_units(GemmParams p, bool quarter, int tile_lo, int n_units, hipStream_t s) {
+    p.tile_lo = tile_lo;
+    p.n_units = n_units;
+    p.units_per_xcd = (n_units + kXcds - 1) / kXcds;
+    const dim3 grid(kXcds * p.units_per_xcd);
+    if (quarter)
+        hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 2>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel<FMT, kBig, kBig, 2, 4>), grid, dim3(512), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_plan(const GemmParams &p, int tiles, int cu_count, hipStream_t s) {
+    // Whole rounds of big tiles (one per compute unit at a time); what is
+    // left over, less than one round, runs as quarter tiles so that the last
+    // round is short instead of mostly idle.
+    const int full = tiles >= cu_count ? tiles / cu_count * cu_count : 0;
+    hipError_t e = hipSuccess;
+    if (full > 0) e = launch_units<FMT>(p, false, 0, full, s);
+    if (e == hipSuccess && tiles > full) e = launch_units<FMT>(p, true, full, 4 * (tiles - full), s);
+    return e;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
                        int cu_count, hipStream_t s) {
-    (void)cu_count;
-    if (t < 1 || n_jobs < 1 || n_jobs > kMaxJobs || n_in % kBlock) return hipErrorInvalidValue;
-    // every buffer descriptor (256 rows of x or of a weight) must stay below 2^31 bytes
-    if ((int64_t)BM * n_in * 2 >= (1ll << 31)) return hipErrorInvalidValue;
+    if (t < 1 || n_jobs < 1 || n_jobs > kMaxJobs || n_in % kBlock || cu_count < 1) return hipErrorInvalidValue;
+    // every buffer descriptor (kBig rows of x or of a weight) must stay below 2^31 bytes
+    if ((int64_t)kBig * n_in * 2 >= (1ll << 31)) return hipErrorInvalidValue;
     GemmParams p{};
     p.t = t;
     p.n_in = n_in;
     p.n_jobs = n_jobs;
-    p.tiles_m = (t + BM - 1) / BM;
+    p.tiles_m = (t + kBig - 1) / kBig;
     int tn = 0;
     for (int j = 0; j < n_jobs; ++j) {
         p.job[j] = jobs[j];
         p.tn0[j] = tn;
-        tn += (jobs[j].n_out + BN - 1) / BN;
+        tn += (jobs[j].n_out + kBig - 1) / kBig;
     }
     for (int j = n_jobs; j <= kMaxJobs; ++j) p.tn0[j] = tn;
-    p.tiles_total = p.tiles_m * tn;
-    p.tiles_per_xcd = (p.tiles_total + kXcds - 1) / kXcds;
+    const int tiles = p.tiles_m * tn;
 
     // x -> bf16 into stream-ordered scratch, freed after the GEMM on the same stream
     const int64_t n8 = (int64_t)t * n_in / 8;
@@ -296,14 +336,12 @@ hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *job
     e = hipGetLastError();
     if (e == hipSuccess) {
         p.xb = static_cast<const uint16_t *>(xb);
-        const dim3 grid(kXcds * p.tiles_per_xcd);
         switch (fmt) {
-            case FMT_BF16: hipLaunchKernelGGL(gemm_kernel<FMT_BF16>, grid, dim3(kThreads), 0, s, p); break;
-            case FMT_Q8: hipLaunchKernelGGL(gemm_kernel<FMT_Q8>, grid, dim3(kThreads), 0, s, p); break;
-            case FMT_Q4: hipLaunchKernelGGL(gemm_kernel<FMT_Q4>, grid, dim3(kThreads), 0, s, p); break;
+            case FMT_BF16: e = launch_plan<FMT_BF16>(p, tiles, cu_count, s); break;
+            case FMT_Q8: e = launch_plan<FMT_Q8>(p, tiles, cu_count, s); break;
+            case FMT_Q4: e = launch_plan<FMT_Q4>(p, tiles, cu_count, s); break;
             default: e = hipErrorInvalidValue;
         }
-        if (e == hipSuccess) e = hipGetLastError();
     }
     hipError_t fe = hipFreeAsync(xb, s);
     return e != hipSuccess ? e : fe;

@@ -159,6 +159,23 @@ def test_mfma_decode_many_tiles(fmt, t, monkeypatch):
         check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_out {n}")
 
 
+@pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
+def test_gemm_full_rounds_and_tail(fmt):
+    """Prefill with more 256 x 256 tiles than compute units: whole rounds of
+    big tiles plus a tail run as 128 x 128 quarters, with ragged edges in t,
+    in every job's n_out and in K (n_in = 96 is one and a half K steps)."""
+    g = np.random.default_rng(1700 + fmt)
+    t, n_in = 600, 96
+    n_outs = [20000, 2000]
+    say(f"[gemm rounds] fmt={FMT_NAME[fmt]} t={t} n_in={n_in} n_outs={n_outs}")
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    ws = [_rand_weight(fmt, g, n, n_in) for n in n_outs]
+    hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
+    ys = run(x, hs, n_outs)
+    for w, n, y in zip(ws, n_outs, ys):
+        check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_out {n}")
+
+
 # ----------------------------------------------------- closed forms on GPU
 def _onehot(fmt, n_out, n_in, cols):
     if fmt == BF16:
