@@ -189,21 +189,25 @@ il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in) {
 
     const int64_t nb = n_in / il::kBlock;
     const int64_t hb = host_bytes(fmt, n_out, n_in);
-    int64_t code_bytes = 0, scale_bytes = 0;
+    int64_t code_bytes = 0, scale_bytes = 0, scale_size = 0;
     if (fmt == IL_BF16) code_bytes = 2 * n_out * n_in;
-    if (fmt == IL_Q8) code_bytes = n_out * n_in, scale_bytes = 4 * n_out * nb;
-    if (fmt == IL_Q4) code_bytes = n_out * n_in / 2, scale_bytes = 2 * n_out * nb;
+    if (fmt == IL_Q8) code_bytes = n_out * n_in, scale_size = 4;
+    if (fmt == IL_Q4) code_bytes = n_out * n_in / 2, scale_size = 2;
+    scale_bytes = scale_size * n_out * nb;
+    const int64_t tiled_bytes = scale_size * il::tiled_scale_count(n_out, nb);
     const int64_t code_alloc = (code_bytes + 255) / 256 * 256;
+    const int64_t scale_alloc = (scale_bytes + 255) / 256 * 256;
 
     void *alloc = nullptr;
-    hipError_t e = hipMalloc(&alloc, (size_t)(code_alloc + scale_bytes));
+    hipError_t e = hipMalloc(&alloc, (size_t)(code_alloc + scale_alloc + tiled_bytes));
     if (e != hipSuccess) {
-        set_err("il_upload: hipMalloc(%" PRId64 ") failed: %s", code_alloc + scale_bytes,
+        set_err("il_upload: hipMalloc(%" PRId64 ") failed: %s", code_alloc + scale_alloc + tiled_bytes,
                 hipGetErrorString(e));
         return nullptr;
     }
     char *codes = static_cast<char *>(alloc);
     char *scales = scale_bytes ? codes + code_alloc : nullptr;
+    char *scales_t = scale_bytes ? codes + code_alloc + scale_alloc : nullptr;
     hipStream_t s = ctx->upload_stream;
     void *staging = nullptr;
     if (fmt == IL_BF16) {
@@ -211,12 +215,16 @@ il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in) {
     } else {
         e = hipMalloc(&staging, (size_t)hb);
         if (e == hipSuccess) e = hipMemcpyAsync(staging, weight, (size_t)hb, hipMemcpyHostToDevice, s);
+        // the tiled plane's padding (rows past n_out, blocks past nb) reads zero
+        if (e == hipSuccess) e = hipMemsetAsync(scales_t, 0, (size_t)tiled_bytes, s);
         if (e == hipSuccess && fmt == IL_Q8)
             e = il::launch_repack_q8(static_cast<const uint8_t *>(staging), reinterpret_cast<int8_t *>(codes),
-                                     reinterpret_cast<float *>(scales), n_out, n_in, s);
+                                     reinterpret_cast<float *>(scales), reinterpret_cast<float *>(scales_t), n_out,
+                                     n_in, s);
         if (e == hipSuccess && fmt == IL_Q4)
             e = il::launch_repack_q4(static_cast<const uint8_t *>(staging), reinterpret_cast<uint8_t *>(codes),
-                                     reinterpret_cast<uint16_t *>(scales), n_out, n_in, s);
+                                     reinterpret_cast<uint16_t *>(scales), reinterpret_cast<uint16_t *>(scales_t),
+                                     n_out, n_in, s);
     }
     hipError_t se = hipStreamSynchronize(s);
     if (e == hipSuccess) e = se;
@@ -235,6 +243,7 @@ il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in) {
     w->alloc = alloc;
     w->codes = codes;
     w->scales = scales;
+    w->scales_t = scales_t;
     g_uploads++;
     g_upload_bytes += (uint64_t)hb;
     return w;
@@ -357,7 +366,7 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
         for (int64_t j = 0; j < n_jobs; ++j) {
             const il_weight *w = jobs[j].w;
             if (w->fmt != fmt) continue;
-            batch.push_back(il::KJob{w->codes, w->scales, jobs[j].y, (int)w->n_out});
+            batch.push_back(il::KJob{w->codes, w->scales, w->scales_t, jobs[j].y, (int)w->n_out});
             bytes += (uint64_t)w->host_bytes;
             if ((int)batch.size() == il::kMaxJobs && !flush()) {
                 g_failed++;

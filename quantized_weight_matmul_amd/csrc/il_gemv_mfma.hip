@@ -205,6 +205,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     const int n = lane & 15;  // weight row within the tile (B column) = A row
     const int g = lane >> 4;  // lane group: quarter of the K slice
     const int t = p.t, nb = p.nb, n_in = p.n_in;
+    const int nb4 = (nb + 3) / 4;
     const int64_t row_bytes = mfma_row_bytes<FMT>(n_in);
 
     // A operand row n: hi of token n (n < 8) or lo of token n - 8; rows of
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         ic_nout = jb.n_out;
         const int64_t rows = ic.cnt > 0 ? jb.n_out : 0;
         crs = make_rsrc(jb.codes, (uint32_t)(rows * row_bytes));
-        srs = make_rsrc(jb.scales, (uint32_t)(rows * nb * (FMT == FMT_Q8 ? 4 : 2)));
+        srs = make_rsrc(jb.scales_t, (uint32_t)(tiled_scale_count(rows, nb) * (FMT == FMT_Q8 ? 4 : 2)));
     };
     set_rsrc();
     auto issue_x = [&]() {
@@ -271,14 +272,16 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         const bool row_ok = r < ic.cnt && row < ic_nout;
         const bool ok = row_ok && (int64_t)kb * 16 < row_bytes;
         wc[r] = bload16(crs, ok ? (uint32_t)(row * row_bytes + kb * 16) : kOut);
+        // scales from the tiled plane: a tile's 16 rows x 4 blocks are one run
         if constexpr (FMT == FMT_Q4) {
             // this lane's 16 bytes are block kb
-            ws[r] = __builtin_amdgcn_raw_buffer_load_b16(srs, ok ? (uint32_t)((row * nb + kb) * 2) : kOut, 0, 0);
+            ws[r] = __builtin_amdgcn_raw_buffer_load_b16(
+                srs, ok ? (uint32_t)(tiled_scale_index(row, kb, nb4) * 2) : kOut, 0, 0);
         } else if constexpr (FMT == FMT_Q8) {
             // this lane's 16 bytes are half of block 2s + g/2
             const int blk = 2 * is + (g >> 1);
-            ws[r] = __builtin_amdgcn_raw_buffer_load_b32(srs, row_ok && blk < nb ? (uint32_t)((row * nb + blk) * 4) : kOut,
-                                                         0, 0);
+            ws[r] = __builtin_amdgcn_raw_buffer_load_b32(
+                srs, row_ok && blk < nb ? (uint32_t)(tiled_scale_index(row, blk, nb4) * 4) : kOut, 0, 0);
         }
     };
     auto advance = [&](Chunk &c, int &s) {
@@ -421,7 +424,8 @@ bool gemv_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
     if (4ll * t * n_in >= (1ll << 31)) return false;
     // every buffer offset a lane forms stays below 2^31
     for (int j = 0; j < n_jobs; ++j)
-        if ((int64_t)jobs[j].n_out * rb >= (1ll << 31) || (int64_t)jobs[j].n_out * (n_in / kBlock) * sb >= (1ll << 31))
+        if ((int64_t)jobs[j].n_out * rb >= (1ll << 31) ||
+            tiled_scale_count(jobs[j].n_out, n_in / kBlock) * sb >= (1ll << 31))
             return false;
     return true;
 }

@@ -11,6 +11,11 @@
 //          scales = uint16 [n_out][n_in/32]       (f16 bits)
 // Every code row starts 16-byte aligned (n_in % 32 == 0), so one lane can
 // fetch 16 bytes of a row with a single global_load_dwordx4.
+// Q8/Q4 also keep a second copy of the scales in tiles of 16 rows x 4 blocks
+// (the order the matrix-core decode kernel reads them in, one 128- or
+// 256-byte run per tile and step):
+//   scales_t[((row / 16) * nb4 + b / 4) * 64 + (row % 16) * 4 + b % 4],
+//   nb4 = ceil(nb / 4), rows padded to a multiple of 16 (padding is zero).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,21 +37,31 @@ struct Weight {
     int64_t host_bytes;  // WeightRef::bytes of the host format
     void *alloc;         // single device allocation holding both planes
     const void *codes;
-    const void *scales;  // nullptr for BF16
+    const void *scales;    // nullptr for BF16
+    const void *scales_t;  // tiled copy of the scales; nullptr for BF16
 };
+
+// Index of the scale of (row, block b) in the tiled scale plane.
+__host__ __device__ inline int64_t tiled_scale_index(int64_t row, int64_t b, int64_t nb4) {
+    return (((row >> 4) * nb4 + (b >> 2)) << 6) + ((row & 15) << 2) + (b & 3);
+}
+__host__ __device__ inline int64_t tiled_scale_count(int64_t n_out, int64_t nb) {
+    return (n_out + 15) / 16 * ((nb + 3) / 4) * 64;
+}
 
 // One job as the kernels see it.
 struct KJob {
     const void *codes;
     const void *scales;
+    const void *scales_t;
     float *y;
     int n_out;
 };
 
 // ---- upload / repack (il_repack.hip) ----
-hipError_t launch_repack_q8(const uint8_t *staging, int8_t *codes, float *scales, int64_t n_out,
-                            int64_t n_in, hipStream_t s);
-hipError_t launch_repack_q4(const uint8_t *staging, uint8_t *codes, uint16_t *scales,
+hipError_t launch_repack_q8(const uint8_t *staging, int8_t *codes, float *scales, float *scales_t,
+                            int64_t n_out, int64_t n_in, hipStream_t s);
+hipError_t launch_repack_q4(const uint8_t *staging, uint8_t *codes, uint16_t *scales, uint16_t *scales_t,
                             int64_t n_out, int64_t n_in, hipStream_t s);
 
 // ---- decode GEMV, t <= kGemvMaxT (il_gemv.hip) ----

@@ -3,7 +3,8 @@
 //
 // The host bytes are first copied to a device staging buffer; these kernels
 // then split the packed array-of-blocks formats into a K-contiguous code plane
-// and a separate scale plane (layouts in il_internal.h).  Integer byte moves
+// and a separate scale plane, plus a tiled copy of the scales (layouts in
+// il_internal.h).  Integer byte moves
 // only: every value is preserved bit for bit.  BF16 needs no kernel, its host
 // layout is already the device layout.
 #include "il_internal.h"
@@ -15,7 +16,7 @@ namespace {
 // 4-byte aligned (36 = 9 dwords), so the block is read as 9 dwords.
 __global__ void repack_q8_kernel(const uint32_t *__restrict__ staging,
                                  uint4 *__restrict__ codes, float *__restrict__ scales,
-                                 int64_t n_blocks) {
+                                 float *__restrict__ scales_t, int64_t n_blocks, int64_t nb) {
     int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= n_blocks) return;
     const uint32_t *src = staging + b * 9;
@@ -23,6 +24,7 @@ __global__ void repack_q8_kernel(const uint32_t *__restrict__ staging,
 #pragma unroll
     for (int i = 0; i < 9; ++i) d[i] = src[i];
     scales[b] = __builtin_bit_cast(float, d[0]);
+    scales_t[tiled_scale_index(b / nb, b % nb, (nb + 3) / 4)] = __builtin_bit_cast(float, d[0]);
     // block b covers codes[b*32 .. b*32+31]: two 16-byte stores
     codes[2 * b] = make_uint4(d[1], d[2], d[3], d[4]);
     codes[2 * b + 1] = make_uint4(d[5], d[6], d[7], d[8]);
@@ -34,7 +36,7 @@ __global__ void repack_q8_kernel(const uint32_t *__restrict__ staging,
 // with one byte-select conversion.
 __global__ void repack_q4_kernel(const uint16_t *__restrict__ staging,
                                  uint4 *__restrict__ codes, uint16_t *__restrict__ scales,
-                                 int64_t n_blocks) {
+                                 uint16_t *__restrict__ scales_t, int64_t n_blocks, int64_t nb) {
     int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= n_blocks) return;
     const uint16_t *src = staging + b * 9;
@@ -42,6 +44,7 @@ __global__ void repack_q4_kernel(const uint16_t *__restrict__ staging,
 #pragma unroll
     for (int i = 0; i < 9; ++i) h[i] = src[i];
     scales[b] = h[0];
+    scales_t[tiled_scale_index(b / nb, b % nb, (nb + 3) / 4)] = h[0];
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -51,23 +54,23 @@ __global__ void repack_q4_kernel(const uint16_t *__restrict__ staging,
 
 }  // namespace
 
-hipError_t launch_repack_q8(const uint8_t *staging, int8_t *codes, float *scales, int64_t n_out,
-                            int64_t n_in, hipStream_t s) {
-    int64_t nb = n_out * (n_in / kBlock);
-    int64_t grid = (nb + 255) / 256;
+hipError_t launch_repack_q8(const uint8_t *staging, int8_t *codes, float *scales, float *scales_t,
+                            int64_t n_out, int64_t n_in, hipStream_t s) {
+    const int64_t n_blocks = n_out * (n_in / kBlock);
+    const int64_t grid = (n_blocks + 255) / 256;
     hipLaunchKernelGGL(repack_q8_kernel, dim3((unsigned)grid), dim3(256), 0, s,
-                       reinterpret_cast<const uint32_t *>(staging),
-                       reinterpret_cast<uint4 *>(codes), scales, nb);
+                       reinterpret_cast<const uint32_t *>(staging), reinterpret_cast<uint4 *>(codes), scales,
+                       scales_t, n_blocks, n_in / kBlock);
     return hipGetLastError();
 }
 
-hipError_t launch_repack_q4(const uint8_t *staging, uint8_t *codes, uint16_t *scales,
+hipError_t launch_repack_q4(const uint8_t *staging, uint8_t *codes, uint16_t *scales, uint16_t *scales_t,
                             int64_t n_out, int64_t n_in, hipStream_t s) {
-    int64_t nb = n_out * (n_in / kBlock);
-    int64_t grid = (nb + 255) / 256;
+    const int64_t n_blocks = n_out * (n_in / kBlock);
+    const int64_t grid = (n_blocks + 255) / 256;
     hipLaunchKernelGGL(repack_q4_kernel, dim3((unsigned)grid), dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t *>(staging),
-                       reinterpret_cast<uint4 *>(codes), scales, nb);
+                       reinterpret_cast<const uint16_t *>(staging), reinterpret_cast<uint4 *>(codes), scales,
+                       scales_t, n_blocks, n_in / kBlock);
     return hipGetLastError();
 }
 
