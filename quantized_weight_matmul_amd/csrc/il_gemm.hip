@@ -26,6 +26,9 @@
 // its workgroups share.
 #include "il_internal.h"
 
+#include <cstdlib>
+#include <cstring>
+
 namespace il {
 namespace {
 
@@ -336,7 +339,15 @@ hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *job
     e = hipGetLastError();
     if (e == hipSuccess) {
         p.xb = static_cast<const uint16_t *>(xb);
-        switch (fmt) {
+        // IL_PREFILL=gemm|verify pins the kernel for mid-size t
+        bool verify = t <= kVerifyMaxT;
+        if (const char *force = getenv("IL_PREFILL")) {
+            if (!strcmp(force, "gemm")) verify = false;
+            if (!strcmp(force, "verify")) verify = true;
+        }
+        if (verify && verify_mfma_fits(fmt, t, n_in, jobs, n_jobs))
+            e = launch_verify_mfma(fmt, p.xb, t, n_in, jobs, n_jobs, cu_count, s);
+        else switch (fmt) {
             case FMT_BF16: e = launch_plan<FMT_BF16>(p, tiles, cu_count, s); break;
             case FMT_Q8: e = launch_plan<FMT_Q8>(p, tiles, cu_count, s); break;
             case FMT_Q4: e = launch_plan<FMT_Q4>(p, tiles, cu_count, s); break;

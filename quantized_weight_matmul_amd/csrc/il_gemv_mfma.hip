@@ -1,4 +1,5 @@
-// il_gemv_mfma.hip -- decode GEMV on the bf16 matrix cores (small t > 1).
+// il_gemv_mfma.hip -- decode GEMV on the bf16 matrix cores (small t > 1),
+// and its "wide" mode for mid-size t (speculative-verify batches, 8 < t <= 32).
 //
 // Computes the same sums as the streaming decode kernel,
 //   y[i][r] = sum_b s_rb * sum_{k in block b} (q_rk - z) * x_ik
@@ -25,6 +26,11 @@
 //     that stay in L2), one step ahead, in the per-lane order of the MFMA.
 //   * The per-block scale multiplies the 16 x 16 f32 result (one FMA per
 //     accumulator element), so no rounding of a dequantised weight occurs.
+//   * Wide mode (8 < t <= 32): A rows are 16 tokens of bf16(x) per group,
+//     read from the bf16 copy of x the prefill path makes anyway (x rounded
+//     to bf16 as on the GEMM path), and one converted B operand feeds one
+//     or two groups of MFMAs, so the weight conversion is shared by up to
+//     32 tokens.
 //
 // Loads: a wave fetches 16 bytes per lane, 64 bytes of each of 16 rows (one
 // bf16 block, two Q8 blocks or four Q4 blocks per row: one "step").  Lane
@@ -36,8 +42,8 @@
 // by slot.
 //
 // Work split: a workgroup of 8 waves owns a contiguous range of 16-row tiles
-// (an equal share of all jobs' tiles), taken in chunks of up to 9 tiles of
-// one job whose accumulators stay in registers.  Wave w streams steps w,
+// (an equal share of all jobs' tiles), taken in chunks of up to 9 tiles (6 with two
+// A row groups) of one job whose accumulators stay in registers.  Wave w streams steps w,
 // w + 8, w + 16, ... of every tile of the chunk, so the workgroup reads 512
 // contiguous bytes of each row at a time.  Each tile has its own register
 // slot, refilled with the next step's 16 bytes as soon as it has been
@@ -57,7 +63,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;                    // weight rows per MFMA tile
-constexpr int kChunk = 9;                    // tiles accumulated in registers at once
+// tiles accumulated in registers at once (fewer with two A row groups, whose
+// accumulators and x operands take twice the registers)
+constexpr int chunk_tiles(int ng) { return ng >= 2 ? 6 : 9; }
 constexpr uint32_t kBufFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
 constexpr uint32_t kOut = 0x7FFFFFF0u;       // a buffer offset past every range: reads 0
 
@@ -175,7 +183,8 @@ __device__ __forceinline__ bf16x8 x_frag(const uint4 &p, const uint4 &q, uint32_
 }
 
 struct MfmaParams {
-    const float *x;  // [t][n_in]
+    const float *x;      // [t][n_in] (split mode)
+    const uint16_t *xb;  // bf16(x) [t][n_in] (wide mode)
     int t;
     int n_in;
     int nb;     // blocks per row
@@ -195,10 +204,15 @@ struct Chunk {
     int lrow0;  // job-local row of the chunk's first row
 };
 
-template <int FMT, int TC>
+// NG = 0: "split" mode, t <= 8, A rows = bf16 hi / lo of x (f32 in memory).
+// NG >= 1: "wide" mode, t <= 16 NG, NG groups of 16 tokens per B operand,
+// A rows = bf16(x) read from the prefill pre-pass's bf16 copy of x.
+template <int FMT, int TC, int NG>
 __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     constexpr int BPS = Mfma<FMT>::BPS;
-    __shared__ f32x4 red[kWaves][TC][32];
+    constexpr bool kWide = NG > 0;
+    constexpr int NA = kWide ? NG : 1;  // A row groups per B operand
+    __shared__ f32x4 red[kWaves][TC][kWide ? 64 : 32];
 
     const int lane = (int)threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -208,14 +222,17 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     const int nb4 = (nb + 3) / 4;
     const int64_t row_bytes = mfma_row_bytes<FMT>(n_in);
 
-    // A operand row n: hi of token n (n < 8) or lo of token n - 8; rows of
-    // tokens >= t read zeros
-    const int tok = n & 7;
-    const uint32_t lo_mask = n >= 8 ? 0xFFFFFFFFu : 0u;
+    // Split mode: A operand row n is the hi part of token n (n < 8) or the
+    // lo part of token n - 8.  Wide mode: row n of group q is token 16 q + n.
+    // Rows of tokens >= t read zeros.
+    const int tok = kWide ? n : (n & 7);
+    const uint32_t lo_mask = (!kWide && n >= 8) ? 0xFFFFFFFFu : 0u;
     const bool xrow_ok = tok < t;
-    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(p.x, (uint32_t)(t * n_in * 4));
-    const uint32_t xoff0 = (uint32_t)((tok * n_in + slot_code<FMT>(g, 0)) * 4);
-    const uint32_t xoff1 = (uint32_t)((tok * n_in + slot_code<FMT>(g, 4)) * 4);
+    const __amdgpu_buffer_rsrc_t xrs =
+        kWide ? make_rsrc(p.xb, (uint32_t)(t * n_in * 2)) : make_rsrc(p.x, (uint32_t)(t * n_in * 4));
+    const int esz = kWide ? 2 : 4;
+    const uint32_t xoff0 = (uint32_t)((tok * n_in + slot_code<FMT>(g, 0)) * esz);
+    const uint32_t xoff1 = (uint32_t)((tok * n_in + slot_code<FMT>(g, 4)) * esz);
 
     // this workgroup's tiles and this wave's K steps
     const int T = p.tiles_total, G = (int)gridDim.x;
@@ -242,7 +259,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     // ---- register ring: one step of every tile of a chunk, plus x ----
     uint4 wc[TC];
     uint32_t ws[TC];
-    uint4 xr[BPS][2];
+    uint4 xr[BPS][2];   // split mode: 8 f32 of x per block
+    uint4 xw[NA][BPS];  // wide mode: 8 bf16 of x per block and group
 
     // issue side: chunk, step and the chunk's buffer descriptors
     Chunk ic = chunk_at(ta);
@@ -261,9 +279,27 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
 #pragma unroll
         for (int jb = 0; jb < BPS; ++jb) {
             const int b = BPS * is + jb;
-            const bool ok = xrow_ok && ic.cnt > 0 && b < nb;
-            xr[jb][0] = bload16(xrs, ok ? xoff0 + (uint32_t)b * 128u : kOut);
-            xr[jb][1] = bload16(xrs, ok ? xoff1 + (uint32_t)b * 128u : kOut);
+            if constexpr (kWide) {
+#pragma unroll
+                for (int q = 0; q < NA; ++q) {
+                    const bool ok = 16 * q + tok < t && ic.cnt > 0 && b < nb;
+                    const uint32_t o = (uint32_t)(q * 16 * n_in * 2) + (uint32_t)b * 64u;
+                    if constexpr (FMT == FMT_Q8) {
+                        // slots 0..3 and 4..7 are two runs of 4 elements
+                        const uint2 lo = __builtin_bit_cast(
+                            uint2, __builtin_amdgcn_raw_buffer_load_b64(xrs, ok ? xoff0 + o : kOut, 0, 0));
+                        const uint2 hi = __builtin_bit_cast(
+                            uint2, __builtin_amdgcn_raw_buffer_load_b64(xrs, ok ? xoff1 + o : kOut, 0, 0));
+                        xw[q][jb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    } else {
+                        xw[q][jb] = bload16(xrs, ok ? xoff0 + o : kOut);
+                    }
+                }
+            } else {
+                const bool ok = xrow_ok && ic.cnt > 0 && b < nb;
+                xr[jb][0] = bload16(xrs, ok ? xoff0 + (uint32_t)b * 128u : kOut);
+                xr[jb][1] = bload16(xrs, ok ? xoff1 + (uint32_t)b * 128u : kOut);
+            }
         }
     };
     auto issue_w = [&](int r) {
@@ -292,69 +328,88 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         }
     };
 
-    f32x4 acc[TC];
+    f32x4 acc[TC][NA];
 #pragma unroll
-    for (int r = 0; r < TC; ++r) acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < TC; ++r)
+#pragma unroll
+        for (int q = 0; q < NA; ++q) acc[r][q] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     // ---- end of a chunk: sum the 8 waves' partials per tile through LDS ----
     auto reduce = [&](const Chunk &c) {
-#pragma unroll
-        for (int r = 0; r < TC; ++r) {
-            if (r < c.cnt) {
-                // rows 8..15 (lo) of lanes 32..63 onto rows 0..7 of lanes 0..31
-                // (whole-vector bit casts only, see bload16)
-                const uint4 ai = __builtin_bit_cast(uint4, acc[r]);
-                const uint32_t av[4] = {ai.x, ai.y, ai.z, ai.w};
-                f32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const auto h = __builtin_amdgcn_permlane32_swap(av[e], av[e], false, false);
-                    const f32x2 hf = __builtin_bit_cast(f32x2, h);
-                    v[e] = hf[0] + hf[1];
-                }
-                if (lane < 32) red[wave][r][lane] = v;
-            }
-            acc[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        }
-        __syncthreads();
-        const float *redf = reinterpret_cast<const float *>(&red[0][0][0]);
         const KJob &jb = p.job[c.j];
-        for (int r = wave; r < c.cnt; r += kWaves) {
+        const float *redf = reinterpret_cast<const float *>(&red[0][0][0]);
+        constexpr int kLanes = kWide ? 64 : 32;  // lanes holding distinct outputs
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int i = 4 * h + (lane >> 4);  // token
-                const int row = c.lrow0 + kTile * r + n;
-                if (i < t && row < jb.n_out) {
-                    // token i, row n sits in lane 16 * (i / 4) + n, element i % 4
-                    const int slot = 16 * (i >> 2) + n, e = i & 3;
-                    float sum = 0.f;
+        for (int q = 0; q < NA; ++q) {
 #pragma unroll
-                    for (int w = 0; w < kWaves; ++w) sum += redf[((w * TC + r) * 32 + slot) * 4 + e];
-                    // Q4 codes entered the MFMAs multiplied by 16
-                    jb.y[(int64_t)i * jb.n_out + row] = FMT == FMT_Q4 ? sum * 0.0625f : sum;
+            for (int r = 0; r < TC; ++r) {
+                if (r < c.cnt) {
+                    if constexpr (kWide) {
+                        red[wave][r][lane] = acc[r][q];
+                    } else {
+                        // rows 8..15 (lo) of lanes 32..63 onto rows 0..7 of lanes 0..31
+                        // (whole-vector bit casts only, see bload16)
+                        const uint4 ai = __builtin_bit_cast(uint4, acc[r][q]);
+                        const uint32_t av[4] = {ai.x, ai.y, ai.z, ai.w};
+                        f32x4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const auto h = __builtin_amdgcn_permlane32_swap(av[e], av[e], false, false);
+                            const f32x2 hf = __builtin_bit_cast(f32x2, h);
+                            v[e] = hf[0] + hf[1];
+                        }
+                        if (lane < 32) red[wave][r][lane] = v;
+                    }
+                }
+                acc[r][q] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
+            __syncthreads();
+            for (int r = wave; r < c.cnt; r += kWaves) {
+#pragma unroll
+                for (int h = 0; h < (kWide ? 4 : 2); ++h) {
+                    const int i = 4 * h + (lane >> 4);  // token within the group
+                    const int row = c.lrow0 + kTile * r + n;
+                    const int token = 16 * q + i;
+                    if (token < t && row < jb.n_out) {
+                        // token i, row n sits in lane 16 * (i / 4) + n, element i % 4
+                        const int slot = 16 * (i >> 2) + n, e = i & 3;
+                        float sum = 0.f;
+#pragma unroll
+                        for (int w = 0; w < kWaves; ++w) sum += redf[((w * TC + r) * kLanes + slot) * 4 + e];
+                        // Q4 codes entered the MFMAs multiplied by 16
+                        jb.y[(int64_t)token * jb.n_out + row] = FMT == FMT_Q4 ? sum * 0.0625f : sum;
+                    }
                 }
             }
+            __syncthreads();  // red is rewritten next
         }
-        __syncthreads();  // red is rewritten by the next chunk
     };
 
     // ---- one step of one tile ----
-    auto consume = [&](int r, const bf16x8 (&a)[BPS]) {
+    auto consume = [&](int r, const bf16x8 (&a)[NA][BPS]) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         if constexpr (FMT == FMT_BF16) {
-            acc[r] = mfma(a[0], __builtin_bit_cast(bf16x8, wc[r]), acc[r]);
+#pragma unroll
+            for (int q = 0; q < NA; ++q) acc[r][q] = mfma(a[q][0], __builtin_bit_cast(bf16x8, wc[r]), acc[r][q]);
         } else if constexpr (FMT == FMT_Q8) {
             uint32_t d0 = wc[r].x, d1 = wc[r].y, d2 = wc[r].z, d3 = wc[r].w;
             xpose4(d0, d1, d2, d3);
             // lane groups 0,1 hold block 2s's scale, groups 2,3 block 2s+1's
             const auto sc = __builtin_amdgcn_permlane32_swap(ws[r], ws[r], false, false);
             const f32x2 scf = __builtin_bit_cast(f32x2, sc);  // whole-vector cast (see bload16)
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 p0 = mfma(a[0], q8_to_bf16(d0, d1), z);
-            const f32x4 p1 = mfma(a[1], q8_to_bf16(d2, d3), z);
-            // both MFMAs issue before the first read of a result
+            const bf16x8 b0 = q8_to_bf16(d0, d1), b1 = q8_to_bf16(d2, d3);
+            f32x4 p0[NA], p1[NA];
+#pragma unroll
+            for (int q = 0; q < NA; ++q) {
+                p0[q] = mfma(a[q][0], b0, z);
+                p1[q] = mfma(a[q][1], b1, z);
+            }
+            // all MFMAs issue before the first read of a result
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(scf[1], p1[e], fmaf(scf[0], p0[e], acc[r][e]));
+            for (int q = 0; q < NA; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[r][q][e] = fmaf(scf[1], p1[q][e], fmaf(scf[0], p0[q][e], acc[r][q][e]));
         } else {
             uint32_t d[4] = {wc[r].x, wc[r].y, wc[r].z, wc[r].w};
             xpose4(d[0], d[1], d[2], d[3]);
@@ -363,18 +418,23 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
             const auto y0 = __builtin_amdgcn_permlane16_swap(x32[0], x32[0], false, false);
             const auto y1 = __builtin_amdgcn_permlane16_swap(x32[1], x32[1], false, false);
             const uint32_t sb[4] = {y0[0], y0[1], y1[0], y1[1]};
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            f32x4 pj[4];
+            f32x4 pj[NA][4];
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) pj[jb] = mfma(a[jb], q4_to_bf16(d[jb]), z);
-            // all four MFMAs issue before the first read of a result, so the
+            for (int jb = 0; jb < 4; ++jb) {
+                const bf16x8 bq = q4_to_bf16(d[jb]);
+#pragma unroll
+                for (int q = 0; q < NA; ++q) pj[q][jb] = mfma(a[q][jb], bq, z);
+            }
+            // all MFMAs issue before the first read of a result, so the
             // scaling of block 0 overlaps the matrix core's work on 1..3
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
                 const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[jb]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(sf, pj[jb][e], acc[r][e]);
+                for (int q = 0; q < NA; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[r][q][e] = fmaf(sf, pj[q][jb][e], acc[r][q][e]);
             }
         }
     };
@@ -397,9 +457,16 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     advance(ic, is);
     set_rsrc();
     while (cc.cnt > 0) {
-        bf16x8 a[BPS];
+        bf16x8 a[NA][BPS];
 #pragma unroll
-        for (int jb = 0; jb < BPS; ++jb) a[jb] = x_frag(xr[jb][0], xr[jb][1], lo_mask);
+        for (int jb = 0; jb < BPS; ++jb) {
+            if constexpr (kWide) {
+#pragma unroll
+                for (int q = 0; q < NA; ++q) a[q][jb] = __builtin_bit_cast(bf16x8, xw[q][jb]);
+            } else {
+                a[0][jb] = x_frag(xr[jb][0], xr[jb][1], lo_mask);
+            }
+        }
         issue_x();
 #pragma unroll
         for (int r = 0; r < TC; ++r) {
@@ -417,12 +484,13 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
 
 }  // namespace
 
-bool gemv_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
-    if (t < 1 || t > kGemvMaxT || n_in <= 0 || n_in % kBlock) return false;
+namespace {
+
+// every buffer offset a lane forms stays below 2^31
+bool mfma_fits(int fmt, int64_t x_bytes, int n_in, const KJob *jobs, int n_jobs) {
+    if (n_in <= 0 || n_in % kBlock || x_bytes >= (1ll << 31) || n_jobs < 1 || n_jobs > kMaxJobs) return false;
     const int64_t rb = fmt == FMT_BF16 ? 2ll * n_in : fmt == FMT_Q8 ? (int64_t)n_in : n_in / 2;
     const int64_t sb = fmt == FMT_Q8 ? 4 : 2;
-    if (4ll * t * n_in >= (1ll << 31)) return false;
-    // every buffer offset a lane forms stays below 2^31
     for (int j = 0; j < n_jobs; ++j)
         if ((int64_t)jobs[j].n_out * rb >= (1ll << 31) ||
             tiled_scale_count(jobs[j].n_out, n_in / kBlock) * sb >= (1ll << 31))
@@ -430,11 +498,7 @@ bool gemv_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
     return true;
 }
 
-hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
-                            int cu_count, hipStream_t s) {
-    if (!gemv_mfma_fits(fmt, t, n_in, jobs, n_jobs) || n_jobs < 1 || n_jobs > kMaxJobs) return hipErrorInvalidValue;
-    MfmaParams p{};
-    p.x = x;
+bool fill_params(MfmaParams &p, int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
     p.t = t;
     p.n_in = n_in;
     p.nb = n_in / kBlock;
@@ -449,15 +513,53 @@ hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob
     }
     for (int j = n_jobs; j <= kMaxJobs; ++j) p.tile0[j] = tiles;
     p.tiles_total = tiles;
-    if (tiles == 0) return hipSuccess;
+    return tiles > 0;
+}
+
+template <int FMT, int NG>
+hipError_t launch_mode(const MfmaParams &p, int cu_count, hipStream_t s) {
     // one workgroup per compute unit at most, each an equal share of the tiles
-    const int grid = tiles < cu_count ? tiles : cu_count;
-    switch (fmt) {
-        case FMT_BF16: hipLaunchKernelGGL((gemv_mfma_kernel<FMT_BF16, kChunk>), dim3(grid), dim3(kThreads), 0, s, p); break;
-        case FMT_Q8: hipLaunchKernelGGL((gemv_mfma_kernel<FMT_Q8, kChunk>), dim3(grid), dim3(kThreads), 0, s, p); break;
-        default: hipLaunchKernelGGL((gemv_mfma_kernel<FMT_Q4, kChunk>), dim3(grid), dim3(kThreads), 0, s, p); break;
-    }
+    const int grid = p.tiles_total < cu_count ? p.tiles_total : cu_count;
+    hipLaunchKernelGGL((gemv_mfma_kernel<FMT, chunk_tiles(NG), NG>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
+}
+
+template <int NG>
+hipError_t launch_fmt_mode(int fmt, const MfmaParams &p, int cu_count, hipStream_t s) {
+    switch (fmt) {
+        case FMT_BF16: return launch_mode<FMT_BF16, NG>(p, cu_count, s);
+        case FMT_Q8: return launch_mode<FMT_Q8, NG>(p, cu_count, s);
+        case FMT_Q4: return launch_mode<FMT_Q4, NG>(p, cu_count, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool gemv_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
+    return t >= 1 && t <= kGemvMaxT && mfma_fits(fmt, 4ll * t * n_in, n_in, jobs, n_jobs);
+}
+
+hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
+                            int cu_count, hipStream_t s) {
+    if (!gemv_mfma_fits(fmt, t, n_in, jobs, n_jobs)) return hipErrorInvalidValue;
+    MfmaParams p{};
+    p.x = x;
+    if (!fill_params(p, fmt, t, n_in, jobs, n_jobs)) return hipSuccess;
+    return launch_fmt_mode<0>(fmt, p, cu_count, s);
+}
+
+bool verify_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
+    return t > kGemvMaxT && t <= kVerifyMaxT && mfma_fits(fmt, 2ll * t * n_in, n_in, jobs, n_jobs);
+}
+
+hipError_t launch_verify_mfma(int fmt, const uint16_t *xb, int t, int n_in, const KJob *jobs, int n_jobs,
+                              int cu_count, hipStream_t s) {
+    if (!verify_mfma_fits(fmt, t, n_in, jobs, n_jobs)) return hipErrorInvalidValue;
+    MfmaParams p{};
+    p.xb = xb;
+    if (!fill_params(p, fmt, t, n_in, jobs, n_jobs)) return hipSuccess;
+    return t <= 16 ? launch_fmt_mode<1>(fmt, p, cu_count, s) : launch_fmt_mode<2>(fmt, p, cu_count, s);
 }
 
 }  // namespace il

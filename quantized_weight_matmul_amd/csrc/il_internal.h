@@ -28,6 +28,7 @@ enum : int { FMT_BF16 = 0, FMT_Q8 = 1, FMT_Q4 = 2 };
 constexpr int kBlock = 32;     // quantisation block (elements)
 constexpr int kMaxJobs = 8;    // jobs per kernel launch (kernarg table)
 constexpr int kGemvMaxT = 8;   // t <= kGemvMaxT runs the decode kernels
+constexpr int kVerifyMaxT = 32;  // largest t the matrix-core decode kernel takes in wide mode
 
 struct Weight {
     int fmt;
@@ -75,6 +76,13 @@ hipError_t launch_gemv(int fmt, const float *x, int t, int n_in, const KJob *job
 bool gemv_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs);
 hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
                             int cu_count, hipStream_t s);
+
+// ---- mid-size t (kGemvMaxT < t <= kVerifyMaxT) on the same kernel, "wide"
+// mode: up to 32 tokens per weight operand, x already rounded to bf16 (xb,
+// row-major [t][n_in], from the prefill pre-pass) ----
+bool verify_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs);
+hipError_t launch_verify_mfma(int fmt, const uint16_t *xb, int t, int n_in, const KJob *jobs, int n_jobs,
+                              int cu_count, hipStream_t s);
 
 // ---- prefill GEMM, t > kGemvMaxT (il_gemm.hip) ----
 hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,

@@ -9,7 +9,9 @@ and the validation paths that must leave y untouched.
 
 Decode (t <= 8) has two kernel families, the f32 streaming kernel ("valu")
 and the matrix-core kernel ("mfma"); the library picks one per format and t,
-and IL_DECODE pins it, so decode cases run under both.
+and IL_DECODE pins it, so decode cases run under both.  Mid-size t (9..32)
+runs either the matrix-core kernel's wide mode ("verify") or the tiled GEMM
+("gemm"), pinned by IL_PREFILL, and is tested under both.
 """
 import numpy as np
 import pytest
@@ -39,25 +41,33 @@ def _hi_lo(a):
     return (hi + _bf16_rne((a - hi).astype(np.float32))).astype(np.float32)
 
 
+def _paths(t):
+    if t <= 8:
+        return ("valu", "mfma")
+    return ("verify", "gemm") if t <= 32 else ("gemm",)
+
+
 def _decode_cases(ts):
-    """(t, path) pairs: both decode families for t <= 8, the GEMM beyond."""
-    return [(t, p) for t in ts for p in (("valu", "mfma") if t <= 8 else ("gemm",))]
+    """(t, path) pairs: both kernel families wherever t has two."""
+    return [(t, p) for t in ts for p in _paths(t)]
 
 
 def _pin(monkeypatch, path):
     if path in ("valu", "mfma"):
         monkeypatch.setenv("IL_DECODE", path)
+    if path in ("verify", "gemm"):
+        monkeypatch.setenv("IL_PREFILL", path)
 
 
 def _selected(x, path):
     """What a one-hot weight row returns for x on each path."""
     if path == "valu":
         return x
-    return _hi_lo(x) if path == "mfma" else _bf16_rne(x)
+    return _hi_lo(x) if path == "mfma" else _bf16_rne(x)  # verify and gemm: bf16(x)
 
 
 # ------------------------------------------------------------- workloads
-@pytest.mark.parametrize("name", ["c1", "c2", "c3a", "c3b", "c4_t1", "c4_t2", "c4_t4", "c4_t8"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3a", "c3b", "c4_t1", "c4_t2", "c4_t4", "c4_t8", "c4_t16", "c4_t32"])
 def test_workload_full(name):
     sub = wl.SUBMISSIONS[name]
     say(f"[parity] {name}: t={sub.t} n_in={sub.n_in} jobs={[(FMT_NAME[j.fmt], j.n_out) for j in sub.jobs]}")
@@ -94,7 +104,7 @@ def _rand_weight(fmt, g, n_out, n_in):
 
 
 @pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
-@pytest.mark.parametrize("t,path", _decode_cases([1, 2, 3, 5, 8, 9, 16, 33, 130, 257]))
+@pytest.mark.parametrize("t,path", _decode_cases([1, 2, 3, 5, 8, 9, 16, 17, 32, 33, 130, 257]))
 def test_odd_shapes(fmt, t, path, monkeypatch):
     """Several tiles plus ragged tails in every dimension, three jobs per call."""
     _pin(monkeypatch, path)
@@ -160,6 +170,25 @@ def test_mfma_decode_many_tiles(fmt, t, monkeypatch):
 
 
 @pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
+@pytest.mark.parametrize("t", [9, 16, 17, 32])
+def test_verify_wide_many_tiles(fmt, t, monkeypatch):
+    """Mid-size t on the matrix-core kernel's wide mode: one or two groups of
+    16 tokens per weight operand, several chunks per workgroup, a job
+    boundary inside a workgroup's range and ragged tiles and K."""
+    _pin(monkeypatch, "verify")
+    g = np.random.default_rng(1800 + 10 * t + fmt)
+    n_in = 1056
+    n_outs = [20000, 777, 31]
+    say(f"[verify tiles] fmt={FMT_NAME[fmt]} t={t} n_in={n_in} n_outs={n_outs}")
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    ws = [_rand_weight(fmt, g, n, n_in) for n in n_outs]
+    hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
+    ys = run(x, hs, n_outs)
+    for w, n, y in zip(ws, n_outs, ys):
+        check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_out {n}")
+
+
+@pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
 def test_gemm_full_rounds_and_tail(fmt):
     """Prefill with more 256 x 256 tiles than compute units: whole rounds of
     big tiles plus a tail run as 128 x 128 quarters, with ragged edges in t,
@@ -193,7 +222,7 @@ def _onehot(fmt, n_out, n_in, cols):
 
 
 @pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
-@pytest.mark.parametrize("t,path", _decode_cases([1, 3, 8, 9, 200]))
+@pytest.mark.parametrize("t,path", _decode_cases([1, 3, 8, 9, 20, 200]))
 def test_onehot_selects_columns(fmt, t, path, monkeypatch):
     """One-hot W: y[:, r] = x[:, c_r] exactly on the f32 decode path, the
     bf16 hi + lo split of it on the matrix-core decode path, and bf16(x)
