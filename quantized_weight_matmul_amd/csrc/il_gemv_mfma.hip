@@ -14,9 +14,11 @@
 // Operands of one MFMA (16 x 16 output, K = 32 = one quantisation block):
 //   * B = 16 weight rows x one block, as exact bf16 values: bf16 weights as
 //     stored; Q8 codes converted through f32 (|q| <= 127 is exact in bf16);
-//     Q4 nibbles (stored as the 4-bit two's complement of code - 8) moved to
-//     the top of a byte are the signed value 16 * (code - 8), converted the
-//     same way (the factor 16 is removed from the result, exactly).  No
+//     Q4 codes come from a table in LDS: each byte of the code plane (two
+//     nibbles, stored as the 4-bit two's complement of code - 8) indexes
+//     256 precomputed pairs of exact bf16 values; the table holds one copy
+//     per lane, so the 64 lookups of a wave hit 64 distinct banks and the
+//     byte-to-address step is a single v_perm.  No
 //     offset is folded out of a sum, so every product of A and B is exact
 //     and the rounding of a result is relative to the sum of |x * w|.
 //   * A = x as 16 rows: row i < 8 holds bf16(x_i) ("hi"), row 8 + i holds
@@ -51,6 +53,8 @@
 // the eight partial 16 x 16 results per tile are summed through LDS in a
 // fixed order, so results are bitwise reproducible (no atomics).
 #include "il_internal.h"
+
+#include <type_traits>
 
 namespace il {
 namespace {
@@ -138,16 +142,25 @@ __device__ __forceinline__ void xpose4(uint32_t &d0, uint32_t &d1, uint32_t &d2,
     d3 = e[1];
 }
 
-// 8 Q4 codes of one dword (stored as code ^ 8, element 2i in the low nibble
-// of byte i) -> 8 exact bf16 values 16 * (code - 8), in order.
-__device__ __forceinline__ bf16x8 q4_to_bf16(uint32_t d) {
-    const uint32_t lo = (d << 4) & 0xF0F0F0F0u;  // elements 0, 2, 4, 6 as signed bytes
-    const uint32_t hi = d & 0xF0F0F0F0u;         // elements 1, 3, 5, 7
+// Q4 code table in LDS: entry (byte b, lane l) at byte offset 256 b + 4 l
+// holds the two codes of b (stored as code ^ 8, element 2i in the low nibble
+// of byte i) as exact bf16 values code - 8, low nibble first.
+constexpr int kQ4LutWords = 256 * 64;
+
+__device__ __forceinline__ uint32_t q4_pair_bf16(int b) {
+    const int lo = ((b & 15) ^ 8) - 8, hi = ((b >> 4) ^ 8) - 8;
+    return pack_bf16((float)lo, (float)hi);
+}
+
+// 8 Q4 codes of one dword -> 8 exact bf16 values, in order: v_perm puts
+// byte i of d next to this lane's column offset, which is the table address.
+__device__ __forceinline__ bf16x8 q4_to_bf16(const uint32_t *lut, uint32_t d, uint32_t lane4) {
+    const char *lb = reinterpret_cast<const char *>(lut);
     uint4 o;
-    o.x = pack_bf16((float)(int8_t)lo, (float)(int8_t)hi);
-    o.y = pack_bf16((float)(int8_t)(lo >> 8), (float)(int8_t)(hi >> 8));
-    o.z = pack_bf16((float)(int8_t)(lo >> 16), (float)(int8_t)(hi >> 16));
-    o.w = pack_bf16((float)(int8_t)(lo >> 24), (float)(int8_t)(hi >> 24));
+    o.x = *reinterpret_cast<const uint32_t *>(lb + __builtin_amdgcn_perm(d, lane4, 0x0C0C0400u));
+    o.y = *reinterpret_cast<const uint32_t *>(lb + __builtin_amdgcn_perm(d, lane4, 0x0C0C0500u));
+    o.z = *reinterpret_cast<const uint32_t *>(lb + __builtin_amdgcn_perm(d, lane4, 0x0C0C0600u));
+    o.w = *reinterpret_cast<const uint32_t *>(lb + __builtin_amdgcn_perm(d, lane4, 0x0C0C0700u));
     return __builtin_bit_cast(bf16x8, o);
 }
 
@@ -213,11 +226,19 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     constexpr bool kWide = NG > 0;
     constexpr int NA = kWide ? NG : 1;  // A row groups per B operand
     __shared__ f32x4 red[kWaves][TC][kWide ? 64 : 32];
+    __shared__ uint32_t lut[FMT == FMT_Q4 ? kQ4LutWords : 1];
 
     const int lane = (int)threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int n = lane & 15;  // weight row within the tile (B column) = A row
     const int g = lane >> 4;  // lane group: quarter of the K slice
+
+    if constexpr (FMT == FMT_Q4) {
+        // the code table: wave w fills byte values w, w + 8, ..., one column per lane
+#pragma unroll 4
+        for (int i = 0; i < 32; ++i) lut[(8 * i + wave) * 64 + lane] = q4_pair_bf16(8 * i + wave);
+        __syncthreads();
+    }
     const int t = p.t, nb = p.nb, n_in = p.n_in;
     const int nb4 = (nb + 3) / 4;
     const int64_t row_bytes = mfma_row_bytes<FMT>(n_in);
@@ -258,7 +279,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
 
     // ---- register ring: one step of every tile of a chunk, plus x ----
     uint4 wc[TC];
-    uint32_t ws[TC];
+    // Q4: the f16 scales of blocks 4s..4s+3 of the lane's row (one 8-byte
+    // load); Q8: the f32 scale of the lane's block
+    typename std::conditional<FMT == FMT_Q4, uint2, uint32_t>::type ws[TC];
     uint4 xr[BPS][2];   // split mode: 8 f32 of x per block
     uint4 xw[NA][BPS];  // wide mode: 8 bf16 of x per block and group
 
@@ -310,9 +333,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         wc[r] = bload16(crs, ok ? (uint32_t)(row * row_bytes + kb * 16) : kOut);
         // scales from the tiled plane: a tile's 16 rows x 4 blocks are one run
         if constexpr (FMT == FMT_Q4) {
-            // this lane's 16 bytes are block kb
-            ws[r] = __builtin_amdgcn_raw_buffer_load_b16(
-                srs, ok ? (uint32_t)(tiled_scale_index(row, kb, nb4) * 2) : kOut, 0, 0);
+            // the run of 4 scales of this lane's row (n) for blocks 4s..4s+3
+            ws[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                srs, row_ok && 4 * is < nb ? (uint32_t)(tiled_scale_index(row, 4 * is, nb4) * 2) : kOut, 0, 0));
         } else if constexpr (FMT == FMT_Q8) {
             // this lane's 16 bytes are half of block 2s + g/2
             const int blk = 2 * is + (g >> 1);
@@ -376,8 +399,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
                         float sum = 0.f;
 #pragma unroll
                         for (int w = 0; w < kWaves; ++w) sum += redf[((w * TC + r) * kLanes + slot) * 4 + e];
-                        // Q4 codes entered the MFMAs multiplied by 16
-                        jb.y[(int64_t)token * jb.n_out + row] = FMT == FMT_Q4 ? sum * 0.0625f : sum;
+                        jb.y[(int64_t)token * jb.n_out + row] = sum;
                     }
                 }
             }
@@ -413,15 +435,11 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         } else {
             uint32_t d[4] = {wc[r].x, wc[r].y, wc[r].z, wc[r].w};
             xpose4(d[0], d[1], d[2], d[3]);
-            // every lane gets the scales of blocks 4s..4s+3 of its row
-            const auto x32 = __builtin_amdgcn_permlane32_swap(ws[r], ws[r], false, false);
-            const auto y0 = __builtin_amdgcn_permlane16_swap(x32[0], x32[0], false, false);
-            const auto y1 = __builtin_amdgcn_permlane16_swap(x32[1], x32[1], false, false);
-            const uint32_t sb[4] = {y0[0], y0[1], y1[0], y1[1]};
+            const uint32_t sb[4] = {ws[r].x, ws[r].x >> 16, ws[r].y, ws[r].y >> 16};
             f32x4 pj[NA][4];
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
-                const bf16x8 bq = q4_to_bf16(d[jb]);
+                const bf16x8 bq = q4_to_bf16(lut, d[jb], (uint32_t)lane << 2);
 #pragma unroll
                 for (int q = 0; q < NA; ++q) pj[q][jb] = mfma(a[q][jb], bq, z);
             }
