@@ -73,14 +73,16 @@ def measured_traffic(workload: str):
     """HBM bytes per launch of the workload's kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE runs (profiles/traffic.json), scaled by
     the same counters on a plain copy of known size; None when absent or when
-    the kernel source changed after the counters were taken."""
+    a source of the call's kernels changed after the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_source_sha") != kernel_source_sha(rec.get("kernel_source", "")):
+    if not rec or not rec.get("kernel_sources"):
+        return None
+    if any(kernel_source_sha(name) != sha for name, sha in rec["kernel_sources"].items()):
         return None
     return int(rec["hbm_bytes_per_launch"])
 

@@ -329,6 +329,17 @@ hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *job
     for (int j = n_jobs; j <= kMaxJobs; ++j) p.tn0[j] = tn;
     const int tiles = p.tiles_m * tn;
 
+    // mid-size t: the matrix-core decode kernel's wide mode, which rounds x
+    // itself up to kWideF32MaxT tokens and reads the bf16 copy made below
+    // beyond (IL_PREFILL=gemm|verify pins the kernel)
+    bool verify = t <= kVerifyMaxT;
+    if (const char *force = getenv("IL_PREFILL")) {
+        if (!strcmp(force, "gemm")) verify = false;
+        if (!strcmp(force, "verify")) verify = true;
+    }
+    verify = verify && verify_mfma_fits(fmt, t, n_in, jobs, n_jobs);
+    if (verify && t <= kWideF32MaxT) return launch_verify_mfma(fmt, x, nullptr, t, n_in, jobs, n_jobs, cu_count, s);
+
     // x -> bf16 into stream-ordered scratch, freed after the GEMM on the same stream
     const int64_t n8 = (int64_t)t * n_in / 8;
     void *xb = nullptr;
@@ -339,14 +350,7 @@ hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *job
     e = hipGetLastError();
     if (e == hipSuccess) {
         p.xb = static_cast<const uint16_t *>(xb);
-        // IL_PREFILL=gemm|verify pins the kernel for mid-size t
-        bool verify = t <= kVerifyMaxT;
-        if (const char *force = getenv("IL_PREFILL")) {
-            if (!strcmp(force, "gemm")) verify = false;
-            if (!strcmp(force, "verify")) verify = true;
-        }
-        if (verify && verify_mfma_fits(fmt, t, n_in, jobs, n_jobs))
-            e = launch_verify_mfma(fmt, p.xb, t, n_in, jobs, n_jobs, cu_count, s);
+        if (verify) e = launch_verify_mfma(fmt, x, p.xb, t, n_in, jobs, n_jobs, cu_count, s);
         else switch (fmt) {
             case FMT_BF16: e = launch_plan<FMT_BF16>(p, tiles, cu_count, s); break;
             case FMT_Q8: e = launch_plan<FMT_Q8>(p, tiles, cu_count, s); break;

@@ -28,11 +28,13 @@
 //     that stay in L2), one step ahead, in the per-lane order of the MFMA.
 //   * The per-block scale multiplies the 16 x 16 f32 result (one FMA per
 //     accumulator element), so no rounding of a dequantised weight occurs.
-//   * Wide mode (8 < t <= 32): A rows are 16 tokens of bf16(x) per group,
-//     read from the bf16 copy of x the prefill path makes anyway (x rounded
-//     to bf16 as on the GEMM path), and one converted B operand feeds one
-//     or two groups of MFMAs, so the weight conversion is shared by up to
-//     32 tokens.
+//   * Wide mode (8 < t <= 32): A rows are 16 tokens of bf16(x) per group
+//     (round-to-nearest-even, as on the GEMM path), and one converted B
+//     operand feeds one or two groups of MFMAs, so the weight conversion is
+//     shared by up to 32 tokens.  With one group x is rounded from f32 in
+//     registers; two groups read the bf16 copy of x that the GEMM's pre-pass
+//     makes, since f32 x for 32 tokens would not fit in registers beside six
+//     tiles.
 //
 // Loads: a wave fetches 16 bytes per lane, 64 bytes of each of 16 rows (one
 // bf16 block, two Q8 blocks or four Q4 blocks per row: one "step").  Lane
@@ -195,9 +197,18 @@ __device__ __forceinline__ bf16x8 x_frag(const uint4 &p, const uint4 &q, uint32_
     return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
+// A operand of one block in wide mode: the lane's 8 x values rounded to
+// bf16 (round-to-nearest-even, as on the GEMM path).
+__device__ __forceinline__ bf16x8 x_bf16(const uint4 &p, const uint4 &q) {
+    const f32x4 a = __builtin_bit_cast(f32x4, p);
+    const f32x4 b = __builtin_bit_cast(f32x4, q);
+    return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]),
+                                                 pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3])));
+}
+
 struct MfmaParams {
-    const float *x;      // [t][n_in] (split mode)
-    const uint16_t *xb;  // bf16(x) [t][n_in] (wide mode)
+    const float *x;      // [t][n_in] (split mode, wide mode with one group)
+    const uint16_t *xb;  // bf16(x) [t][n_in] (wide mode with two groups)
     int t;
     int n_in;
     int nb;     // blocks per row
@@ -219,7 +230,8 @@ struct Chunk {
 
 // NG = 0: "split" mode, t <= 8, A rows = bf16 hi / lo of x (f32 in memory).
 // NG >= 1: "wide" mode, t <= 16 NG, NG groups of 16 tokens per B operand,
-// A rows = bf16(x) read from the prefill pre-pass's bf16 copy of x.
+// A rows = bf16(x): rounded from the f32 x as it is loaded (NG = 1) or read
+// from the pre-pass's bf16 copy (NG = 2).
 template <int FMT, int TC, int NG>
 __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     constexpr int BPS = Mfma<FMT>::BPS;
@@ -249,9 +261,11 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     const int tok = kWide ? n : (n & 7);
     const uint32_t lo_mask = (!kWide && n >= 8) ? 0xFFFFFFFFu : 0u;
     const bool xrow_ok = tok < t;
+    constexpr bool kXb16 = NG >= 2;  // x given as bf16
+    constexpr int esz = kXb16 ? 2 : 4;
     const __amdgpu_buffer_rsrc_t xrs =
-        kWide ? make_rsrc(p.xb, (uint32_t)(t * n_in * 2)) : make_rsrc(p.x, (uint32_t)(t * n_in * 4));
-    const int esz = kWide ? 2 : 4;
+        kXb16 ? make_rsrc(p.xb, (uint32_t)(t * n_in * 2)) : make_rsrc(p.x, (uint32_t)(t * n_in * 4));
+    // the lane's 8 x values of a block are two runs of 4 elements
     const uint32_t xoff0 = (uint32_t)((tok * n_in + slot_code<FMT>(g, 0)) * esz);
     const uint32_t xoff1 = (uint32_t)((tok * n_in + slot_code<FMT>(g, 4)) * esz);
 
@@ -282,8 +296,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     // Q4: the f16 scales of blocks 4s..4s+3 of the lane's row (one 8-byte
     // load); Q8: the f32 scale of the lane's block
     typename std::conditional<FMT == FMT_Q4, uint2, uint32_t>::type ws[TC];
-    uint4 xr[BPS][2];   // split mode: 8 f32 of x per block
-    uint4 xw[NA][BPS];  // wide mode: 8 bf16 of x per block and group
+    uint4 xr[kXb16 ? 1 : NA][BPS][2];  // 8 f32 of x per block (and token group)
+    uint4 xw[kXb16 ? NA : 1][BPS];     // two groups: 8 bf16 of x per block and group
 
     // issue side: chunk, step and the chunk's buffer descriptors
     Chunk ic = chunk_at(ta);
@@ -302,26 +316,22 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
 #pragma unroll
         for (int jb = 0; jb < BPS; ++jb) {
             const int b = BPS * is + jb;
-            if constexpr (kWide) {
 #pragma unroll
-                for (int q = 0; q < NA; ++q) {
-                    const bool ok = 16 * q + tok < t && ic.cnt > 0 && b < nb;
-                    const uint32_t o = (uint32_t)(q * 16 * n_in * 2) + (uint32_t)b * 64u;
-                    if constexpr (FMT == FMT_Q8) {
-                        // slots 0..3 and 4..7 are two runs of 4 elements
-                        const uint2 lo = __builtin_bit_cast(
-                            uint2, __builtin_amdgcn_raw_buffer_load_b64(xrs, ok ? xoff0 + o : kOut, 0, 0));
-                        const uint2 hi = __builtin_bit_cast(
-                            uint2, __builtin_amdgcn_raw_buffer_load_b64(xrs, ok ? xoff1 + o : kOut, 0, 0));
-                        xw[q][jb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    } else {
-                        xw[q][jb] = bload16(xrs, ok ? xoff0 + o : kOut);
-                    }
+            for (int q = 0; q < NA; ++q) {
+                const bool ok = 16 * q + tok < t && ic.cnt > 0 && b < nb;
+                const uint32_t o = (uint32_t)(q * 16 * n_in * esz) + (uint32_t)(b * 32 * esz);
+                if constexpr (kXb16 && FMT != FMT_Q8) {
+                    xw[q][jb] = bload16(xrs, ok ? xoff0 + o : kOut);  // slots 0..7 are one run
+                } else if constexpr (kXb16) {
+                    const uint2 lo = __builtin_bit_cast(
+                        uint2, __builtin_amdgcn_raw_buffer_load_b64(xrs, ok ? xoff0 + o : kOut, 0, 0));
+                    const uint2 hi = __builtin_bit_cast(
+                        uint2, __builtin_amdgcn_raw_buffer_load_b64(xrs, ok ? xoff1 + o : kOut, 0, 0));
+                    xw[q][jb] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                } else {
+                    xr[q][jb][0] = bload16(xrs, ok ? xoff0 + o : kOut);
+                    xr[q][jb][1] = bload16(xrs, ok ? xoff1 + o : kOut);
                 }
-            } else {
-                const bool ok = xrow_ok && ic.cnt > 0 && b < nb;
-                xr[jb][0] = bload16(xrs, ok ? xoff0 + (uint32_t)b * 128u : kOut);
-                xr[jb][1] = bload16(xrs, ok ? xoff1 + (uint32_t)b * 128u : kOut);
             }
         }
     };
@@ -478,11 +488,13 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         bf16x8 a[NA][BPS];
 #pragma unroll
         for (int jb = 0; jb < BPS; ++jb) {
-            if constexpr (kWide) {
+            if constexpr (kXb16) {
 #pragma unroll
                 for (int q = 0; q < NA; ++q) a[q][jb] = __builtin_bit_cast(bf16x8, xw[q][jb]);
+            } else if constexpr (kWide) {
+                a[0][jb] = x_bf16(xr[0][jb][0], xr[0][jb][1]);
             } else {
-                a[0][jb] = x_frag(xr[jb][0], xr[jb][1], lo_mask);
+                a[0][jb] = x_frag(xr[0][jb][0], xr[0][jb][1], lo_mask);
             }
         }
         issue_x();
@@ -568,16 +580,18 @@ hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob
 }
 
 bool verify_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
-    return t > kGemvMaxT && t <= kVerifyMaxT && mfma_fits(fmt, 2ll * t * n_in, n_in, jobs, n_jobs);
+    return t > kGemvMaxT && t <= kVerifyMaxT && mfma_fits(fmt, 4ll * t * n_in, n_in, jobs, n_jobs);
 }
 
-hipError_t launch_verify_mfma(int fmt, const uint16_t *xb, int t, int n_in, const KJob *jobs, int n_jobs,
-                              int cu_count, hipStream_t s) {
+hipError_t launch_verify_mfma(int fmt, const float *x, const uint16_t *xb, int t, int n_in, const KJob *jobs,
+                              int n_jobs, int cu_count, hipStream_t s) {
     if (!verify_mfma_fits(fmt, t, n_in, jobs, n_jobs)) return hipErrorInvalidValue;
+    if (t > kWideF32MaxT && xb == nullptr) return hipErrorInvalidValue;
     MfmaParams p{};
+    p.x = x;
     p.xb = xb;
     if (!fill_params(p, fmt, t, n_in, jobs, n_jobs)) return hipSuccess;
-    return t <= 16 ? launch_fmt_mode<1>(fmt, p, cu_count, s) : launch_fmt_mode<2>(fmt, p, cu_count, s);
+    return t <= kWideF32MaxT ? launch_fmt_mode<1>(fmt, p, cu_count, s) : launch_fmt_mode<2>(fmt, p, cu_count, s);
 }
 
 }  // namespace il

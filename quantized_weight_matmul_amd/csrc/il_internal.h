@@ -78,11 +78,13 @@ hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob
                             int cu_count, hipStream_t s);
 
 // ---- mid-size t (kGemvMaxT < t <= kVerifyMaxT) on the same kernel, "wide"
-// mode: up to 32 tokens per weight operand, x already rounded to bf16 (xb,
-// row-major [t][n_in], from the prefill pre-pass) ----
+// mode: up to 32 tokens per weight operand.  For t <= kWideF32MaxT the kernel
+// rounds x (f32, row-major [t][n_in]) to bf16 as it loads it and xb may be
+// null; above, xb must be bf16(x) (row-major, from the GEMM's pre-pass) ----
+constexpr int kWideF32MaxT = 16;
 bool verify_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs);
-hipError_t launch_verify_mfma(int fmt, const uint16_t *xb, int t, int n_in, const KJob *jobs, int n_jobs,
-                              int cu_count, hipStream_t s);
+hipError_t launch_verify_mfma(int fmt, const float *x, const uint16_t *xb, int t, int n_in, const KJob *jobs,
+                              int n_jobs, int cu_count, hipStream_t s);
 
 // ---- prefill GEMM, t > kGemvMaxT (il_gemm.hip) ----
 hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
