@@ -14,12 +14,19 @@ sum_k |x*w| in f64; the acceptance test is |y - y_ref| <= 4e-3 * bound per
 output element.  The arithmetic lives in ``il_oracle.c`` (plain C, gcc -O2);
 this module only marshals numpy arrays.
 
+Also here, for the upload-quantiser row: ``quantize`` (f32 weights -> Q8 / Q4
+host blocks by per-block absmax scaling, rule stated in ``il_oracle.c``) and
+``f16_bits`` (f32 -> binary16, round to nearest even, from the format
+definition).
+
 Pins live in ``tests/oracle_pins.py`` (run by ``tests/test_oracle_pins.py``):
 exhaustive bf16 / f16 decode against library casts; exact-rational brute
 force on tiny shapes; closed forms (one-hot / identity W selects x columns,
 x = 1 gives row sums, all-zero codes give 0); Q8/Q4 round trips on
 representable values; hand-derived fixtures under ``tests/golden/``; numpy
-float64 matmul at full shapes.  ``tests/test_oracle_mutants.py`` plants
+float64 matmul at full shapes; for the quantiser, numpy's float16 cast,
+hand-derived blocks, exact round trips and the nearest-grid-point property.
+``tests/test_oracle_mutants.py`` plants
 mistakes in copies of ``il_oracle.c`` and checks that the pins catch each.
 """
 from __future__ import annotations
@@ -100,6 +107,12 @@ class Oracle:
         lib.orc_matmul_points.restype = ctypes.c_int
         lib.orc_matmul_points.argtypes = [_ptr, _i64, _i64, _ptr, ctypes.c_int, _i64, _i64,
                                           _ptr, _ptr, _ptr, _ptr, ctypes.c_int]
+        lib.orc_f16_bits.restype = ctypes.c_uint16
+        lib.orc_f16_bits.argtypes = [ctypes.c_float]
+        lib.orc_f16_bits_array.restype = None
+        lib.orc_f16_bits_array.argtypes = [_ptr, _i64, _ptr]
+        lib.orc_quantize.restype = ctypes.c_int
+        lib.orc_quantize.argtypes = [_ptr, ctypes.c_int, _i64, _i64, _ptr]
         lib.orc_check.restype = _i64
         lib.orc_check.argtypes = [_ptr, _ptr, _ptr, _i64, ctypes.c_double,
                                   ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]
@@ -174,6 +187,29 @@ class Oracle:
             raise ValueError("oracle matmul_points failed")
         return y, bound
 
+    def f16_bits(self, values) -> np.ndarray:
+        """f32 values -> binary16 bit patterns (round to nearest even),
+        converted from the format definition."""
+        v = np.ascontiguousarray(values, dtype=np.float32)
+        out = np.empty(v.shape, dtype=np.uint16)
+        self.lib.orc_f16_bits_array(_p(v), v.size, _p(out))
+        return out
+
+    def quantize(self, w, fmt: int) -> np.ndarray:
+        """f32 weights [n_out, n_in] -> host-format Q8 / Q4 blocks (uint8),
+        by the absmax rule of ``orc_quantize``."""
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        if w.ndim != 2:
+            raise ValueError("w must be [n_out, n_in]")
+        n_out, n_in = w.shape
+        need = int(self.lib.orc_weight_bytes(fmt, n_out, n_in))
+        if need < 0 or fmt == BF16:
+            raise ValueError("bad format or shape")
+        out = np.empty(need, dtype=np.uint8)
+        if self.lib.orc_quantize(_p(w), fmt, n_out, n_in, _p(out)) != 0:
+            raise ValueError("oracle quantize failed")
+        return out
+
     def check(self, y, y_ref, bound, tol: float = TOL) -> dict:
         """Element-wise |y - y_ref| <= tol * bound (NaN/Inf in y fail)."""
         y = np.ascontiguousarray(y, dtype=np.float32)
@@ -224,3 +260,11 @@ def matmul_points(x, weight, fmt, n_out, ii, rr, threads=0):
 
 def check(y, y_ref, bound, tol=TOL):
     return default().check(y, y_ref, bound, tol)
+
+
+def f16_bits(values):
+    return default().f16_bits(values)
+
+
+def quantize(w, fmt):
+    return default().quantize(w, fmt)

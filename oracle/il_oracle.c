@@ -144,6 +144,116 @@ int orc_dequant_row(const void *weight, int fmt, int64_t n_in, int64_t r, float 
     return -1;
 }
 
+/* ------------------------------------------------------------- quantiser
+ * The upload quantiser: the step before the matmul that builds the Q8 / Q4
+ * blocks from full-precision weights.  The pages import QMatrix / Q4Matrix
+ * without printing how they are built, so the rule is this library's
+ * reading: symmetric absmax scaling per 32-element block of a row.  With
+ * amax = max_e |w_e| over the block,
+ *   Q8: s = amax / 127 (one f32 division); q_e = rint(w_e / s) clamped to
+ *       [-127, 127]; the block stores s as f32;
+ *   Q4: s = the f32 quotient amax / 7 rounded to the nearest binary16 (ties
+ *       to even) and saturated at 65504, the largest finite binary16;
+ *       code_e = rint(w_e / s) clamped to [-8, 7], plus 8, with s the stored
+ *       binary16 scale read back as f32 -- so codes are chosen against the
+ *       scale the dequantisation will use;
+ *   a zero scale (amax == 0, or a quotient that rounds to 0) stores scale 0
+ *   and all-zero values (Q8 code 0, Q4 code 8).
+ * Every division is one correctly rounded f32 division and rint rounds half
+ * to even (the default rounding mode).  Inputs must be finite. */
+
+/* f32 -> binary16 bits, round to nearest even, from the format definition:
+ * bias 15, 10 fraction bits, subnormal quantum 2^-24; magnitudes from 65520
+ * (halfway between 65504 and 2^16) up round to Inf; NaN -> a quiet NaN. */
+uint16_t orc_f16_bits(float v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs((double)v);
+    if (isnan(v)) return 0x7E00;
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal or zero: a count of 2^-24 quanta (a count of 1024 is the
+         * smallest normal number, whose bits are exactly 1024) */
+        double q = nearbyint(a * ldexp(1.0, 24));
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    int e;
+    double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1): a = (1 + f/1024) * 2^(e-1) */
+    double f = nearbyint((2.0 * m - 1.0) * 1024.0);
+    int be = e - 1 + 15;
+    if (f == 1024.0) {
+        f = 0.0;
+        ++be;
+    }
+    if (be >= 31) return sign | 0x7C00; /* rounded past 65504: Inf */
+    return (uint16_t)(sign | (uint16_t)(be << 10) | (uint16_t)f);
+}
+
+void orc_f16_bits_array(const float *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_bits(v[i]);
+}
+
+static void wr_f32(uint8_t *p, float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    p[0] = (uint8_t)u;
+    p[1] = (uint8_t)(u >> 8);
+    p[2] = (uint8_t)(u >> 16);
+    p[3] = (uint8_t)(u >> 24);
+}
+
+/* f32 weights [n_out][n_in] -> host-format Q8 or Q4 blocks in `out`
+ * (orc_weight_bytes(fmt, n_out, n_in) bytes).  Returns 0, or -1 on a bad
+ * format (bf16 is not a quantised format) or shape. */
+int orc_quantize(const float *w, int fmt, int64_t n_out, int64_t n_in, uint8_t *out)
+{
+    if (fmt != ORC_Q8 && fmt != ORC_Q4) return -1;
+    if (orc_weight_bytes(fmt, n_out, n_in) < 0) return -1;
+    int64_t nb = n_in / ORC_BLOCK;
+    for (int64_t r = 0; r < n_out; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *src = w + (size_t)r * (size_t)n_in + (size_t)b * ORC_BLOCK;
+            float amax = 0.0f;
+            for (int e = 0; e < ORC_BLOCK; ++e)
+                if (fabsf(src[e]) > amax) amax = fabsf(src[e]);
+            if (fmt == ORC_Q8) {
+                uint8_t *blk = out + ((size_t)r * (size_t)nb + (size_t)b) * ORC_Q8_BLOCK_BYTES;
+                float s = amax / 127.0f;
+                wr_f32(blk, s);
+                for (int e = 0; e < ORC_BLOCK; ++e) {
+                    float q = 0.0f;
+                    if (s != 0.0f) {
+                        q = rintf(src[e] / s);
+                        if (q > 127.0f) q = 127.0f;
+                        if (q < -127.0f) q = -127.0f;
+                    }
+                    blk[4 + e] = (uint8_t)(int8_t)q;
+                }
+            } else {
+                uint8_t *blk = out + ((size_t)r * (size_t)nb + (size_t)b) * ORC_Q4_BLOCK_BYTES;
+                uint16_t sb = orc_f16_bits(amax / 7.0f);
+                if (sb == 0x7C00) sb = 0x7BFF; /* saturate at 65504 */
+                float s = (float)orc_f16_value(sb);
+                blk[0] = (uint8_t)sb;
+                blk[1] = (uint8_t)(sb >> 8);
+                memset(blk + 2, 0, 16);
+                for (int e = 0; e < ORC_BLOCK; ++e) {
+                    int code = 8;
+                    if (s != 0.0f) {
+                        float q = rintf(src[e] / s);
+                        if (q > 7.0f) q = 7.0f;
+                        if (q < -8.0f) q = -8.0f;
+                        code = (int)q + 8;
+                    }
+                    blk[2 + e / 2] |= (uint8_t)((e % 2 == 0) ? code : code << 4);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
 /* Equation (1) for output rows [r0, r1) of one weight.  y and bound are
  * [t][r1 - r0] row-major: y[i][j] = (float) sum_k x[i][k] * w[r0 + j][k] with
  * f64 products and an f64 running sum in increasing k; bound[i][j] =

@@ -231,6 +231,138 @@ def pin_roundtrip_q4(O):
     assert np.array_equal(w.astype(np.float64) / s + 8.0, codes.astype(np.float64)), "Q4 round trip"
 
 
+# --------------------------------------------------------------- quantiser
+# The upload quantiser (absmax per 32-element block; the rule is stated in
+# il_oracle.c).  Its pins: numpy's float16 cast on every binary16 value, on
+# every midpoint between neighbours and on random f32 values; hand-derived
+# blocks; exact round trips of codes on power-of-two scales; and, on random
+# blocks, the properties the rule implies (largest code reaches the grid end,
+# every code is the nearest grid point to its weight, the Q4 scale is the
+# nearest binary16 to amax / 7).  The block decoders below read the host
+# formats directly, without the oracle.
+def _q8_parts(blocks, n_out, n_in):
+    nb = n_in // 32
+    blk = np.asarray(blocks, dtype=np.uint8).reshape(n_out, nb, 36)
+    scales = blk[:, :, :4].copy().view("<f4").reshape(n_out, nb)
+    codes = blk[:, :, 4:].copy().view(np.int8).reshape(n_out, n_in)
+    return codes, scales
+
+
+def _q4_parts(blocks, n_out, n_in):
+    nb = n_in // 32
+    blk = np.asarray(blocks, dtype=np.uint8).reshape(n_out, nb, 18)
+    sbits = blk[:, :, :2].copy().view("<u2").reshape(n_out, nb)
+    qs = blk[:, :, 2:]
+    codes = np.empty((n_out, nb, 32), dtype=np.uint8)
+    codes[:, :, 0::2] = qs & 0x0F
+    codes[:, :, 1::2] = qs >> 4
+    return codes.reshape(n_out, n_in), sbits
+
+
+def pin_f16_rounding(O):
+    """f32 -> binary16 agrees with numpy's float16 cast (round to nearest
+    even) on every finite binary16 value, every midpoint between neighbours
+    (the ties) and random f32 values across the whole range."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = pats.view(np.float16)
+    fin = np.isfinite(vals)
+    got = O.f16_bits(vals[fin].astype(np.float32))
+    assert np.array_equal(got, pats[fin]), "f16 values do not map to themselves"
+    pos = np.sort(vals[fin & (vals >= 0) & ~np.signbit(vals)].astype(np.float64))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)  # exact: <= 12 significant bits
+    mids = np.concatenate([mids, -mids, np.float32([65520.0, -65520.0, 65519.0])])
+    rng = np.random.default_rng(20)
+    rnd = (rng.uniform(1, 2, 200000) * np.exp2(rng.integers(-30, 18, 200000))).astype(np.float32)
+    rnd *= np.where(rng.random(200000) < 0.5, -1, 1).astype(np.float32)
+    for v in (mids, rnd):
+        with np.errstate(over="ignore"):
+            want = v.astype(np.float16).view(np.uint16)
+        assert np.array_equal(O.f16_bits(v), want), "f16 rounding differs from numpy"
+    nan = int(O.f16_bits(np.float32([np.nan]))[0])
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0, "NaN must stay NaN"
+
+
+def pin_quantize_hand(O):
+    """Hand-derived blocks.  Q8: amax = 127/8, so s = 1/8 and w / s is the
+    list 127, -64, 0.5, 1.5, 2.5 -> codes 127, -64, 0, 2, 2 (ties to even).
+    Q4: amax = 7/4, s = 1/4 (binary16 0x3400) and w / s = 7, -7, 3.5, -0.5,
+    1.5, 2.5 -> values 7, -7, 4, 0, 2, 2 -> codes 15, 1, 12, 8, 10, 10."""
+    w8 = np.zeros((1, 32), np.float32)
+    w8[0, :5] = np.array([127, -64, 0.5, 1.5, 2.5]) / 8
+    codes, scales = _q8_parts(O.quantize(w8, Q8), 1, 32)
+    assert scales[0, 0] == np.float32(0.125), "Q8 hand scale"
+    assert list(codes[0, :5]) == [127, -64, 0, 2, 2] and not codes[0, 5:].any(), "Q8 hand codes"
+    w4 = np.zeros((1, 32), np.float32)
+    w4[0, :6] = np.array([7, -7, 3.5, -0.5, 1.5, 2.5]) / 4
+    codes, sbits = _q4_parts(O.quantize(w4, Q4), 1, 32)
+    assert sbits[0, 0] == 0x3400, "Q4 hand scale"
+    assert list(codes[0, :6]) == [15, 1, 12, 8, 10, 10] and np.all(codes[0, 6:] == 8), "Q4 hand codes"
+    z = np.zeros((2, 64), np.float32)
+    c8, s8 = _q8_parts(O.quantize(z, Q8), 2, 64)
+    c4, s4 = _q4_parts(O.quantize(z, Q4), 2, 64)
+    assert not c8.any() and not s8.any() and np.all(c4 == 8) and not s4.any(), "zero blocks"
+
+
+def pin_quantize_roundtrip(O):
+    """Codes on a power-of-two scale, each block holding the grid end (Q8
+    +-127, Q4 +-7): quantising the exact values returns those codes and
+    that scale bit for bit."""
+    rng = np.random.default_rng(21)
+    n_out, n_in = 24, 128
+    for fmt, top, exps in ((Q8, 127, range(-20, 4)), (Q4, 7, range(-14, 10))):
+        v = rng.integers(-top, top + 1, (n_out, n_in))
+        blocks = v.reshape(n_out, -1, 32)
+        pos = rng.integers(0, 32, blocks.shape[:2])
+        sign = np.where(rng.random(blocks.shape[:2]) < 0.5, -1, 1)
+        np.put_along_axis(blocks, pos[..., None], (top * sign)[..., None], axis=2)
+        e = np.array(list(exps))[:n_out]
+        w = (v.astype(np.float64) * np.exp2(e)[:, None]).astype(np.float32)
+        if fmt == Q8:
+            codes, scales = _q8_parts(O.quantize(w, Q8), n_out, n_in)
+            assert np.array_equal(codes, v), "Q8 codes do not round-trip"
+            assert np.array_equal(scales, np.repeat(np.exp2(e)[:, None], n_in // 32, 1).astype(np.float32))
+        else:
+            codes, sbits = _q4_parts(O.quantize(w, Q4), n_out, n_in)
+            assert np.array_equal(codes.astype(np.int64) - 8, v), "Q4 codes do not round-trip"
+            assert np.array_equal(sbits, np.repeat(((e + 15) << 10)[:, None], n_in // 32, 1)), "Q4 scale"
+
+
+def pin_quantize_nearest(O):
+    """Random blocks over 12 decades of scale: the Q8 scale is amax / 127 to
+    within f32 rounding and the largest |code| is 127; the Q4 scale is the
+    binary16 nearest amax / 7; every code is the grid point nearest its
+    weight on the stored scale (within f32 rounding of the quotient), or the
+    end of the grid it was clamped to."""
+    rng = np.random.default_rng(22)
+    n_out, n_in = 64, 256
+    sig = np.exp2(rng.uniform(-20, 20, (n_out, 1)))
+    w = (rng.standard_normal((n_out, n_in)) * sig).astype(np.float32)
+    w[3, 32:64] = 0.0  # one all-zero block
+    amax = np.abs(w.astype(np.float64)).reshape(n_out, -1, 32).max(axis=2)
+    slack = 1 + 2.0 ** -20
+    codes, scales = _q8_parts(O.quantize(w, Q8), n_out, n_in)
+    s = scales.astype(np.float64)
+    assert np.all(np.abs(s * 127 - amax) <= amax * 2.0 ** -22), "Q8 scale is not amax / 127"
+    nz = amax > 0
+    top = np.abs(codes.astype(np.int64)).reshape(n_out, -1, 32).max(axis=2)
+    assert np.all(top[nz] == 127) and np.all(top[~nz] == 0), "Q8 grid end not reached"
+    se = np.repeat(s, 32, axis=1)
+    err = np.abs(w - codes * se)
+    assert np.all(err <= 0.5 * se * slack), "Q8 code is not the nearest grid point"
+    codes, sbits = _q4_parts(O.quantize(w, Q4), n_out, n_in)
+    s16 = lib_f16(sbits)
+    q = amax / 7
+    spacing = np.spacing(s16.astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(s16 - q) <= 0.5 * spacing * slack), "Q4 scale is not the nearest binary16"
+    se = np.repeat(s16, 32, axis=1)
+    v = codes.astype(np.float64) - 8
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(se > 0, w / se, 0.0)
+    inside = (ratio >= -8.5) & (ratio <= 7.5)
+    assert np.all(np.abs(w - v * se)[inside] <= 0.5 * se[inside] * slack), "Q4 code is not the nearest"
+    assert np.all(v[ratio > 7.5] == 7) and np.all(v[ratio < -8.5] == -8), "Q4 clamp"
+
+
 # -------------------------------------------------------------- brute force
 def _exact_values(fmt, parts):
     """Exact rationals of every weight element, from library-decoded values."""
@@ -373,6 +505,7 @@ ALL_PINS = [
     pin_bf16_exhaustive, pin_f16_exhaustive, pin_goldens, pin_onehot, pin_identity,
     pin_row_sums, pin_zero_codes, pin_roundtrip_q8, pin_roundtrip_q4, pin_bruteforce,
     pin_numpy_matmul, pin_points_equal_rows, pin_thread_invariance, pin_check_rule,
+    pin_f16_rounding, pin_quantize_hand, pin_quantize_roundtrip, pin_quantize_nearest,
 ]
 
 

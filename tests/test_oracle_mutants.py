@@ -49,6 +49,17 @@ MUTANTS = {
     "points_x_row": ("const float *xi = x + (size_t)ii[p] * (size_t)n_in;", "const float *xi = x;"),
     "check_loose": ("ok = (err <= tol * bound[e]);", "ok = (err <= 2 * tol * bound[e]);"),
     "check_zero_bound": ("ok = (err == 0.0);", "ok = 1;"),
+    "f16_round_down": ("double f = nearbyint((2.0 * m - 1.0) * 1024.0);",
+                       "double f = floor((2.0 * m - 1.0) * 1024.0);"),
+    "f16_subnormal_round_down": ("double q = nearbyint(a * ldexp(1.0, 24));",
+                                 "double q = floor(a * ldexp(1.0, 24));"),
+    "f16_overflow": ("if (be >= 31) return sign", "if (be >= 32) return sign"),
+    "quant_q8_divisor": ("float s = amax / 127.0f;", "float s = amax / 128.0f;"),
+    "quant_q8_truncate": ("q = rintf(src[e] / s);\n                        if (q > 127.0f)",
+                          "q = truncf(src[e] / s);\n                        if (q > 127.0f)"),
+    "quant_q4_divisor": ("orc_f16_bits(amax / 7.0f)", "orc_f16_bits(amax / 8.0f)"),
+    "quant_q4_nibbles": ("(e % 2 == 0) ? code : code << 4", "(e % 2 == 0) ? code << 4 : code"),
+    "quant_q4_unrounded_scale": ("float s = (float)orc_f16_value(sb);", "float s = amax / 7.0f;"),
 }
 
 _CHILD = r"""
