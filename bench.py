@@ -118,12 +118,97 @@ def cpu_baseline(sub: wl.Submission, x, weights, budget_s: float) -> dict:
             "sample": sample, "seconds": round(el, 2)}
 
 
+def stats_device_ms(il, path: str) -> float:
+    """Cumulative device time (IL_TIMING=1) of one path from il_stats."""
+    for line in il.il_stats().splitlines():
+        if line.startswith(path + ":"):
+            return float(line.split("device_ms=")[1].split()[0])
+    raise RuntimeError(f"no {path} line in il_stats")
+
+
+def bench_quantize(args, name: str) -> int:
+    """The upload quantiser: f32 weights resident in HBM -> Q8 / Q4 device
+    planes, one il_upload_quantize call per step.  value = f32 input bytes
+    per second of whole calls (plane allocation included); the roofline
+    takes the quantise kernel alone (HIP events around its launch on the
+    library's upload stream, read back through il_stats)."""
+    import torch
+
+    import quantized_weight_matmul_amd as il
+    os.environ["IL_TIMING"] = "1"
+    fmt, n_out, n_in, cfg, tid = wl.QUANTIZE[name]
+    n = n_out * n_in
+    code_b = n if fmt == wl.Q8 else n // 2
+    scale_b = (n // wl.BLOCK) * (4 if fmt == wl.Q8 else 2)
+    algo = 4 * n + code_b + 2 * scale_b  # read f32; write codes, scales and their tiled copy
+    log(f"[bench] workload {name}: f32 [{n_out}, {n_in}] -> {wl.FMT_NAMES[fmt]} on upload")
+    w_np = wl.gen_f32_weight(cfg, tid, n_out, n_in)
+    w = torch.from_numpy(w_np).cuda()
+    torch.cuda.synchronize()
+
+    def call():
+        h = il.il_upload_quantize(w, il.IL_SRC_F32, fmt, n_out, n_in)
+        if h is None:
+            raise RuntimeError(il.il_last_error())
+        return h
+
+    for _ in range(args.warmup):
+        call().free()
+    steps = args.steps
+    dev0 = stats_device_ms(il, "upload_quantize")
+    keep, wall = [], 0.0
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        keep.append(call())
+        wall += time.perf_counter() - t0
+    kern_ms = (stats_device_ms(il, "upload_quantize") - dev0) / steps
+    for h in keep:
+        h.free()
+    ms_per_step = wall * 1e3 / steps
+    value = 4 * n / (ms_per_step * 1e-3) / 1e9
+    achieved = algo / (kern_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
+                "kernel_ms": round(kern_ms, 6),
+                "timing": "HIP events around each quantise launch on its stream (il_stats device_ms)",
+                "algorithmic_bytes_per_launch": algo}
+    log(f"[bench] {ms_per_step * 1e3:.1f} us per call ({value:.1f} GB/s of f32 in); kernel "
+        f"{kern_ms * 1e3:.2f} us ({achieved:.1f} GB/s algorithmic)")
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        threads = 1  # the oracle quantiser is serial
+        rows = max(16, min(n_out, int(2e6 // n_in)))
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.quantize(w_np[:rows], fmt)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or el / reps * (reps + 1) > args.cpu_seconds * 2:
+                break
+        cpu = {"value": round(4 * rows * n_in * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle", "sample": f"{reps} oracle quantisations of the first {rows} rows",
+               "seconds": round(el, 2)}
+    out = {
+        "metric": "quantised GB/s of f32 weights (upload quantiser); roofline on HBM bytes",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{name}: quantise f32 [{n_out}, {n_in}] ~N(0, 0.02) to "
+                               f"{wl.FMT_NAMES[fmt]} on upload (input resident in HBM)",
+                   "n_out": n_out, "n_in": n_in, "format": wl.FMT_NAMES[fmt]},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="c2", choices=sorted(wl.SUBMISSIONS))
+    ap.add_argument("--workload", default="c2", choices=sorted(wl.SUBMISSIONS) + sorted(wl.QUANTIZE))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -154,6 +239,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.workload in wl.QUANTIZE:
+        return bench_quantize(args, args.workload)
     sub = wl.SUBMISSIONS[args.workload]
     decode = sub.t <= 8
     streaming = sub.t <= STREAMING_MAX_T

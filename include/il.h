@@ -82,6 +82,50 @@ typedef struct {
  * reason is in il_last_error(). */
 IL_API il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in);
 
+/* Element type of the full-precision weights given to il_upload_quantize. */
+typedef enum {
+    IL_SRC_F32 = 0,  /* float[n_out][n_in] */
+    IL_SRC_BF16 = 1  /* uint16_t[n_out][n_in], raw bfloat16 bits */
+} il_src;
+
+/* Quantise on upload -- builds a Q8 or Q4 weight on the device from
+ * full-precision weights (the step before `enum WeightRef`'s Q8 / Q4 on the
+ * oxinfer 0.0.0 src/gpu.rs page: constructing the QMatrix / Q4Matrix that
+ * page imports; the README page's "quantized weights").  The pages do not
+ * show the quantiser, so this library's rule is symmetric absmax scaling per
+ * 32-element block of a row, with amax = max |w| over the block:
+ *   IL_Q8: s = amax / 127 (f32 division); q = rint(w / s) clamped to
+ *          [-127, 127]; the block stores s as f32;
+ *   IL_Q4: s = amax / 7 (f32 division) rounded to the nearest binary16 (ties
+ *          to even), saturated at 65504; code = rint(w / s) clamped to
+ *          [-8, 7], plus 8, where s is the stored binary16 value;
+ *   a zero scale stores 0 and all-zero values (Q8 code 0, Q4 code 8).
+ * rint rounds half to even; every division is correctly rounded.
+ *   weight : HOST or DEVICE pointer (on the current device) to n_out * n_in
+ *            elements of type `src`, row-major; borrowed for the call (a
+ *            host buffer is copied to the device first).  Device contents
+ *            must be complete when the call starts (synchronize the stream
+ *            that wrote them).  Elements must be finite.
+ *   src    : IL_SRC_F32 or IL_SRC_BF16.
+ *   fmt    : IL_Q8 or IL_Q4 (IL_BF16 is rejected: nothing to quantise to).
+ *   n_out, n_in : as for il_upload (n_in a positive multiple of 32).
+ * The handle is the same kind il_upload returns: il_download of it yields
+ * the host-format blocks of the rule above, and il_matmul uses it like any
+ * other.  Synchronous.  Returns NULL on failure (bad arguments, no device,
+ * out of memory); the reason is in il_last_error(). */
+IL_API il_weight *il_upload_quantize(const void *weight, int src, int fmt, int64_t n_out, int64_t n_in);
+
+/* Export -- writes the weight of a handle back in its host format (see
+ * il_fmt: bf16 words, or the Q8 / Q4 blocks), bit for bit what il_upload
+ * would accept to recreate it.
+ *   host_out : HOST buffer of at least il_weight_bytes(w) bytes, or NULL.
+ *   cap      : size of host_out in bytes.
+ * Returns the number of bytes the host format needs; the bytes are written
+ * only when host_out is not NULL and cap is at least that number (so a call
+ * with NULL, 0 is a size query).  Synchronous.  Returns -1 on failure (NULL
+ * handle, device error), with the reason in il_last_error(). */
+IL_API int64_t il_download(const il_weight *w, void *host_out, int64_t cap);
+
 /* Drops a handle and its device memory.  NULL is ignored.  The caller must
  * make sure no il_matmul still using it is in flight (synchronize the
  * streams it was used on first). */
@@ -116,7 +160,9 @@ IL_API int il_wants(int64_t n_out, int64_t n_in, int64_t t);
 IL_API const char *il_name(void);
 
 /* Backend::stats -- cumulative summary (calls, jobs and weight bytes per
- * kernel path; device times when IL_TIMING=1 is set) written as text into
+ * kernel path -- decode GEMV, prefill GEMM, upload quantiser, whose bytes are
+ * the full-precision input; device times of the kernels, from HIP events
+ * around their launches, when IL_TIMING=1 is set) written as text into
  * buf (NUL-terminated, truncated to cap bytes).  Returns the length the full
  * text needs, excluding the NUL; buf may be NULL when cap is 0. */
 IL_API int64_t il_stats(char *buf, int64_t cap);

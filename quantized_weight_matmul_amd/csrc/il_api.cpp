@@ -112,7 +112,7 @@ DeviceCtx *context(int *device_out) {
 struct PathStats {
     std::atomic<uint64_t> calls{0}, launches{0}, jobs{0}, bytes{0}, flops{0}, timed_ns{0};
 };
-PathStats g_stats[2];  // 0: decode GEMV, 1: prefill GEMM
+PathStats g_stats[3];  // 0: decode GEMV, 1: prefill GEMM, 2: upload quantiser
 std::atomic<uint64_t> g_uploads{0}, g_upload_bytes{0}, g_failed{0};
 
 int64_t host_bytes(int fmt, int64_t n_out, int64_t n_in) {
@@ -151,9 +151,96 @@ bool device_range_ok(const void *ptr, int64_t bytes, const char *what) {
     return true;
 }
 
+// Device (or managed) memory, and on which device; false for host memory.
+bool device_pointer(const void *ptr, int *device) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return false;
+    *device = attr.device;
+    return true;
+}
+
+bool timing_on() {
+    const char *v = getenv("IL_TIMING");
+    return v && strcmp(v, "1") == 0;
+}
+
 bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
     const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
     return pa < pb + nb && pb < pa + na;
+}
+
+// One weight's device planes (layouts in il_internal.h) in a single
+// allocation: codes, then scales and the tiled scale copy (Q8 / Q4).
+struct Planes {
+    void *alloc = nullptr;
+    char *codes = nullptr, *scales = nullptr, *scales_t = nullptr;
+    int64_t tiled_bytes = 0;
+};
+
+bool alloc_planes(const char *who, int fmt, int64_t n_out, int64_t n_in, Planes *pl) {
+    const int64_t nb = n_in / il::kBlock;
+    int64_t code_bytes = 0, scale_size = 0;
+    if (fmt == IL_BF16) code_bytes = 2 * n_out * n_in;
+    if (fmt == IL_Q8) code_bytes = n_out * n_in, scale_size = 4;
+    if (fmt == IL_Q4) code_bytes = n_out * n_in / 2, scale_size = 2;
+    const int64_t scale_bytes = scale_size * n_out * nb;
+    pl->tiled_bytes = scale_size * il::tiled_scale_count(n_out, nb);
+    const int64_t code_alloc = (code_bytes + 255) / 256 * 256;
+    const int64_t scale_alloc = (scale_bytes + 255) / 256 * 256;
+    const int64_t total = code_alloc + scale_alloc + pl->tiled_bytes;
+    hipError_t e = hipMalloc(&pl->alloc, (size_t)total);
+    if (e != hipSuccess) {
+        set_err("%s: hipMalloc(%" PRId64 ") failed: %s", who, total, hipGetErrorString(e));
+        pl->alloc = nullptr;
+        return false;
+    }
+    pl->codes = static_cast<char *>(pl->alloc);
+    pl->scales = scale_bytes ? pl->codes + code_alloc : nullptr;
+    pl->scales_t = scale_bytes ? pl->codes + code_alloc + scale_alloc : nullptr;
+    return true;
+}
+
+il_weight *make_handle(int fmt, int dev, int64_t n_out, int64_t n_in, const Planes &pl) {
+    il_weight *w = new il_weight();
+    w->fmt = fmt;
+    w->device = dev;
+    w->n_out = n_out;
+    w->n_in = n_in;
+    w->host_bytes = host_bytes(fmt, n_out, n_in);
+    w->alloc = pl.alloc;
+    w->codes = pl.codes;
+    w->scales = pl.scales;
+    w->scales_t = pl.scales_t;
+    g_uploads++;
+    g_upload_bytes += (uint64_t)w->host_bytes;
+    return w;
+}
+
+bool shape_ok(const char *who, int64_t n_out, int64_t n_in) {
+    if (n_out < 1 || n_out > INT_MAX) {
+        set_err("%s: n_out = %" PRId64 " is outside [1, %d]", who, n_out, INT_MAX);
+        return false;
+    }
+    if (n_in < il::kBlock || n_in % il::kBlock || n_in > INT_MAX) {
+        set_err("%s: n_in = %" PRId64 " must be a positive multiple of 32", who, n_in);
+        return false;
+    }
+    return true;
+}
+
+// Runs f with the handle's device current, restoring the caller's after.
+template <class F>
+auto on_device(int device, F f) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != device) (void)hipSetDevice(device);
+    auto r = f();
+    if (cur != device && cur >= 0) (void)hipSetDevice(cur);
+    return r;
 }
 
 }  // namespace
@@ -171,14 +258,7 @@ il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in) {
         set_err("il_upload: unknown format %d", fmt);
         return nullptr;
     }
-    if (n_out < 1 || n_out > INT_MAX) {
-        set_err("il_upload: n_out = %" PRId64 " is outside [1, %d]", n_out, INT_MAX);
-        return nullptr;
-    }
-    if (n_in < il::kBlock || n_in % il::kBlock || n_in > INT_MAX) {
-        set_err("il_upload: n_in = %" PRId64 " must be a positive multiple of 32", n_in);
-        return nullptr;
-    }
+    if (!shape_ok("il_upload", n_out, n_in)) return nullptr;
     if (env_flag("IL_FORCE_FAIL", "upload")) {
         set_err("il_upload: failure injected by IL_FORCE_FAIL");
         return nullptr;
@@ -187,27 +267,12 @@ il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in) {
     DeviceCtx *ctx = context(&dev);
     if (!ctx) return nullptr;
 
-    const int64_t nb = n_in / il::kBlock;
     const int64_t hb = host_bytes(fmt, n_out, n_in);
-    int64_t code_bytes = 0, scale_bytes = 0, scale_size = 0;
-    if (fmt == IL_BF16) code_bytes = 2 * n_out * n_in;
-    if (fmt == IL_Q8) code_bytes = n_out * n_in, scale_size = 4;
-    if (fmt == IL_Q4) code_bytes = n_out * n_in / 2, scale_size = 2;
-    scale_bytes = scale_size * n_out * nb;
-    const int64_t tiled_bytes = scale_size * il::tiled_scale_count(n_out, nb);
-    const int64_t code_alloc = (code_bytes + 255) / 256 * 256;
-    const int64_t scale_alloc = (scale_bytes + 255) / 256 * 256;
-
-    void *alloc = nullptr;
-    hipError_t e = hipMalloc(&alloc, (size_t)(code_alloc + scale_alloc + tiled_bytes));
-    if (e != hipSuccess) {
-        set_err("il_upload: hipMalloc(%" PRId64 ") failed: %s", code_alloc + scale_alloc + tiled_bytes,
-                hipGetErrorString(e));
-        return nullptr;
-    }
-    char *codes = static_cast<char *>(alloc);
-    char *scales = scale_bytes ? codes + code_alloc : nullptr;
-    char *scales_t = scale_bytes ? codes + code_alloc + scale_alloc : nullptr;
+    Planes pl;
+    if (!alloc_planes("il_upload", fmt, n_out, n_in, &pl)) return nullptr;
+    char *codes = pl.codes, *scales = pl.scales, *scales_t = pl.scales_t;
+    const int64_t tiled_bytes = pl.tiled_bytes;
+    hipError_t e = hipSuccess;
     hipStream_t s = ctx->upload_stream;
     void *staging = nullptr;
     if (fmt == IL_BF16) {
@@ -230,23 +295,121 @@ il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in) {
     if (e == hipSuccess) e = se;
     if (staging) (void)hipFree(staging);
     if (e != hipSuccess) {
-        (void)hipFree(alloc);
+        (void)hipFree(pl.alloc);
         set_err("il_upload: copy/repack failed: %s", hipGetErrorString(e));
         return nullptr;
     }
-    il_weight *w = new il_weight();
-    w->fmt = fmt;
-    w->device = dev;
-    w->n_out = n_out;
-    w->n_in = n_in;
-    w->host_bytes = hb;
-    w->alloc = alloc;
-    w->codes = codes;
-    w->scales = scales;
-    w->scales_t = scales_t;
-    g_uploads++;
-    g_upload_bytes += (uint64_t)hb;
-    return w;
+    return make_handle(fmt, dev, n_out, n_in, pl);
+}
+
+il_weight *il_upload_quantize(const void *weight, int src, int fmt, int64_t n_out, int64_t n_in) {
+    g_err.clear();
+    if (!weight) {
+        set_err("il_upload_quantize: weight is NULL");
+        return nullptr;
+    }
+    if (src != IL_SRC_F32 && src != IL_SRC_BF16) {
+        set_err("il_upload_quantize: unknown source type %d", src);
+        return nullptr;
+    }
+    if (fmt != IL_Q8 && fmt != IL_Q4) {
+        set_err("il_upload_quantize: format %d is not a quantised format (IL_Q8 or IL_Q4)", fmt);
+        return nullptr;
+    }
+    if (!shape_ok("il_upload_quantize", n_out, n_in)) return nullptr;
+    if (env_flag("IL_FORCE_FAIL", "upload")) {
+        set_err("il_upload_quantize: failure injected by IL_FORCE_FAIL");
+        return nullptr;
+    }
+    int dev = -1;
+    DeviceCtx *ctx = context(&dev);
+    if (!ctx) return nullptr;
+    const int64_t src_bytes = n_out * n_in * (src == IL_SRC_F32 ? 4 : 2);
+    int wdev = -1;
+    const bool in_hbm = device_pointer(weight, &wdev);
+    if (in_hbm) {
+        if (wdev != dev) {
+            set_err("il_upload_quantize: weight is on device %d, the current device is %d", wdev, dev);
+            return nullptr;
+        }
+        if (!device_range_ok(weight, src_bytes, "il_upload_quantize: weight")) return nullptr;
+    }
+    Planes pl;
+    if (!alloc_planes("il_upload_quantize", fmt, n_out, n_in, &pl)) return nullptr;
+    hipStream_t s = ctx->upload_stream;
+    void *staging = nullptr;
+    hipError_t e = hipSuccess;
+    if (!in_hbm) {
+        e = hipMalloc(&staging, (size_t)src_bytes);
+        if (e == hipSuccess) e = hipMemcpyAsync(staging, weight, (size_t)src_bytes, hipMemcpyHostToDevice, s);
+    }
+    // the tiled plane's padding (rows past n_out, blocks past nb) reads zero
+    if (e == hipSuccess) e = hipMemsetAsync(pl.scales_t, 0, (size_t)pl.tiled_bytes, s);
+    const bool timing = timing_on();
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if (timing) {
+        (void)hipEventCreate(&ev0);
+        (void)hipEventCreate(&ev1);
+        (void)hipEventRecord(ev0, s);
+    }
+    if (e == hipSuccess)
+        e = il::launch_quantize(fmt, src == IL_SRC_F32 ? il::SRC_F32 : il::SRC_BF16, in_hbm ? weight : staging,
+                                reinterpret_cast<uint8_t *>(pl.codes), pl.scales, pl.scales_t, n_out, n_in, s);
+    if (timing) (void)hipEventRecord(ev1, s);
+    hipError_t se = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = se;
+    if (timing) {
+        float ms = 0.f;
+        if (e == hipSuccess && hipEventElapsedTime(&ms, ev0, ev1) == hipSuccess)
+            g_stats[2].timed_ns += (uint64_t)(ms * 1e6);
+        (void)hipEventDestroy(ev0);
+        (void)hipEventDestroy(ev1);
+    }
+    if (staging) (void)hipFree(staging);
+    if (e != hipSuccess) {
+        (void)hipFree(pl.alloc);
+        set_err("il_upload_quantize: copy/quantise failed: %s", hipGetErrorString(e));
+        return nullptr;
+    }
+    g_stats[2].calls++;
+    g_stats[2].launches++;
+    g_stats[2].jobs++;
+    g_stats[2].bytes += (uint64_t)src_bytes;
+    return make_handle(fmt, dev, n_out, n_in, pl);
+}
+
+int64_t il_download(const il_weight *w, void *host_out, int64_t cap) {
+    g_err.clear();
+    if (!w) {
+        set_err("il_download: handle is NULL");
+        return -1;
+    }
+    const int64_t hb = w->host_bytes;
+    if (!host_out || cap < hb) return hb;  // size query
+    return on_device(w->device, [&]() -> int64_t {
+        DeviceCtx *ctx = context(nullptr);
+        if (!ctx) return -1;
+        hipStream_t s = ctx->upload_stream;
+        void *staging = nullptr;
+        hipError_t e = hipSuccess;
+        if (w->fmt == IL_BF16) {
+            e = hipMemcpyAsync(host_out, w->codes, (size_t)hb, hipMemcpyDeviceToHost, s);
+        } else {
+            e = hipMalloc(&staging, (size_t)hb);
+            if (e == hipSuccess)
+                e = il::launch_unrepack(w->fmt, w->codes, w->scales, static_cast<uint8_t *>(staging), w->n_out,
+                                        w->n_in, s);
+            if (e == hipSuccess) e = hipMemcpyAsync(host_out, staging, (size_t)hb, hipMemcpyDeviceToHost, s);
+        }
+        hipError_t se = hipStreamSynchronize(s);
+        if (e == hipSuccess) e = se;
+        if (staging) (void)hipFree(staging);
+        if (e != hipSuccess) {
+            set_err("il_download: %s", hipGetErrorString(e));
+            return (int64_t)-1;
+        }
+        return hb;
+    });
 }
 
 void il_free(il_weight *w) {
@@ -412,8 +575,8 @@ const char *il_name(void) { return "il-hip-gfx950"; }
 int64_t il_stats(char *buf, int64_t cap) {
     std::string s;
     char line[256];
-    const char *names[2] = {"decode_gemv", "prefill_gemm"};
-    for (int i = 0; i < 2; ++i) {
+    const char *names[3] = {"decode_gemv", "prefill_gemm", "upload_quantize"};
+    for (int i = 0; i < 3; ++i) {
         const PathStats &p = g_stats[i];
         snprintf(line, sizeof line,
                  "%s: calls=%" PRIu64 " launches=%" PRIu64 " jobs=%" PRIu64 " weight_bytes=%" PRIu64

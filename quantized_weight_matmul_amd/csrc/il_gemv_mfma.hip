@@ -260,7 +260,6 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     // Rows of tokens >= t read zeros.
     const int tok = kWide ? n : (n & 7);
     const uint32_t lo_mask = (!kWide && n >= 8) ? 0xFFFFFFFFu : 0u;
-    const bool xrow_ok = tok < t;
     constexpr bool kXb16 = NG >= 2;  // x given as bf16
     constexpr int esz = kXb16 ? 2 : 4;
     const __amdgpu_buffer_rsrc_t xrs =

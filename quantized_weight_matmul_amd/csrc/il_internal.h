@@ -60,6 +60,13 @@ struct KJob {
 };
 
 // ---- upload / repack (il_repack.hip) ----
+enum : int { SRC_F32 = 0, SRC_BF16 = 1 };  // element type of a weight to quantise
+// f32 / bf16 [n_out][n_in] (device) -> the Q8 / Q4 device planes.
+hipError_t launch_quantize(int fmt, int src_type, const void *src, uint8_t *codes, void *scales, void *scales_t,
+                           int64_t n_out, int64_t n_in, hipStream_t s);
+// Q8 / Q4 device planes -> host-format blocks in `out` (device memory).
+hipError_t launch_unrepack(int fmt, const void *codes, const void *scales, uint8_t *out, int64_t n_out,
+                           int64_t n_in, hipStream_t s);
 hipError_t launch_repack_q8(const uint8_t *staging, int8_t *codes, float *scales, float *scales_t,
                             int64_t n_out, int64_t n_in, hipStream_t s);
 hipError_t launch_repack_q4(const uint8_t *staging, uint8_t *codes, uint16_t *scales, uint16_t *scales_t,

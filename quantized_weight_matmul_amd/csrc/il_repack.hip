@@ -4,9 +4,11 @@
 // The host bytes are first copied to a device staging buffer; these kernels
 // then split the packed array-of-blocks formats into a K-contiguous code plane
 // and a separate scale plane, plus a tiled copy of the scales (layouts in
-// il_internal.h).  Integer byte moves
-// only: every value is preserved bit for bit.  BF16 needs no kernel, its host
-// layout is already the device layout.
+// il_internal.h).  Integer byte moves only: every value is preserved bit for
+// bit.  BF16 needs no kernel, its host layout is already the device layout.
+// Also here: the quantiser that builds the Q8 / Q4 planes from f32 or bf16
+// weights on upload, and the inverse repack that writes a weight back in its
+// host format.
 #include "il_internal.h"
 
 namespace il {
@@ -52,7 +54,142 @@ __global__ void repack_q4_kernel(const uint16_t *__restrict__ staging,
     codes[b] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// ---- quantise on upload: full-precision weights -> the Q8 / Q4 planes ----
+// Per 32-element block of a row, with amax = max |w| over the block
+// (symmetric absmax scaling; the pages import QMatrix / Q4Matrix without
+// showing how they are built, so this rule is a reading):
+//   Q8: s = amax / 127 (f32); q = rint(w / s) clamped to [-127, 127];
+//   Q4: s = binary16(amax / 7), round to nearest even, saturated at 65504;
+//       q = rint(w / s) clamped to [-8, 7] against that stored scale, and the
+//       nibble holds q's 4-bit two's complement (= code ^ 8, code = q + 8);
+//   a zero scale stores 0 and all-zero values.
+// Divisions are the correctly rounded f32 division, rint rounds half to even.
+// Eight lanes share a block, four consecutive elements each (one 16-byte
+// load of f32, 8 bytes of bf16), and find amax with three lane exchanges.
+template <int FMT, int SRC>
+__global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ src, uint8_t *__restrict__ codes,
+                                                       void *__restrict__ scales, void *__restrict__ scales_t,
+                                                       int64_t n_blocks, int64_t nb) {
+    const int64_t b = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+    const int part = threadIdx.x & 7;  // elements 4 part .. 4 part + 3 of the block
+    const bool live = b < n_blocks;
+    const int64_t e0 = b * kBlock + 4 * part;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+        if constexpr (SRC == SRC_F32) {
+            const float4 f = static_cast<const float4 *>(src)[e0 / 4];
+            v[0] = f.x, v[1] = f.y, v[2] = f.z, v[3] = f.w;
+        } else {
+            const uint2 h = static_cast<const uint2 *>(src)[e0 / 4];  // bf16 -> f32 is exact
+            v[0] = __builtin_bit_cast(float, h.x << 16), v[1] = __builtin_bit_cast(float, h.x & 0xFFFF0000u);
+            v[2] = __builtin_bit_cast(float, h.y << 16), v[3] = __builtin_bit_cast(float, h.y & 0xFFFF0000u);
+        }
+    }
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    if (!live) return;
+    const int64_t row = b / nb, blk = b - row * nb;
+    const int64_t ti = tiled_scale_index(row, blk, (nb + 3) / 4);
+    if constexpr (FMT == FMT_Q8) {
+        const float s = amax / 127.0f;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float q = 0.f;
+            if (s != 0.f) q = fminf(fmaxf(rintf(v[i] / s), -127.f), 127.f);
+            packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * i);
+        }
+        *reinterpret_cast<uint32_t *>(codes + e0) = packed;
+        if (part == 0) {
+            static_cast<float *>(scales)[b] = s;
+            static_cast<float *>(scales_t)[ti] = s;
+        }
+    } else {
+        uint16_t sb = __builtin_bit_cast(uint16_t, (_Float16)(amax / 7.0f));
+        if (sb == 0x7C00u) sb = 0x7BFFu;
+        const float s = (float)__builtin_bit_cast(_Float16, sb);
+        uint32_t nib = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float q = 0.f;
+            if (s != 0.f) q = fminf(fmaxf(rintf(v[i] / s), -8.f), 7.f);
+            nib |= ((uint32_t)(int)q & 0xFu) << (4 * i);
+        }
+        // elements 4 part + i sit in bytes 2 part (i < 2) and 2 part + 1,
+        // element 2j in the low nibble of byte j
+        *reinterpret_cast<uint16_t *>(codes + e0 / 2) = (uint16_t)nib;
+        if (part == 0) {
+            static_cast<uint16_t *>(scales)[b] = sb;
+            static_cast<uint16_t *>(scales_t)[ti] = sb;
+        }
+    }
+}
+
+// ---- download: the device planes back to the host block formats ----
+// One thread per block, the inverse of the repack kernels above.
+__global__ void unrepack_q8_kernel(const uint4 *__restrict__ codes, const float *__restrict__ scales,
+                                   uint32_t *__restrict__ out, int64_t n_blocks) {
+    int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= n_blocks) return;
+    const uint4 c0 = codes[2 * b], c1 = codes[2 * b + 1];
+    uint32_t *dst = out + b * 9;
+    dst[0] = __builtin_bit_cast(uint32_t, scales[b]);
+    dst[1] = c0.x, dst[2] = c0.y, dst[3] = c0.z, dst[4] = c0.w;
+    dst[5] = c1.x, dst[6] = c1.y, dst[7] = c1.z, dst[8] = c1.w;
+}
+
+__global__ void unrepack_q4_kernel(const uint4 *__restrict__ codes, const uint16_t *__restrict__ scales,
+                                   uint16_t *__restrict__ out, int64_t n_blocks) {
+    int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= n_blocks) return;
+    const uint4 c = codes[b];
+    const uint32_t w[4] = {c.x ^ 0x88888888u, c.y ^ 0x88888888u, c.z ^ 0x88888888u, c.w ^ 0x88888888u};
+    uint16_t *dst = out + b * 9;
+    dst[0] = scales[b];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        dst[1 + 2 * i] = (uint16_t)w[i];
+        dst[2 + 2 * i] = (uint16_t)(w[i] >> 16);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_quantize(int fmt, int src_type, const void *src, uint8_t *codes, void *scales, void *scales_t,
+                           int64_t n_out, int64_t n_in, hipStream_t s) {
+    const int64_t n_blocks = n_out * (n_in / kBlock);
+    const int64_t grid = (n_blocks * 8 + 255) / 256;
+    const int64_t nb = n_in / kBlock;
+    const dim3 g((unsigned)grid), t(256);
+    if (fmt == FMT_Q8 && src_type == SRC_F32)
+        hipLaunchKernelGGL((quantize_kernel<FMT_Q8, SRC_F32>), g, t, 0, s, src, codes, scales, scales_t, n_blocks, nb);
+    else if (fmt == FMT_Q8 && src_type == SRC_BF16)
+        hipLaunchKernelGGL((quantize_kernel<FMT_Q8, SRC_BF16>), g, t, 0, s, src, codes, scales, scales_t, n_blocks, nb);
+    else if (fmt == FMT_Q4 && src_type == SRC_F32)
+        hipLaunchKernelGGL((quantize_kernel<FMT_Q4, SRC_F32>), g, t, 0, s, src, codes, scales, scales_t, n_blocks, nb);
+    else if (fmt == FMT_Q4 && src_type == SRC_BF16)
+        hipLaunchKernelGGL((quantize_kernel<FMT_Q4, SRC_BF16>), g, t, 0, s, src, codes, scales, scales_t, n_blocks, nb);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_unrepack(int fmt, const void *codes, const void *scales, uint8_t *out, int64_t n_out,
+                           int64_t n_in, hipStream_t s) {
+    const int64_t n_blocks = n_out * (n_in / kBlock);
+    const dim3 g((unsigned)((n_blocks + 255) / 256)), t(256);
+    if (fmt == FMT_Q8)
+        hipLaunchKernelGGL(unrepack_q8_kernel, g, t, 0, s, static_cast<const uint4 *>(codes),
+                           static_cast<const float *>(scales), reinterpret_cast<uint32_t *>(out), n_blocks);
+    else if (fmt == FMT_Q4)
+        hipLaunchKernelGGL(unrepack_q4_kernel, g, t, 0, s, static_cast<const uint4 *>(codes),
+                           static_cast<const uint16_t *>(scales), reinterpret_cast<uint16_t *>(out), n_blocks);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_repack_q8(const uint8_t *staging, int8_t *codes, float *scales, float *scales_t,
                             int64_t n_out, int64_t n_in, hipStream_t s) {

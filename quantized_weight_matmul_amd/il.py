@@ -13,6 +13,7 @@ import threading
 import numpy as np
 
 IL_BF16, IL_Q8, IL_Q4 = 0, 1, 2
+IL_SRC_F32, IL_SRC_BF16 = 0, 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libil.so")
 
 _lock = threading.Lock()
@@ -36,6 +37,10 @@ def lib() -> ctypes.CDLL:
             L = ctypes.CDLL(LIB_PATH)
             L.il_upload.restype = ctypes.c_void_p
             L.il_upload.argtypes = [ctypes.c_void_p, ctypes.c_int, _i64, _i64]
+            L.il_upload_quantize.restype = ctypes.c_void_p
+            L.il_upload_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, _i64, _i64]
+            L.il_download.restype = _i64
+            L.il_download.argtypes = [ctypes.c_void_p, ctypes.c_void_p, _i64]
             L.il_free.restype = None
             L.il_free.argtypes = [ctypes.c_void_p]
             L.il_matmul.restype = ctypes.c_int
@@ -104,6 +109,44 @@ def il_upload(weight, fmt: int, n_out: int, n_in: int):
     if not h:
         return None
     return Weight(h, int(fmt), int(n_out), int(n_in))
+
+
+def il_upload_quantize(weight, src: int, fmt: int, n_out: int, n_in: int):
+    """Quantise full-precision weights to Q8 / Q4 on the device; None if
+    declined.  `weight` is a numpy array (float32, or bfloat16 bits as
+    uint16) or a contiguous torch tensor (float32 or bfloat16) on the host or
+    on the current device; a device tensor must be ready (synchronized)."""
+    if hasattr(weight, "data_ptr"):
+        import torch
+        want = torch.float32 if src == IL_SRC_F32 else torch.bfloat16
+        if weight.dtype != want or not weight.is_contiguous():
+            raise TypeError(f"src {src} expects a contiguous {want} tensor, got {weight.dtype}")
+        n = weight.numel()
+        ptr = weight.data_ptr()
+    else:
+        weight = np.ascontiguousarray(weight)
+        want = np.float32 if src == IL_SRC_F32 else np.uint16
+        if weight.dtype != want:
+            raise TypeError(f"src {src} expects {np.dtype(want).name} weights, got {weight.dtype}")
+        n = weight.size
+        ptr = weight.ctypes.data
+    if n != n_out * n_in:
+        raise ValueError(f"weight has {n} elements, shape needs {n_out * n_in}")
+    h = lib().il_upload_quantize(ctypes.c_void_p(ptr), int(src), int(fmt), int(n_out), int(n_in))
+    if not h:
+        return None
+    return Weight(h, int(fmt), int(n_out), int(n_in))
+
+
+def il_download(w: Weight) -> np.ndarray:
+    """The handle's weight in its host format, as uint8 bytes."""
+    n = int(lib().il_download(w.handle, None, 0))
+    if n < 0:
+        raise RuntimeError(il_last_error())
+    out = np.empty(n, dtype=np.uint8)
+    if int(lib().il_download(w.handle, ctypes.c_void_p(out.ctypes.data), n)) != n:
+        raise RuntimeError(il_last_error())
+    return out
 
 
 def il_free(w: Weight) -> None:

@@ -99,6 +99,21 @@ def gen_bf16(cfg: int, tensor_id: int, n_out: int, n_in: int) -> np.ndarray:
     return f32_to_bf16_bits(w)
 
 
+def gen_f32_weight(cfg: int, tensor_id: int, n_out: int, n_in: int) -> np.ndarray:
+    """Full-precision weights for the upload quantiser: f32 ~ N(0, 0.02), the
+    bf16 weights' distribution before rounding."""
+    g = rng_for(cfg, tensor_id)
+    return g.standard_normal((n_out, n_in), dtype=np.float32) * np.float32(0.02)
+
+
+# Upload-quantiser workloads (f32 [n_out, n_in] -> Q8 / Q4 on the device):
+# the Q8 gate/up shape and the Q4 verify shape, one weight each.
+QUANTIZE = {
+    "f2_q8": (Q8, 14336, 4096, 6, 1),  # fmt, n_out, n_in, cfg, tensor_id
+    "f2_q4": (Q4, 17408, 5120, 6, 2),
+}
+
+
 def gen_q8_parts(cfg: int, tensor_id: int, n_out: int, n_in: int):
     g = rng_for(cfg, tensor_id)
     codes = g.integers(-127, 128, size=(n_out, n_in), dtype=np.int8)

@@ -22,8 +22,8 @@ def header_symbols():
 
 def test_header_declares_the_abi():
     assert header_symbols() == sorted([
-        "il_upload", "il_free", "il_matmul", "il_wants", "il_name", "il_stats",
-        "il_weight_bytes", "il_last_error"])
+        "il_upload", "il_upload_quantize", "il_download", "il_free", "il_matmul", "il_wants",
+        "il_name", "il_stats", "il_weight_bytes", "il_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -142,3 +142,47 @@ def test_matmul_injected_failure(monkeypatch):
     monkeypatch.setenv("IL_FORCE_FAIL", "upload,matmul")
     assert _matmul_raw(0x1000, 1, 64, [(0x10, 4, 0x2000)]) == 0
     assert "IL_FORCE_FAIL" in il.il_last_error()
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((None, 0, 1, 4, 64), "NULL"),
+    ((b"\0" * 1024, 5, 1, 4, 64), "source type"),
+    ((b"\0" * 1024, 0, 0, 4, 64), "not a quantised format"),
+    ((b"\0" * 1024, 0, 9, 4, 64), "not a quantised format"),
+    ((b"\0" * 1024, 0, 1, 0, 64), "n_out"),
+    ((b"\0" * 1024, 1, 2, 4, 40), "multiple of 32"),
+])
+def test_upload_quantize_rejects_bad_arguments(args, msg):
+    weight, src, fmt, n_out, n_in = args
+    buf = ctypes.create_string_buffer(weight) if weight is not None else None
+    assert not binding.lib().il_upload_quantize(buf, src, fmt, n_out, n_in)
+    assert msg in il.il_last_error()
+
+
+def test_upload_quantize_injected_failure(monkeypatch):
+    monkeypatch.setenv("IL_FORCE_FAIL", "upload")
+    w = np.zeros((4, 64), np.float32)
+    assert il.il_upload_quantize(w, il.IL_SRC_F32, il.IL_Q8, 4, 64) is None
+    assert "IL_FORCE_FAIL" in il.il_last_error()
+
+
+def test_upload_quantize_binding_checks_dtype_and_size():
+    with pytest.raises(TypeError):
+        il.il_upload_quantize(np.zeros((4, 64), np.float64), il.IL_SRC_F32, il.IL_Q8, 4, 64)
+    with pytest.raises(TypeError):
+        il.il_upload_quantize(np.zeros((4, 64), np.float32), il.IL_SRC_BF16, il.IL_Q4, 4, 64)
+    with pytest.raises(ValueError):
+        il.il_upload_quantize(np.zeros((4, 32), np.float32), il.IL_SRC_F32, il.IL_Q8, 4, 64)
+
+
+def test_upload_quantize_without_a_device_declines():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert il.il_upload_quantize(np.zeros((4, 64), np.float32), il.IL_SRC_F32, il.IL_Q4, 4, 64) is None
+    assert il.il_last_error()
+
+
+def test_download_null_handle():
+    assert binding.lib().il_download(None, None, 0) == -1
+    assert "NULL" in il.il_last_error()
