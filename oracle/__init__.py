@@ -14,7 +14,9 @@ sum_k |x*w| in f64; the acceptance test is |y - y_ref| <= 4e-3 * bound per
 output element.  The arithmetic lives in ``il_oracle.c`` (plain C, gcc -O2);
 this module only marshals numpy arrays.
 
-Also here, for the upload-quantiser row: ``quantize`` (f32 weights -> Q8 / Q4
+Also here: ``gelu_mul`` (the fused gate/up feed-forward step, GELU(x G^T) *
+(x U^T), with its propagated error bound; ``gelu`` alone), and, for the
+upload-quantiser row, ``quantize`` (f32 weights -> Q8 / Q4
 host blocks by per-block absmax scaling, rule stated in ``il_oracle.c``) and
 ``f16_bits`` (f32 -> binary16, round to nearest even, from the format
 definition).
@@ -113,6 +115,11 @@ class Oracle:
         lib.orc_f16_bits_array.argtypes = [_ptr, _i64, _ptr]
         lib.orc_quantize.restype = ctypes.c_int
         lib.orc_quantize.argtypes = [_ptr, ctypes.c_int, _i64, _i64, _ptr]
+        lib.orc_gelu.restype = ctypes.c_double
+        lib.orc_gelu.argtypes = [ctypes.c_double]
+        lib.orc_gelu_mul_rows.restype = ctypes.c_int
+        lib.orc_gelu_mul_rows.argtypes = [_ptr, _i64, _i64, _ptr, _ptr, ctypes.c_int, _i64, _i64, _i64,
+                                          _ptr, _ptr, ctypes.c_int]
         lib.orc_check.restype = _i64
         lib.orc_check.argtypes = [_ptr, _ptr, _ptr, _i64, ctypes.c_double,
                                   ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]
@@ -210,6 +217,29 @@ class Oracle:
             raise ValueError("oracle quantize failed")
         return out
 
+    def gelu(self, v) -> np.ndarray:
+        """GELU(v) = v * Phi(v) in double (erf from the C library)."""
+        a = np.asarray(v, dtype=np.float64)
+        f = self.lib.orc_gelu
+        return np.array([f(float(e)) for e in a.ravel()], dtype=np.float64).reshape(a.shape)
+
+    def gelu_mul(self, x: np.ndarray, gate, up, fmt: int, n_out: int, r0: int = 0,
+                 r1: int | None = None, threads: int = 0):
+        """(y_ref [t, r1-r0] f32, bound [t, r1-r0] f64) of GELU(x G^T) * (x U^T);
+        check with the usual 4e-3 * bound rule (the bound carries the
+        propagation of both matmuls' tolerance through GELU)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        t, n_in = x.shape
+        g = self._host_weight(gate, fmt, n_out, n_in)
+        u = self._host_weight(up, fmt, n_out, n_in)
+        r1 = n_out if r1 is None else r1
+        y = np.empty((t, r1 - r0), dtype=np.float32)
+        bound = np.empty((t, r1 - r0), dtype=np.float64)
+        if self.lib.orc_gelu_mul_rows(_p(x), t, n_in, _p(g), _p(u), fmt, n_out, r0, r1, _p(y), _p(bound),
+                                      int(threads)) != 0:
+            raise ValueError("oracle gelu_mul failed")
+        return y, bound
+
     def check(self, y, y_ref, bound, tol: float = TOL) -> dict:
         """Element-wise |y - y_ref| <= tol * bound (NaN/Inf in y fail)."""
         y = np.ascontiguousarray(y, dtype=np.float32)
@@ -260,6 +290,14 @@ def matmul_points(x, weight, fmt, n_out, ii, rr, threads=0):
 
 def check(y, y_ref, bound, tol=TOL):
     return default().check(y, y_ref, bound, tol)
+
+
+def gelu(v):
+    return default().gelu(v)
+
+
+def gelu_mul(x, gate, up, fmt, n_out, r0=0, r1=None, threads=0):
+    return default().gelu_mul(x, gate, up, fmt, n_out, r0, r1, threads)
 
 
 def f16_bits(values):

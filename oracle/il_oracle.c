@@ -347,6 +347,78 @@ int orc_matmul_points(const float *x, int64_t t, int64_t n_in, const void *weigh
     return failed ? -1 : 0;
 }
 
+/* ------------------------------------------------ fused gate/up + GELU
+ * The feed-forward step of the drafter page (oxinfer 0.0.1 src/drafter.rs,
+ * `Drafter::step`): gate and up projections of the same input, then
+ * `gelu_mul(&mut g, &u)`, i.e. g <- GELU(g) * u element-wise.  The page calls
+ * gelu_mul without printing it; the reading taken is the plain GELU,
+ *     GELU(v) = v * Phi(v) = 0.5 * v * (1 + erf(v / sqrt(2))),
+ * Phi the standard normal CDF (erf from the C library, in double).
+ *
+ * For output rows [r0, r1) of the two weights (same format and shape):
+ *   G, U = the f64 sums of (1) for the gate and up rows (as orc_matmul_rows),
+ *   y    = (float)(GELU(G) * U),
+ *   bound such that 4e-3 * bound is the error a product of two matmuls each
+ *   within 4e-3 * sum|x*w| of its exact value may carry:
+ *     |GELU(g) u - GELU(G) U| <= L tau Bg (|U| + tau Bu) + |GELU(G)| tau Bu
+ *   with tau = 4e-3, Bg / Bu the sum |x*w| of each row and L = 1.13 >= the
+ *   largest slope of GELU (Phi(v) + v phi(v) peaks at 1.1289 at v = sqrt 2);
+ *   plus 2^-20 |y| for the rounding of the final product, divided by tau. */
+double orc_gelu(double v) { return 0.5 * v * (1.0 + erf(v / sqrt(2.0))); }
+
+int orc_gelu_mul_rows(const float *x, int64_t t, int64_t n_in, const void *gate, const void *up, int fmt,
+                      int64_t n_out, int64_t r0, int64_t r1, float *y, double *bound, int nthreads)
+{
+    if (t < 0 || n_in <= 0 || r0 < 0 || r1 > n_out || r0 > r1) return -1;
+    if (orc_weight_bytes(fmt, n_out, n_in) < 0) return -1;
+    const double tau = 4e-3, lip = 1.13;
+    int64_t nr = r1 - r0;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+#endif
+    {
+        float *wg = (float *)malloc((size_t)n_in * sizeof(float));
+        float *wu = (float *)malloc((size_t)n_in * sizeof(float));
+        if (!wg || !wu) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+            for (int64_t j = 0; j < nr; ++j) {
+                if (orc_dequant_row(gate, fmt, n_in, r0 + j, wg) || orc_dequant_row(up, fmt, n_in, r0 + j, wu)) {
+                    failed = 1;
+                    continue;
+                }
+                for (int64_t i = 0; i < t; ++i) {
+                    const float *xrow = x + (size_t)i * (size_t)n_in;
+                    double g = 0.0, u = 0.0, bg = 0.0, bu = 0.0;
+                    for (int64_t k = 0; k < n_in; ++k) {
+                        double gk = (double)xrow[k] * (double)wg[k];
+                        double uk = (double)xrow[k] * (double)wu[k];
+                        g += gk;
+                        u += uk;
+                        bg += fabs(gk);
+                        bu += fabs(uk);
+                    }
+                    double gl = orc_gelu(g);
+                    double v = gl * u;
+                    double allow = lip * tau * bg * (fabs(u) + tau * bu) + fabs(gl) * tau * bu +
+                                   ldexp(fabs(v), -20);
+                    y[(size_t)i * (size_t)nr + (size_t)j] = (float)v;
+                    bound[(size_t)i * (size_t)nr + (size_t)j] = allow / tau;
+                }
+            }
+        }
+        free(wg);
+        free(wu);
+    }
+    (void)nthreads;
+    return failed ? -1 : 0;
+}
+
 /* The acceptance test on n outputs: |y - y_ref| <= tol * bound, element by
  * element; a NaN or Inf in y always fails, and bound == 0 demands y == y_ref.
  * Returns the number of failing elements; *first_bad is the first failing

@@ -231,6 +231,83 @@ def pin_roundtrip_q4(O):
     assert np.array_equal(w.astype(np.float64) / s + 8.0, codes.astype(np.float64)), "Q4 round trip"
 
 
+# ---------------------------------------------------- gate/up with GELU
+# The fused feed-forward step GELU(x G^T) * (x U^T) (gelu_mul of the drafter
+# page).  Pinned by scipy's normal CDF (GELU(v) = v Phi(v)), the exact
+# identity GELU(v) - GELU(-v) = v, one-hot weights that select x columns,
+# the composition with a numpy float64 matmul of library-decoded weights,
+# and a Monte Carlo check that the bound covers every g, u within the
+# matmul tolerance of the exact sums.
+def _lib_gelu(v):
+    from scipy.stats import norm
+    v = np.asarray(v, dtype=np.float64)
+    return v * norm.cdf(v)
+
+
+def _lib_values(fmt, parts):
+    """Library-decoded weight values (float64) of generated parts."""
+    if fmt == BF16:
+        return lib_bf16(parts)
+    if fmt == Q8:
+        return lib_q8_values(*parts).astype(np.float64)
+    return lib_q4_values(*parts).astype(np.float64)
+
+
+def pin_gelu_values(O):
+    v = np.concatenate([np.linspace(-12, 12, 2401), [0.0, 1e-300, -1e-300, 1e-8, 37.0, -37.0]])
+    g = O.gelu(v)
+    assert np.all(np.abs(g - _lib_gelu(v)) <= 1e-15 * np.maximum(1, np.abs(v))), "GELU vs v * Phi(v)"
+    assert np.all(np.abs(g - O.gelu(-v) - v) <= 1e-15 * np.maximum(1, np.abs(v))), "GELU(v) - GELU(-v) = v"
+    assert O.gelu(np.array([0.0]))[0] == 0.0 and O.gelu(np.array([10.0]))[0] == 10.0
+    assert abs(O.gelu(np.array([-10.0]))[0]) < 1e-20
+    d = np.diff(g[:2401]) / np.diff(v[:2401])
+    assert 1.12 < d.max() <= 1.13, "largest GELU slope (the bound's constant)"
+
+
+def pin_gelu_mul_onehot(O):
+    n_out, n_in = 6, 64
+    cg = np.array([0, 5, 17, 63, 31, 2])
+    cu = np.array([1, 5, 40, 0, 31, 63])
+    x = (np.random.default_rng(30).standard_normal((3, n_in)) * 2).astype(np.float32)
+    xg, xu = x[:, cg].astype(np.float64), x[:, cu].astype(np.float64)
+    want = (_lib_gelu(xg) * xu).astype(np.float32)
+    for fmt in (BF16, Q8, Q4):
+        y, bound = O.gelu_mul(x, _onehot_weight(fmt, n_out, n_in, cg), _onehot_weight(fmt, n_out, n_in, cu),
+                              fmt, n_out)
+        assert np.all(np.abs(y.astype(np.float64) - want) <= 2.0 ** -23 * np.abs(want)), f"one-hot fmt {fmt}"
+        # the bound holds at least the up term |GELU(G)| Bu and the gate term 1.13 Bg |U|
+        assert np.all(bound >= np.abs(_lib_gelu(xg)) * np.abs(xu) * 0.999), "bound: up term"
+        assert np.all(bound >= 1.13 * np.abs(xg) * np.abs(xu) * 0.999), "bound: gate term"
+    zg = _onehot_weight(Q4, n_out, n_in, cg)
+    zero = wl.encode_q4(np.full((n_out, n_in), 8, np.uint8), np.full((n_out, 2), 0x3C00, np.uint16))
+    for G, U in ((zero, zg), (zg, zero)):
+        y, bound = O.gelu_mul(x, G, U, Q4, n_out)
+        assert np.all(y == 0) and np.all(bound == 0), "an all-zero projection gives exactly 0"
+
+
+def pin_gelu_mul_composition(O):
+    rng = np.random.default_rng(31)
+    t, n_out, n_in = 3, 20, 96
+    x = rng.standard_normal((t, n_in)).astype(np.float32)
+    for fmt in (BF16, Q8, Q4):
+        parts = [_random_parts(fmt, rng, n_out, n_in) for _ in range(2)]
+        (G, U) = [_encode(fmt, p) for p in parts]
+        Wg, Wu = [_lib_values(fmt, p) for p in parts]
+        g64 = x.astype(np.float64) @ Wg.T
+        u64 = x.astype(np.float64) @ Wu.T
+        want = _lib_gelu(g64) * u64
+        y, bound = O.gelu_mul(x, G, U, fmt, n_out)
+        err = np.abs(y.astype(np.float64) - want)
+        assert np.all(err <= 2.0 ** -23 * np.abs(want) + 1e-12 * bound), f"composition fmt {fmt}"
+        # Monte Carlo: any g, u within the matmul tolerance stays within the bound
+        bg = np.abs(x.astype(np.float64)) @ np.abs(Wg).T
+        bu = np.abs(x.astype(np.float64)) @ np.abs(Wu).T
+        for _ in range(200):
+            g = g64 + 4e-3 * bg * rng.uniform(-1, 1, g64.shape)
+            u = u64 + 4e-3 * bu * rng.uniform(-1, 1, u64.shape)
+            assert np.all(np.abs(_lib_gelu(g) * u - y) <= 4e-3 * bound * (1 + 1e-9)), "bound too small"
+
+
 # --------------------------------------------------------------- quantiser
 # The upload quantiser (absmax per 32-element block; the rule is stated in
 # il_oracle.c).  Its pins: numpy's float16 cast on every binary16 value, on
@@ -506,6 +583,7 @@ ALL_PINS = [
     pin_row_sums, pin_zero_codes, pin_roundtrip_q8, pin_roundtrip_q4, pin_bruteforce,
     pin_numpy_matmul, pin_points_equal_rows, pin_thread_invariance, pin_check_rule,
     pin_f16_rounding, pin_quantize_hand, pin_quantize_roundtrip, pin_quantize_nearest,
+    pin_gelu_values, pin_gelu_mul_onehot, pin_gelu_mul_composition,
 ]
 
 

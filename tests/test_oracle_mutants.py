@@ -54,6 +54,13 @@ MUTANTS = {
     "f16_subnormal_round_down": ("double q = nearbyint(a * ldexp(1.0, 24));",
                                  "double q = floor(a * ldexp(1.0, 24));"),
     "f16_overflow": ("if (be >= 31) return sign", "if (be >= 32) return sign"),
+    "gelu_x_row": ("const float *xrow = x + (size_t)i * (size_t)n_in;", "const float *xrow = x;"),
+    "gelu_half": ("return 0.5 * v * (1.0 + erf(v / sqrt(2.0)));", "return v * (1.0 + erf(v / sqrt(2.0)));"),
+    "gelu_erf_argument": ("erf(v / sqrt(2.0))", "erf(v)"),
+    "gelu_mul_operand": ("double v = gl * u;", "double v = gl * g;"),
+    "gelu_up_row": ("orc_dequant_row(up, fmt, n_in, r0 + j, wu)", "orc_dequant_row(gate, fmt, n_in, r0 + j, wu)"),
+    "gelu_bound_up_term": ("+ fabs(gl) * tau * bu +", "+"),
+    "gelu_bound_slope": ("const double tau = 4e-3, lip = 1.13;", "const double tau = 4e-3, lip = 1.0;"),
     "quant_q8_divisor": ("float s = amax / 127.0f;", "float s = amax / 128.0f;"),
     "quant_q8_truncate": ("q = rintf(src[e] / s);\n                        if (q > 127.0f)",
                           "q = truncf(src[e] / s);\n                        if (q > 127.0f)"),
