@@ -52,6 +52,9 @@ DESCRIPTIONS = {
     "c4_t32": "Q4 verify, t=32, 2 jobs [17408, 5120]",
     "c5a": "bf16 prefill, t=2048, 2 jobs [4096|14336] x 4096",
     "c5b": "Q4 prefill, t=512, 1 job [14336, 4096]",
+    "f3_q8_t1": "fused gate/up + GELU, Q8, t=1, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T)",
+    "f3_q4_t1": "fused gate/up + GELU, Q4, t=1, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T)",
+    "f3_bf16_t1": "fused gate/up + GELU, bf16, t=1, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T)",
 }
 
 
@@ -124,6 +127,89 @@ def stats_device_ms(il, path: str) -> float:
         if line.startswith(path + ":"):
             return float(line.split("device_ms=")[1].split()[0])
     raise RuntimeError(f"no {path} line in il_stats")
+
+
+def bench_gelu_mul(args, name: str) -> int:
+    """The fused gate/up step: one il_matmul_gelu_mul per step over weight
+    pairs rotated past the MALL, timed like the matmul workloads (HIP graph,
+    events on the launch stream).  The unfused il_matmul of the same pair
+    (writing g and u, no GELU) is timed the same way as context."""
+    import torch
+
+    import quantized_weight_matmul_amd as il
+    fmt, n_out, n_in, t, cfg = wl.GELU_MUL[name]
+    log(f"[bench] workload {name}: {DESCRIPTIONS[name]}")
+    x_np, G, U = wl.make_gelu_mul_inputs(name)
+    per_set = 2 * wl.weight_bytes(fmt, n_out, n_in)
+    flops = 4 * t * n_out * n_in
+    n_sets = max(1, -(-ROTATE_BYTES // per_set))
+    log(f"[bench] uploading {n_sets} gate/up pairs x {per_set / 1e6:.1f} MB")
+    sets = []
+    for _ in range(n_sets):
+        pair = (il.il_upload(G, fmt, n_out, n_in), il.il_upload(U, fmt, n_out, n_in))
+        if None in pair:
+            raise RuntimeError(il.il_last_error())
+        sets.append(pair)
+    x = torch.from_numpy(x_np).cuda()
+    y = torch.empty((t, n_out), dtype=torch.float32, device="cuda")
+    g = torch.empty((t, n_out), dtype=torch.float32, device="cuda")
+    u = torch.empty((t, n_out), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()  # default priority
+
+    def fused(i, s):
+        hg, hu = sets[i % n_sets]
+        if il.il_matmul_gelu_mul(x, t, n_in, hg, hu, n_out, y, s) != 1:
+            raise RuntimeError(il.il_last_error())
+
+    def unfused(i, s):
+        hg, hu = sets[i % n_sets]
+        if il.il_matmul(x, t, n_in, [(hg, n_out, g), (hu, n_out, u)], s) != 1:
+            raise RuntimeError(il.il_last_error())
+
+    ms_per_step, kern_ms, pair_ms = time_steps(fused, args, stream, 1)
+    ms_unfused, kern_unfused, _ = time_steps(unfused, args, stream, 1)
+    hbm = t <= STREAMING_MAX_T
+    if hbm:
+        value, unit = per_set / (ms_per_step * 1e-3) / 1e9, "GB/s"
+        achieved, peak = per_set / (kern_ms * 1e-3) / 1e9, HBM_PEAK_GBS
+    else:
+        value, unit = flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+        achieved, peak = flops / (kern_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS
+    roofline = {"bound": "hbm" if hbm else "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(name),
+                "kernel_ms": round(kern_ms, 6),
+                "timing": "HIP events on the launch stream around the timed region / launches",
+                "event_pair_ms_median": round(pair_ms, 6)}
+    log(f"[bench] fused {ms_per_step * 1e3:.2f} us/step ({value:.1f} {unit}), kernel {kern_ms * 1e3:.2f} us; "
+        f"unfused il_matmul {kern_unfused * 1e3:.2f} us")
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.gelu_mul(x_np, G, U, fmt, n_out, threads=threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or el / reps * (reps + 1) > args.cpu_seconds * 2:
+                break
+        per = el / reps
+        cpu = {"value": round((per_set / per / 1e9) if hbm else (flops / per / 1e12), 4), "unit": unit,
+               "cores": threads, "kind": "oracle", "sample": f"{reps} full oracle gate/up + GELU passes",
+               "seconds": round(el, 2)}
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if t <= 8 else "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: {DESCRIPTIONS[name]}", "t": t, "n_in": n_in,
+                   "jobs": [[wl.FMT_NAMES[fmt], n_out], [wl.FMT_NAMES[fmt], n_out]],
+                   "weight_bytes_per_step": per_set, "flops_per_step": flops, "weight_sets_rotated": n_sets,
+                   "timing": "eager" if args.no_graph else "hip-graph",
+                   "unfused_il_matmul_kernel_ms": round(kern_unfused, 6)},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def bench_quantize(args, name: str) -> int:
@@ -208,7 +294,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="c2", choices=sorted(wl.SUBMISSIONS) + sorted(wl.QUANTIZE))
+    ap.add_argument("--workload", default="c2",
+                    choices=sorted(wl.SUBMISSIONS) + sorted(wl.QUANTIZE) + sorted(wl.GELU_MUL))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -241,6 +328,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.workload in wl.QUANTIZE:
         return bench_quantize(args, args.workload)
+    if args.workload in wl.GELU_MUL:
+        return bench_gelu_mul(args, args.workload)
     sub = wl.SUBMISSIONS[args.workload]
     decode = sub.t <= 8
     streaming = sub.t <= STREAMING_MAX_T
@@ -266,7 +355,16 @@ def main() -> int:
         if rc != 1:
             raise RuntimeError(il.il_last_error())
 
-    # ---- warm-up, then an event pair around each of a few eager launches ----
+    ms_per_step, kern_ms, pair_ms = time_steps(step, args, stream, len({j.fmt for j in sub.jobs}))
+    launches_per_step = len({j.fmt for j in sub.jobs})
+    return report(args, sub, per_set, n_sets, ms_per_step, kern_ms, pair_ms, x_np, weights)
+
+
+def time_steps(step, args, stream, launches_per_step):
+    """Warm-up, event pairs around a few eager launches, then K steps in one
+    HIP graph (or eager) with HIP events on the launch stream around them.
+    Returns (wall ms per step, kernel ms per launch, median event pair ms)."""
+    import torch
     n_ev = min(args.steps, 100)
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
@@ -312,9 +410,14 @@ def main() -> int:
         torch.cuda.synchronize()
         total_s = time.perf_counter() - t0
     ms_per_step = total_s * 1e3 / args.steps
-    launches_per_step = len({j.fmt for j in sub.jobs})
     kern_ms = e0.elapsed_time(e1) / (args.steps * launches_per_step)
+    return ms_per_step, kern_ms, pair_ms
 
+
+def report(args, sub, per_set, n_sets, ms_per_step, kern_ms, pair_ms, x_np, weights) -> int:
+    decode = sub.t <= 8
+    streaming = sub.t <= STREAMING_MAX_T
+    launches_per_step = len({j.fmt for j in sub.jobs})
     if streaming:
         value = per_set / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"

@@ -149,6 +149,25 @@ IL_API void il_free(il_weight *w);
 IL_API int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64_t n_jobs,
               void *hip_stream);
 
+/* Fused feed-forward gate/up step -- in one submission,
+ *     y[t][n_out] = GELU(x * G^T) (.) (x * U^T)        (element-wise product)
+ * the `matmul_multi` over the gate and up projections followed by
+ * `gelu_mul(&mut g, &u)` in `Drafter::step` on the oxinfer 0.0.1
+ * src/drafter.rs page, without writing g or u to memory.  The page does not
+ * print gelu_mul; GELU here is the plain definition
+ *     GELU(v) = v * Phi(v) = 0.5 * v * (1 + erf(v / sqrt(2))).
+ *   x        : DEVICE float[t][n_in], 16-byte aligned (as for il_matmul).
+ *   gate, up : handles of the same format with shape [n_out, n_in].
+ *   y        : DEVICE float[t][n_out] row-major, written in full; must not
+ *              overlap x.
+ *   hip_stream : as for il_matmul.
+ * Accuracy: g and u are formed by the same kernels as il_matmul, so y is
+ * within the propagation of their tolerance through GELU (slope <= 1.13).
+ * Validation, stream semantics and the 1 / 0 return follow il_matmul;
+ * t == 0 is a no-op. */
+IL_API int il_matmul_gelu_mul(const float *x, int64_t t, int64_t n_in, const il_weight *gate,
+                              const il_weight *up, int64_t n_out, float *y, void *hip_stream);
+
 /* Backend::wants -- whether a matmul of these dimensions is worth running on
  * the GPU (the page: dispatch has a fixed cost, so small ops stay on the
  * CPU).  A pure function of the sizes: 1 if 2 * n_out * n_in * t is at least

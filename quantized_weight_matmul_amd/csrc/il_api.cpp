@@ -559,6 +559,86 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
     return 1;
 }
 
+int il_matmul_gelu_mul(const float *x, int64_t t, int64_t n_in, const il_weight *gate, const il_weight *up,
+                       int64_t n_out, float *y, void *hip_stream) {
+    g_err.clear();
+    if (t < 0) {
+        set_err("il_matmul_gelu_mul: negative t (%" PRId64 ")", t);
+        return 0;
+    }
+    if (t == 0) return 1;
+    if (!x || !y || !gate || !up) {
+        set_err("il_matmul_gelu_mul: x, y, gate or up is NULL");
+        return 0;
+    }
+    if (t > INT_MAX || n_in < il::kBlock || n_in % il::kBlock || n_in > INT_MAX) {
+        set_err("il_matmul_gelu_mul: bad sizes t = %" PRId64 ", n_in = %" PRId64, t, n_in);
+        return 0;
+    }
+    if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 4) {
+        set_err("il_matmul_gelu_mul: x must be 16-byte and y 4-byte aligned");
+        return 0;
+    }
+    if (gate->fmt != up->fmt || gate->n_in != n_in || up->n_in != n_in || gate->n_out != n_out ||
+        up->n_out != n_out) {
+        set_err("il_matmul_gelu_mul: gate and up must share the format and the shape [n_out = %" PRId64
+                ", n_in = %" PRId64 "]",
+                n_out, n_in);
+        return 0;
+    }
+    if (env_flag("IL_FORCE_FAIL", "matmul")) {
+        set_err("il_matmul_gelu_mul: failure injected by IL_FORCE_FAIL");
+        return 0;
+    }
+    int dev = -1;
+    DeviceCtx *ctx = context(&dev);
+    if (!ctx) return 0;
+    if (gate->device != dev || up->device != dev) {
+        set_err("il_matmul_gelu_mul: the weights live on another device than the current %d", dev);
+        return 0;
+    }
+    const int64_t x_bytes = t * n_in * (int64_t)sizeof(float);
+    const int64_t y_bytes = t * n_out * (int64_t)sizeof(float);
+    if (!device_range_ok(x, x_bytes, "x") || !device_range_ok(y, y_bytes, "y")) return 0;
+    if (overlaps(y, y_bytes, x, x_bytes)) {
+        set_err("il_matmul_gelu_mul: y overlaps x");
+        return 0;
+    }
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const bool decode = t <= il::kGemvMaxT;
+    PathStats &st = g_stats[decode ? 0 : 1];
+    const bool timing = timing_on();
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if (timing) {
+        (void)hipEventCreate(&ev0);
+        (void)hipEventCreate(&ev1);
+        (void)hipEventRecord(ev0, s);
+    }
+    const il::KJob jobs[2] = {il::KJob{gate->codes, gate->scales, gate->scales_t, y, (int)n_out},
+                              il::KJob{up->codes, up->scales, up->scales_t, y, (int)n_out}};
+    hipError_t e = decode ? il::launch_gemv(gate->fmt, x, (int)t, (int)n_in, jobs, 2, ctx->cu_count, s, true)
+                          : il::launch_gemm(gate->fmt, x, (int)t, (int)n_in, jobs, 2, ctx->cu_count, s, true);
+    if (timing) {
+        (void)hipEventRecord(ev1, s);
+        (void)hipEventSynchronize(ev1);
+        float ms = 0.f;
+        if (e == hipSuccess && hipEventElapsedTime(&ms, ev0, ev1) == hipSuccess) st.timed_ns += (uint64_t)(ms * 1e6);
+        (void)hipEventDestroy(ev0);
+        (void)hipEventDestroy(ev1);
+    }
+    if (e != hipSuccess) {
+        set_err("il_matmul_gelu_mul: kernel launch failed: %s", hipGetErrorString(e));
+        g_failed++;
+        return 0;
+    }
+    st.calls++;
+    st.launches++;
+    st.jobs += 2;
+    st.bytes += (uint64_t)(gate->host_bytes + up->host_bytes);
+    st.flops += 4ull * (uint64_t)t * (uint64_t)n_out * (uint64_t)n_in;
+    return 1;
+}
+
 int il_wants(int64_t n_out, int64_t n_in, int64_t t) {
     if (n_out <= 0 || n_in <= 0 || t <= 0) return 0;
     double min_flop = 262144.0;  // 2^18

@@ -89,13 +89,21 @@ __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float *__restrict_
     xb[i] = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
 }
 
-template <int FMT, int BM, int BN, int WM, int WN>
+// GLU: jobs 0 and 1 are the gate and up projections.  A tile covers BN / 2
+// output columns; B-tile rows come in groups of 32 alternating between the
+// two weights (virtual row v holds row (v / 64) * 32 + v % 32 of the gate if
+// (v / 32) is even, of the up projection if odd), so every wave's two 32-column
+// MFMA tiles are the gate and up sums of the same outputs and the epilogue
+// writes GELU(gate) * up from registers.
+template <int FMT, int BM, int BN, int WM, int WN, bool GLU = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     constexpr int kThreads = 64 * WM * WN;
     constexpr int kChunksA = BM * BK / 8 / kThreads;  // 16-byte chunks per thread, A tile
     constexpr int kChunksB = BN * BK / 8 / kThreads;  // same, bf16 B tile
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
     constexpr bool kQuarter = BM < kBig;
+    constexpr int kCols = GLU ? BN / 2 : BN;  // output columns of a tile
+    static_assert(!GLU || TN == 2, "GLU pairs the two 32-column tiles of a wave");
     static_assert(kThreads == 2 * BN, "Q8/Q4 staging: two threads per B row");
     static_assert(kChunksA >= 1 && kChunksB >= 1 && (kThreads / 8) % 16 == 0, "staging shape");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][(BM > BN ? BM : BN) * BK];  // [stage][A|B]
@@ -109,12 +117,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     const int tn_all = tile / p.tiles_m;
     const int tm = tile - tn_all * p.tiles_m;
     int j = 0;
+    if constexpr (!GLU) {
 #pragma unroll
-    for (int jj = 1; jj < kMaxJobs; ++jj)
-        if (jj < p.n_jobs && tn_all >= p.tn0[jj]) j = jj;
+        for (int jj = 1; jj < kMaxJobs; ++jj)
+            if (jj < p.n_jobs && tn_all >= p.tn0[jj]) j = jj;
+    }
     const KJob jb = p.job[j];
     const int m0 = tm * kBig + (q >> 1) * BM;
-    const int n0 = (tn_all - p.tn0[j]) * kBig + (q & 1) * BN;
+    const int n0 = (tn_all - p.tn0[j]) * (GLU ? kBig / 2 : kBig) + (q & 1) * kCols;
     if (m0 >= p.t || n0 >= jb.n_out) return;  // a quarter past the edge of x or W
     const int n_in = p.n_in;
     const int nb = n_in / kBlock;
@@ -126,24 +136,30 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
 
     // ---- operand descriptors: exactly the tile's valid rows ----
     const int a_rows = min(BM, p.t - m0);
-    const int b_rows = min(BN, jb.n_out - n0);
+    const int b_rows = min(kCols, jb.n_out - n0);
     const uint32_t row2 = (uint32_t)n_in * 2u;
     const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.xb + (int64_t)m0 * n_in, (uint32_t)a_rows * row2);
-    __amdgpu_buffer_rsrc_t brs, bss;
-    if constexpr (FMT == FMT_BF16) {
-        brs = make_rsrc(static_cast<const uint16_t *>(jb.codes) + (int64_t)n0 * n_in, (uint32_t)b_rows * row2);
-        bss = brs;
-    } else if constexpr (FMT == FMT_Q8) {
-        brs = make_rsrc(static_cast<const int8_t *>(jb.codes) + (int64_t)n0 * n_in,
-                        (uint32_t)b_rows * (uint32_t)n_in);
-        bss = make_rsrc(static_cast<const float *>(jb.scales) + (int64_t)n0 * nb,
-                        (uint32_t)b_rows * (uint32_t)nb * 4u);
-    } else {
-        brs = make_rsrc(static_cast<const uint8_t *>(jb.codes) + (int64_t)n0 * (n_in / 2),
-                        (uint32_t)b_rows * (uint32_t)(n_in / 2));
-        bss = make_rsrc(static_cast<const uint16_t *>(jb.scales) + (int64_t)n0 * nb,
-                        (uint32_t)b_rows * (uint32_t)nb * 2u);
-    }
+    // B descriptors over the tile's weight rows [n0, n0 + b_rows) of job k
+    auto b_rsrc = [&](const KJob &k, __amdgpu_buffer_rsrc_t &c, __amdgpu_buffer_rsrc_t &sc) {
+        if constexpr (FMT == FMT_BF16) {
+            c = make_rsrc(static_cast<const uint16_t *>(k.codes) + (int64_t)n0 * n_in, (uint32_t)b_rows * row2);
+            sc = c;
+        } else if constexpr (FMT == FMT_Q8) {
+            c = make_rsrc(static_cast<const int8_t *>(k.codes) + (int64_t)n0 * n_in,
+                          (uint32_t)b_rows * (uint32_t)n_in);
+            sc = make_rsrc(static_cast<const float *>(k.scales) + (int64_t)n0 * nb,
+                           (uint32_t)b_rows * (uint32_t)nb * 4u);
+        } else {
+            c = make_rsrc(static_cast<const uint8_t *>(k.codes) + (int64_t)n0 * (n_in / 2),
+                          (uint32_t)b_rows * (uint32_t)(n_in / 2));
+            sc = make_rsrc(static_cast<const uint16_t *>(k.scales) + (int64_t)n0 * nb,
+                           (uint32_t)b_rows * (uint32_t)nb * 2u);
+        }
+    };
+    __amdgpu_buffer_rsrc_t brs, bss, brs2, bss2;
+    b_rsrc(jb, brs, bss);
+    if constexpr (GLU) b_rsrc(p.job[1], brs2, bss2);
+    else brs2 = brs, bss2 = bss;
 
     // bf16 staging: chunk i of this thread is row crow0 + (threads / 8) i,
     // 16-byte chunk cc, so 8 consecutive threads read one 128-byte row
@@ -166,22 +182,35 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
             sa[i] = bload16(ars, kok ? (uint32_t)(crow0 + (kThreads / 8) * i) * row2 + (uint32_t)k * 2u : kOut);
         if constexpr (FMT == FMT_BF16) {
 #pragma unroll
-            for (int i = 0; i < kChunksB; ++i)
-                sb[i] = bload16(brs, kok ? (uint32_t)(crow0 + (kThreads / 8) * i) * row2 + (uint32_t)k * 2u : kOut);
+            for (int i = 0; i < kChunksB; ++i) {
+                const int v = crow0 + (kThreads / 8) * i;  // B-tile row
+                if constexpr (GLU) {
+                    // gate or up: (v / 32) % 2, the same for the whole wave
+                    const bool up = ((wave >> 2) + ((kThreads / 8) * i >> 5)) & 1;
+                    const int wr = (v >> 6) * 32 + (v & 31);
+                    sb[i] = bload16(up ? brs2 : brs, kok ? (uint32_t)wr * row2 + (uint32_t)k * 2u : kOut);
+                } else {
+                    sb[i] = bload16(brs, kok ? (uint32_t)v * row2 + (uint32_t)k * 2u : kOut);
+                }
+            }
         }
         if constexpr (FMT != FMT_BF16) {
             const int kh = k0 + 32 * qh;
             const bool ok = kh < n_in;
+            // GLU: B-tile row qr is row wr of the gate (wave even) or up (odd)
+            const bool up = GLU && (wave & 1);
+            const int wr = GLU ? (qr >> 6) * 32 + (qr & 31) : qr;
+            const __amdgpu_buffer_rsrc_t crs = up ? brs2 : brs, srs = up ? bss2 : bss;
             if constexpr (FMT == FMT_Q8) {
-                const uint32_t off = ok ? (uint32_t)qr * (uint32_t)n_in + (uint32_t)kh : kOut;
-                sb[0] = bload16(brs, off);
-                sb[1] = bload16(brs, ok ? off + 16u : kOut);
+                const uint32_t off = ok ? (uint32_t)wr * (uint32_t)n_in + (uint32_t)kh : kOut;
+                sb[0] = bload16(crs, off);
+                sb[1] = bload16(crs, ok ? off + 16u : kOut);
                 ssc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                    bss, ok ? ((uint32_t)qr * nb + kh / kBlock) * 4u : kOut, 0, 0));
+                                                    srs, ok ? ((uint32_t)wr * nb + kh / kBlock) * 4u : kOut, 0, 0));
             } else {
-                sb[0] = bload16(brs, ok ? (uint32_t)qr * (uint32_t)(n_in / 2) + (uint32_t)(kh / 2) : kOut);
+                sb[0] = bload16(crs, ok ? (uint32_t)wr * (uint32_t)(n_in / 2) + (uint32_t)(kh / 2) : kOut);
                 const uint16_t bits = __builtin_amdgcn_raw_buffer_load_b16(
-                    bss, ok ? ((uint32_t)qr * nb + kh / kBlock) * 2u : kOut, 0, 0);
+                    srs, ok ? ((uint32_t)wr * nb + kh / kBlock) * 2u : kOut, 0, 0);
                 ssc = (float)__builtin_bit_cast(_Float16, bits) * 0.0625f;  // values carry *16
             }
         }
@@ -269,50 +298,64 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
 
     // ---- epilogue: 32x32 tile, lane holds rows 8 (i / 4) + 4 (lane / 32) + i % 4
     //      of column lane % 32 ----
+    if constexpr (GLU) {
 #pragma unroll
-    for (int a = 0; a < TM; ++a) {
-#pragma unroll
-        for (int n = 0; n < TN; ++n) {
-            const int col = n0 + wn * (BN / WN) + n * 32 + (lane & 31);
+        for (int a = 0; a < TM; ++a) {
+            const int col = n0 + wn * (BN / WN) / 2 + (lane & 31);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int row = m0 + wm * (BM / WM) + a * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-                if (row < p.t && col < jb.n_out) jb.y[(int64_t)row * jb.n_out + col] = acc[a][n][i];
+                if (row < p.t && col < jb.n_out)
+                    jb.y[(int64_t)row * jb.n_out + col] = gelu(acc[a][0][i]) * acc[a][1][i];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+#pragma unroll
+            for (int n = 0; n < TN; ++n) {
+                const int col = n0 + wn * (BN / WN) + n * 32 + (lane & 31);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int row = m0 + wm * (BM / WM) + a * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+                    if (row < p.t && col < jb.n_out) jb.y[(int64_t)row * jb.n_out + col] = acc[a][n][i];
+                }
             }
         }
     }
 }
 
-template <int FMT>
+template <int FMT, bool GLU>
 hipError_t launch_units(GemmParams p, bool quarter, int tile_lo, int n_units, hipStream_t s) {
     p.tile_lo = tile_lo;
     p.n_units = n_units;
     p.units_per_xcd = (n_units + kXcds - 1) / kXcds;
     const dim3 grid(kXcds * p.units_per_xcd);
     if (quarter)
-        hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 2>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 2, GLU>), grid, dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((gemm_kernel<FMT, kBig, kBig, 2, 4>), grid, dim3(512), 0, s, p);
+        hipLaunchKernelGGL((gemm_kernel<FMT, kBig, kBig, 2, 4, GLU>), grid, dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, bool GLU = false>
 hipError_t launch_plan(const GemmParams &p, int tiles, int cu_count, hipStream_t s) {
     // Whole rounds of big tiles (one per compute unit at a time); what is
     // left over, less than one round, runs as quarter tiles so that the last
     // round is short instead of mostly idle.
     const int full = tiles >= cu_count ? tiles / cu_count * cu_count : 0;
     hipError_t e = hipSuccess;
-    if (full > 0) e = launch_units<FMT>(p, false, 0, full, s);
-    if (e == hipSuccess && tiles > full) e = launch_units<FMT>(p, true, full, 4 * (tiles - full), s);
+    if (full > 0) e = launch_units<FMT, GLU>(p, false, 0, full, s);
+    if (e == hipSuccess && tiles > full) e = launch_units<FMT, GLU>(p, true, full, 4 * (tiles - full), s);
     return e;
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
-                       int cu_count, hipStream_t s) {
+                       int cu_count, hipStream_t s, bool glu) {
     if (t < 1 || n_jobs < 1 || n_jobs > kMaxJobs || n_in % kBlock || cu_count < 1) return hipErrorInvalidValue;
+    if (glu && (n_jobs != 2 || jobs[0].n_out != jobs[1].n_out)) return hipErrorInvalidValue;
     // every buffer descriptor (kBig rows of x or of a weight) must stay below 2^31 bytes
     if ((int64_t)kBig * n_in * 2 >= (1ll << 31)) return hipErrorInvalidValue;
     GemmParams p{};
@@ -324,9 +367,11 @@ hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *job
     for (int j = 0; j < n_jobs; ++j) {
         p.job[j] = jobs[j];
         p.tn0[j] = tn;
-        tn += (jobs[j].n_out + kBig - 1) / kBig;
+        // GLU: tiles of kBig / 2 output columns over the gate's rows only
+        if (!glu) tn += (jobs[j].n_out + kBig - 1) / kBig;
+        else if (j == 0) tn += (jobs[j].n_out + kBig / 2 - 1) / (kBig / 2);
     }
-    for (int j = n_jobs; j <= kMaxJobs; ++j) p.tn0[j] = tn;
+    for (int j = glu ? 1 : n_jobs; j <= kMaxJobs; ++j) p.tn0[j] = tn;
     const int tiles = p.tiles_m * tn;
 
     // mid-size t: the matrix-core decode kernel's wide mode, which rounds x
@@ -338,7 +383,8 @@ hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *job
         if (!strcmp(force, "verify")) verify = true;
     }
     verify = verify && verify_mfma_fits(fmt, t, n_in, jobs, n_jobs);
-    if (verify && t <= kWideF32MaxT) return launch_verify_mfma(fmt, x, nullptr, t, n_in, jobs, n_jobs, cu_count, s);
+    if (verify && t <= kWideF32MaxT)
+        return launch_verify_mfma(fmt, x, nullptr, t, n_in, jobs, n_jobs, cu_count, s, glu);
 
     // x -> bf16 into stream-ordered scratch, freed after the GEMM on the same stream
     const int64_t n8 = (int64_t)t * n_in / 8;
@@ -350,11 +396,14 @@ hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *job
     e = hipGetLastError();
     if (e == hipSuccess) {
         p.xb = static_cast<const uint16_t *>(xb);
-        if (verify) e = launch_verify_mfma(fmt, x, p.xb, t, n_in, jobs, n_jobs, cu_count, s);
+        if (verify) e = launch_verify_mfma(fmt, x, p.xb, t, n_in, jobs, n_jobs, cu_count, s, glu);
         else switch (fmt) {
-            case FMT_BF16: e = launch_plan<FMT_BF16>(p, tiles, cu_count, s); break;
-            case FMT_Q8: e = launch_plan<FMT_Q8>(p, tiles, cu_count, s); break;
-            case FMT_Q4: e = launch_plan<FMT_Q4>(p, tiles, cu_count, s); break;
+            case FMT_BF16: e = glu ? launch_plan<FMT_BF16, true>(p, tiles, cu_count, s)
+                                   : launch_plan<FMT_BF16>(p, tiles, cu_count, s); break;
+            case FMT_Q8: e = glu ? launch_plan<FMT_Q8, true>(p, tiles, cu_count, s)
+                                 : launch_plan<FMT_Q8>(p, tiles, cu_count, s); break;
+            case FMT_Q4: e = glu ? launch_plan<FMT_Q4, true>(p, tiles, cu_count, s)
+                                 : launch_plan<FMT_Q4>(p, tiles, cu_count, s); break;
             default: e = hipErrorInvalidValue;
         }
     }

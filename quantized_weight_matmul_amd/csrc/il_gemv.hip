@@ -325,8 +325,13 @@ __host__ __device__ constexpr int stream_steps(int n_in) {
     return (n_in + STEP * P - 1) / (STEP * P) * P;
 }
 
-template <int FMT, int T, int R, int P>
+// GLU: the R rows of a wave are R / 2 output rows of the gate projection
+// (jobs[0]) followed by the same R / 2 rows of the up projection (jobs[1]);
+// the epilogue writes GELU(gate) * up to jobs[0].y.
+template <int FMT, int T, int R, int P, bool GLU>
 __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvParams p) {
+    constexpr int RO = GLU ? R / 2 : R;  // output rows per wave
+    static_assert(!GLU || R % 2 == 0, "gate/up pairs");
     constexpr int E = FmtTraits<FMT>::E;
     constexpr int STEP = 64 * E;
     constexpr int G = E / 4;
@@ -368,15 +373,17 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvParams 
     float *yrow[R];
     int ystride[R];
     bool valid[R];
-    const int row_base = ((int)blockIdx.x * kStreamWaves + wave) * R;
+    const int row_base = ((int)blockIdx.x * kStreamWaves + wave) * RO;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int g = row_base + r;
+        const int g = row_base + (GLU ? r % RO : r);
         valid[r] = g < p.total_rows;
-        int j = 0;
+        int j = GLU ? r / RO : 0;
+        if constexpr (!GLU) {
 #pragma unroll
-        for (int q = 1; q < kMaxJobs; ++q)
-            if (q < p.n_jobs && g >= p.row0[q]) j = q;
+            for (int q = 1; q < kMaxJobs; ++q)
+                if (q < p.n_jobs && g >= p.row0[q]) j = q;
+        }
         const int local = valid[r] ? g - p.row0[j] : 0;
         const uint32_t rb = valid[r] ? (uint32_t)row_bytes<FMT>(n_in) : 0u;
         crs[r] = make_rsrc(static_cast<const uint8_t *>(p.job[j].codes) + (int64_t)local * row_bytes<FMT>(n_in), rb);
@@ -455,12 +462,24 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvParams 
     }
 
     // ---- 5. wave reductions; lane 0 stores ----
+    if constexpr (GLU) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < RO; ++r) {
 #pragma unroll
-        for (int i = 0; i < T; ++i) {
-            const float v = wave_sum_dpp(acc[r][i]);
-            if (lane == 0 && valid[r]) yrow[r][(int64_t)i * ystride[r]] = v;
+            for (int i = 0; i < T; ++i) {
+                const float vg = wave_sum_dpp(acc[r][i]);
+                const float vu = wave_sum_dpp(acc[RO + r][i]);
+                if (lane == 0 && valid[r]) yrow[r][(int64_t)i * ystride[r]] = gelu(vg) * vu;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int i = 0; i < T; ++i) {
+                const float v = wave_sum_dpp(acc[r][i]);
+                if (lane == 0 && valid[r]) yrow[r][(int64_t)i * ystride[r]] = v;
+            }
         }
     }
 }
@@ -471,10 +490,10 @@ size_t stream_lds_bytes(int t, int n_in) {
     return (size_t)t * stream_steps<FMT, P>(n_in) * STEP * sizeof(float);
 }
 
-template <int FMT, int T, int R, int P>
+template <int FMT, int T, int R, int P, bool GLU>
 hipError_t launch_stream(const GemvParams &p, hipStream_t s) {
     const size_t lds = stream_lds_bytes<FMT, P>(T, p.n_in);
-    auto kern = gemv_stream_kernel<FMT, T, R, P>;
+    auto kern = gemv_stream_kernel<FMT, T, R, P, GLU>;
     if (lds > 64 * 1024) {
         static bool raised = false;  // benign race: the attribute is idempotent
         if (!raised) {
@@ -484,7 +503,7 @@ hipError_t launch_stream(const GemvParams &p, hipStream_t s) {
             raised = true;
         }
     }
-    const int rows_per_block = kStreamWaves * R;
+    const int rows_per_block = kStreamWaves * (GLU ? R / 2 : R);
     const int grid = (p.total_rows + rows_per_block - 1) / rows_per_block;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kStreamThreads), lds, s, p);
     return hipGetLastError();
@@ -493,7 +512,7 @@ hipError_t launch_stream(const GemvParams &p, hipStream_t s) {
 // Ring depth for a row of `steps` 16-byte lane loads.
 inline int stream_ring(int steps) { return steps >= 5 ? 8 : steps >= 3 ? 4 : 2; }
 
-template <int FMT, int T>
+template <int FMT, int T, bool GLU = false>
 hipError_t try_stream(const GemvParams &p, hipStream_t s, bool *taken) {
     constexpr int STEP = 64 * FmtTraits<FMT>::E;
     const int steps = (p.n_in + STEP - 1) / STEP;
@@ -501,15 +520,34 @@ hipError_t try_stream(const GemvParams &p, hipStream_t s, bool *taken) {
     // bytes of every buffer descriptor (x and one row) stay far below 2^31
     *taken = (int64_t)T * p.n_in * 4 < (1ll << 31);
     // rows per wave: enough weight bytes per workgroup next to its copy of x
-    constexpr int R = (FMT == FMT_Q4) ? 4 : (FMT == FMT_Q8) ? 2 : 1;
+    // (with GLU at least one gate/up pair)
+    constexpr int R0 = (FMT == FMT_Q4) ? 4 : (FMT == FMT_Q8) ? 2 : 1;
+    constexpr int R = GLU && R0 < 2 ? 2 : R0;
     if (P == 8 && *taken && stream_lds_bytes<FMT, 8>(T, p.n_in) <= kStreamMaxLds)
-        return launch_stream<FMT, T, R, 8>(p, s);
+        return launch_stream<FMT, T, R, 8, GLU>(p, s);
     if (P == 4 && *taken && stream_lds_bytes<FMT, 4>(T, p.n_in) <= kStreamMaxLds)
-        return launch_stream<FMT, T, R, 4>(p, s);
+        return launch_stream<FMT, T, R, 4, GLU>(p, s);
     if (P == 2 && *taken && stream_lds_bytes<FMT, 2>(T, p.n_in) <= kStreamMaxLds)
-        return launch_stream<FMT, T, R, 2>(p, s);
+        return launch_stream<FMT, T, R, 2, GLU>(p, s);
     *taken = false;
     return hipSuccess;
+}
+
+// The gate/up step on the streaming kernel; *taken is false when x does not
+// fit in LDS (the caller then uses the matrix-core kernel).
+template <int FMT>
+hipError_t try_stream_glu(const GemvParams &p, hipStream_t s, bool *taken) {
+    switch (p.t) {
+        case 1: return try_stream<FMT, 1, true>(p, s, taken);
+        case 2: return try_stream<FMT, 2, true>(p, s, taken);
+        case 3: return try_stream<FMT, 3, true>(p, s, taken);
+        case 4: return try_stream<FMT, 4, true>(p, s, taken);
+        case 5: return try_stream<FMT, 5, true>(p, s, taken);
+        case 6: return try_stream<FMT, 6, true>(p, s, taken);
+        case 7: return try_stream<FMT, 7, true>(p, s, taken);
+        case 8: return try_stream<FMT, 8, true>(p, s, taken);
+        default: *taken = false; return hipErrorInvalidValue;
+    }
 }
 
 template <int FMT, int T>
@@ -576,8 +614,9 @@ hipError_t launch_fmt(GemvParams &p, int cu_count, hipStream_t s) {
 static int mfma_min_t(int fmt) { return fmt == FMT_Q4 ? 1 : fmt == FMT_Q8 ? 4 : kGemvMaxT + 1; }
 
 hipError_t launch_gemv(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
-                       int cu_count, hipStream_t s) {
+                       int cu_count, hipStream_t s, bool glu) {
     if (t < 1 || t > kGemvMaxT || n_jobs < 1 || n_jobs > kMaxJobs) return hipErrorInvalidValue;
+    if (glu && (n_jobs != 2 || jobs[0].n_out != jobs[1].n_out)) return hipErrorInvalidValue;
     // IL_DECODE=valu|mfma pins the kernel family (both compute the same sums)
     bool use_mfma = t >= mfma_min_t(fmt);
     if (const char *force = getenv("IL_DECODE")) {
@@ -585,12 +624,30 @@ hipError_t launch_gemv(int fmt, const float *x, int t, int n_in, const KJob *job
         if (!strcmp(force, "valu")) use_mfma = false;
     }
     if (use_mfma && gemv_mfma_fits(fmt, t, n_in, jobs, n_jobs))
-        return launch_gemv_mfma(fmt, x, t, n_in, jobs, n_jobs, cu_count, s);
+        return launch_gemv_mfma(fmt, x, t, n_in, jobs, n_jobs, cu_count, s, glu);
     GemvParams p{};
     p.x = x;
     p.t = t;
     p.n_in = n_in;
     p.n_jobs = n_jobs;
+    if (glu) {
+        // both projections are numbered from row 0; the pairs are the rows
+        p.job[0] = jobs[0];
+        p.job[1] = jobs[1];
+        for (int j = 0; j <= kMaxJobs; ++j) p.row0[j] = 0;
+        p.total_rows = jobs[0].n_out;
+        bool taken = false;
+        hipError_t e = hipSuccess;
+        switch (fmt) {
+            case FMT_BF16: e = try_stream_glu<FMT_BF16>(p, s, &taken); break;
+            case FMT_Q8: e = try_stream_glu<FMT_Q8>(p, s, &taken); break;
+            case FMT_Q4: e = try_stream_glu<FMT_Q4>(p, s, &taken); break;
+            default: return hipErrorInvalidValue;
+        }
+        if (taken || e != hipSuccess) return e;
+        if (!gemv_mfma_fits(fmt, t, n_in, jobs, n_jobs)) return hipErrorInvalidValue;
+        return launch_gemv_mfma(fmt, x, t, n_in, jobs, n_jobs, cu_count, s, true);
+    }
     int rows = 0;
     for (int j = 0; j < n_jobs; ++j) {
         p.job[j] = jobs[j];

@@ -71,7 +71,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;                    // weight rows per MFMA tile
 // tiles accumulated in registers at once (fewer with two A row groups, whose
 // accumulators and x operands take twice the registers)
-constexpr int chunk_tiles(int ng) { return ng >= 2 ? 6 : 9; }
+// (with gate/up pairs an even count: 4 pairs, or 2 with two A row groups)
+constexpr int chunk_tiles(int ng, bool glu) { return ng >= 2 ? (glu ? 4 : 6) : (glu ? 8 : 9); }
 constexpr uint32_t kBufFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
 constexpr uint32_t kOut = 0x7FFFFFF0u;       // a buffer offset past every range: reads 0
 
@@ -232,9 +233,15 @@ struct Chunk {
 // NG >= 1: "wide" mode, t <= 16 NG, NG groups of 16 tokens per B operand,
 // A rows = bf16(x): rounded from the f32 x as it is loaded (NG = 1) or read
 // from the pre-pass's bf16 copy (NG = 2).
-template <int FMT, int TC, int NG>
+// GLU: jobs 0 and 1 are the gate and up projections (same rows); a chunk
+// holds TC / 2 tiles of each, slot r < TC / 2 gate tile r and slot TC / 2 + r
+// the up tile with the same rows, and the reduction writes
+// GELU(gate) * up to job 0's y.
+template <int FMT, int TC, int NG, bool GLU>
 __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     constexpr int BPS = Mfma<FMT>::BPS;
+    constexpr int TCh = GLU ? TC / 2 : TC;  // tiles of one job in a chunk
+    static_assert(!GLU || TC % 2 == 0, "gate/up tile pairs");
     constexpr bool kWide = NG > 0;
     constexpr int NA = kWide ? NG : 1;  // A row groups per B operand
     __shared__ f32x4 red[kWaves][TC][kWide ? 64 : 32];
@@ -282,10 +289,12 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         Chunk c;
         c.start = start;
         c.j = 0;
+        if constexpr (!GLU) {
 #pragma unroll
-        for (int q = 1; q < kMaxJobs; ++q)
-            if (q < p.n_jobs && start >= p.tile0[q]) c.j = q;
-        c.cnt = start < tb ? min(TC, min(tb, p.tile0[c.j + 1]) - start) : 0;
+            for (int q = 1; q < kMaxJobs; ++q)
+                if (q < p.n_jobs && start >= p.tile0[q]) c.j = q;
+        }
+        c.cnt = start < tb ? min(TCh, min(tb, p.tile0[c.j + 1]) - start) : 0;
         c.lrow0 = (start - p.tile0[c.j]) * kTile;
         return c;
     };
@@ -301,14 +310,19 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     // issue side: chunk, step and the chunk's buffer descriptors
     Chunk ic = chunk_at(ta);
     int is = wave;
-    __amdgpu_buffer_rsrc_t crs, srs;
+    __amdgpu_buffer_rsrc_t crs, srs, crs2, srs2;  // *2: the up projection (GLU)
     int ic_nout;  // rows of the issue chunk's job
     auto set_rsrc = [&]() {
         const KJob &jb = p.job[ic.j];
         ic_nout = jb.n_out;
         const int64_t rows = ic.cnt > 0 ? jb.n_out : 0;
+        const uint32_t sbytes = (uint32_t)(tiled_scale_count(rows, nb) * (FMT == FMT_Q8 ? 4 : 2));
         crs = make_rsrc(jb.codes, (uint32_t)(rows * row_bytes));
-        srs = make_rsrc(jb.scales_t, (uint32_t)(tiled_scale_count(rows, nb) * (FMT == FMT_Q8 ? 4 : 2)));
+        srs = make_rsrc(jb.scales_t, sbytes);
+        if constexpr (GLU) {
+            crs2 = make_rsrc(p.job[1].codes, (uint32_t)(rows * row_bytes));
+            srs2 = make_rsrc(p.job[1].scales_t, sbytes);
+        }
     };
     set_rsrc();
     auto issue_x = [&]() {
@@ -336,20 +350,23 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     };
     auto issue_w = [&](int r) {
         const int kb = 4 * is + g;  // 16-byte chunk of the row this lane fetches
-        const int row = ic.lrow0 + kTile * r + n;
-        const bool row_ok = r < ic.cnt && row < ic_nout;
+        const int rt = r % TCh;     // tile of its job
+        const bool up = GLU && r >= TCh;
+        const __amdgpu_buffer_rsrc_t wrs = up ? crs2 : crs, qrs = up ? srs2 : srs;
+        const int row = ic.lrow0 + kTile * rt + n;
+        const bool row_ok = rt < ic.cnt && row < ic_nout;
         const bool ok = row_ok && (int64_t)kb * 16 < row_bytes;
-        wc[r] = bload16(crs, ok ? (uint32_t)(row * row_bytes + kb * 16) : kOut);
+        wc[r] = bload16(wrs, ok ? (uint32_t)(row * row_bytes + kb * 16) : kOut);
         // scales from the tiled plane: a tile's 16 rows x 4 blocks are one run
         if constexpr (FMT == FMT_Q4) {
             // the run of 4 scales of this lane's row (n) for blocks 4s..4s+3
             ws[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                srs, row_ok && 4 * is < nb ? (uint32_t)(tiled_scale_index(row, 4 * is, nb4) * 2) : kOut, 0, 0));
+                qrs, row_ok && 4 * is < nb ? (uint32_t)(tiled_scale_index(row, 4 * is, nb4) * 2) : kOut, 0, 0));
         } else if constexpr (FMT == FMT_Q8) {
             // this lane's 16 bytes are half of block 2s + g/2
             const int blk = 2 * is + (g >> 1);
             ws[r] = __builtin_amdgcn_raw_buffer_load_b32(
-                srs, row_ok && blk < nb ? (uint32_t)(tiled_scale_index(row, blk, nb4) * 4) : kOut, 0, 0);
+                qrs, row_ok && blk < nb ? (uint32_t)(tiled_scale_index(row, blk, nb4) * 4) : kOut, 0, 0);
         }
     };
     auto advance = [&](Chunk &c, int &s) {
@@ -375,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         for (int q = 0; q < NA; ++q) {
 #pragma unroll
             for (int r = 0; r < TC; ++r) {
-                if (r < c.cnt) {
+                if (r % TCh < c.cnt) {
                     if constexpr (kWide) {
                         red[wave][r][lane] = acc[r][q];
                     } else {
@@ -408,6 +425,13 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
                         float sum = 0.f;
 #pragma unroll
                         for (int w = 0; w < kWaves; ++w) sum += redf[((w * TC + r) * kLanes + slot) * 4 + e];
+                        if constexpr (GLU) {
+                            float su = 0.f;
+#pragma unroll
+                            for (int w = 0; w < kWaves; ++w)
+                                su += redf[((w * TC + TCh + r) * kLanes + slot) * 4 + e];
+                            sum = gelu(sum) * su;
+                        }
                         jb.y[(int64_t)token * jb.n_out + row] = sum;
                     }
                 }
@@ -499,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         issue_x();
 #pragma unroll
         for (int r = 0; r < TC; ++r) {
-            if (r < cc.cnt) consume(r, a);
+            if (r % TCh < cc.cnt) consume(r, a);
             issue_w(r);
         }
         const bool chunk_end = cs + kWaves >= S;
@@ -527,7 +551,9 @@ bool mfma_fits(int fmt, int64_t x_bytes, int n_in, const KJob *jobs, int n_jobs)
     return true;
 }
 
-bool fill_params(MfmaParams &p, int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
+// With glu the tile range is job 0's (the gate); each tile also stands for
+// the up projection's tile with the same rows.
+bool fill_params(MfmaParams &p, int fmt, int t, int n_in, const KJob *jobs, int n_jobs, bool glu) {
     p.t = t;
     p.n_in = n_in;
     p.nb = n_in / kBlock;
@@ -538,27 +564,31 @@ bool fill_params(MfmaParams &p, int fmt, int t, int n_in, const KJob *jobs, int 
     for (int j = 0; j < n_jobs; ++j) {
         p.job[j] = jobs[j];
         p.tile0[j] = tiles;
-        tiles += (jobs[j].n_out + kTile - 1) / kTile;
+        if (!glu || j == 0) tiles += (jobs[j].n_out + kTile - 1) / kTile;
     }
-    for (int j = n_jobs; j <= kMaxJobs; ++j) p.tile0[j] = tiles;
+    for (int j = glu ? 1 : n_jobs; j <= kMaxJobs; ++j) p.tile0[j] = tiles;
     p.tiles_total = tiles;
     return tiles > 0;
 }
 
-template <int FMT, int NG>
+template <int FMT, int NG, bool GLU>
 hipError_t launch_mode(const MfmaParams &p, int cu_count, hipStream_t s) {
     // one workgroup per compute unit at most, each an equal share of the tiles
     const int grid = p.tiles_total < cu_count ? p.tiles_total : cu_count;
-    hipLaunchKernelGGL((gemv_mfma_kernel<FMT, chunk_tiles(NG), NG>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemv_mfma_kernel<FMT, chunk_tiles(NG, GLU), NG, GLU>), dim3(grid), dim3(kThreads), 0, s,
+                       p);
     return hipGetLastError();
 }
 
 template <int NG>
-hipError_t launch_fmt_mode(int fmt, const MfmaParams &p, int cu_count, hipStream_t s) {
+hipError_t launch_fmt_mode(int fmt, const MfmaParams &p, int cu_count, hipStream_t s, bool glu) {
     switch (fmt) {
-        case FMT_BF16: return launch_mode<FMT_BF16, NG>(p, cu_count, s);
-        case FMT_Q8: return launch_mode<FMT_Q8, NG>(p, cu_count, s);
-        case FMT_Q4: return launch_mode<FMT_Q4, NG>(p, cu_count, s);
+        case FMT_BF16: return glu ? launch_mode<FMT_BF16, NG, true>(p, cu_count, s)
+                                  : launch_mode<FMT_BF16, NG, false>(p, cu_count, s);
+        case FMT_Q8: return glu ? launch_mode<FMT_Q8, NG, true>(p, cu_count, s)
+                                : launch_mode<FMT_Q8, NG, false>(p, cu_count, s);
+        case FMT_Q4: return glu ? launch_mode<FMT_Q4, NG, true>(p, cu_count, s)
+                                : launch_mode<FMT_Q4, NG, false>(p, cu_count, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -570,12 +600,13 @@ bool gemv_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
 }
 
 hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
-                            int cu_count, hipStream_t s) {
+                            int cu_count, hipStream_t s, bool glu) {
     if (!gemv_mfma_fits(fmt, t, n_in, jobs, n_jobs)) return hipErrorInvalidValue;
+    if (glu && (n_jobs != 2 || jobs[0].n_out != jobs[1].n_out)) return hipErrorInvalidValue;
     MfmaParams p{};
     p.x = x;
-    if (!fill_params(p, fmt, t, n_in, jobs, n_jobs)) return hipSuccess;
-    return launch_fmt_mode<0>(fmt, p, cu_count, s);
+    if (!fill_params(p, fmt, t, n_in, jobs, n_jobs, glu)) return hipSuccess;
+    return launch_fmt_mode<0>(fmt, p, cu_count, s, glu);
 }
 
 bool verify_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
@@ -583,14 +614,16 @@ bool verify_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
 }
 
 hipError_t launch_verify_mfma(int fmt, const float *x, const uint16_t *xb, int t, int n_in, const KJob *jobs,
-                              int n_jobs, int cu_count, hipStream_t s) {
+                              int n_jobs, int cu_count, hipStream_t s, bool glu) {
     if (!verify_mfma_fits(fmt, t, n_in, jobs, n_jobs)) return hipErrorInvalidValue;
+    if (glu && (n_jobs != 2 || jobs[0].n_out != jobs[1].n_out)) return hipErrorInvalidValue;
     if (t > kWideF32MaxT && xb == nullptr) return hipErrorInvalidValue;
     MfmaParams p{};
     p.x = x;
     p.xb = xb;
-    if (!fill_params(p, fmt, t, n_in, jobs, n_jobs)) return hipSuccess;
-    return t <= kWideF32MaxT ? launch_fmt_mode<1>(fmt, p, cu_count, s) : launch_fmt_mode<2>(fmt, p, cu_count, s);
+    if (!fill_params(p, fmt, t, n_in, jobs, n_jobs, glu)) return hipSuccess;
+    return t <= kWideF32MaxT ? launch_fmt_mode<1>(fmt, p, cu_count, s, glu)
+                             : launch_fmt_mode<2>(fmt, p, cu_count, s, glu);
 }
 
 }  // namespace il

@@ -50,6 +50,11 @@ __host__ __device__ inline int64_t tiled_scale_count(int64_t n_out, int64_t nb) 
     return (n_out + 15) / 16 * ((nb + 3) / 4) * 64;
 }
 
+// GELU(v) = v * Phi(v) = 0.5 v (1 + erf(v / sqrt 2)), the activation of the
+// fused gate/up step (gelu_mul on the oxinfer 0.0.1 src/drafter.rs page,
+// which does not print it; this is the plain definition).
+__device__ __forceinline__ float gelu(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
 // One job as the kernels see it.
 struct KJob {
     const void *codes;
@@ -72,17 +77,22 @@ hipError_t launch_repack_q8(const uint8_t *staging, int8_t *codes, float *scales
 hipError_t launch_repack_q4(const uint8_t *staging, uint8_t *codes, uint16_t *scales, uint16_t *scales_t,
                             int64_t n_out, int64_t n_in, hipStream_t s);
 
+// Every launcher below takes `glu`: when set, jobs[0] and jobs[1] are the
+// gate and up projections of one feed-forward step (same fmt and n_out,
+// n_jobs == 2) and the launch writes y = GELU(x G^T) * (x U^T) into
+// jobs[0].y only; g and u never reach memory.
+
 // ---- decode GEMV, t <= kGemvMaxT (il_gemv.hip) ----
 // All jobs share fmt, x and n_in; n_jobs <= kMaxJobs.
 hipError_t launch_gemv(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
-                       int cu_count, hipStream_t s);
+                       int cu_count, hipStream_t s, bool glu = false);
 
 // ---- decode GEMV on the bf16 matrix cores, t <= kGemvMaxT (il_gemv_mfma.hip) ----
 // Same contract as launch_gemv.  gemv_mfma_fits says whether the kernel's
 // 32-bit buffer offsets cover x and every job's weight planes.
 bool gemv_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs);
 hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
-                            int cu_count, hipStream_t s);
+                            int cu_count, hipStream_t s, bool glu = false);
 
 // ---- mid-size t (kGemvMaxT < t <= kVerifyMaxT) on the same kernel, "wide"
 // mode: up to 32 tokens per weight operand.  For t <= kWideF32MaxT the kernel
@@ -91,10 +101,10 @@ hipError_t launch_gemv_mfma(int fmt, const float *x, int t, int n_in, const KJob
 constexpr int kWideF32MaxT = 16;
 bool verify_mfma_fits(int fmt, int t, int n_in, const KJob *jobs, int n_jobs);
 hipError_t launch_verify_mfma(int fmt, const float *x, const uint16_t *xb, int t, int n_in, const KJob *jobs,
-                              int n_jobs, int cu_count, hipStream_t s);
+                              int n_jobs, int cu_count, hipStream_t s, bool glu = false);
 
 // ---- prefill GEMM, t > kGemvMaxT (il_gemm.hip) ----
 hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
-                       int cu_count, hipStream_t s);
+                       int cu_count, hipStream_t s, bool glu = false);
 
 }  // namespace il

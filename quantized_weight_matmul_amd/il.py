@@ -46,6 +46,9 @@ def lib() -> ctypes.CDLL:
             L.il_matmul.restype = ctypes.c_int
             L.il_matmul.argtypes = [ctypes.c_void_p, _i64, _i64, ctypes.POINTER(il_job), _i64,
                                     ctypes.c_void_p]
+            L.il_matmul_gelu_mul.restype = ctypes.c_int
+            L.il_matmul_gelu_mul.argtypes = [ctypes.c_void_p, _i64, _i64, ctypes.c_void_p, ctypes.c_void_p, _i64,
+                                             ctypes.c_void_p, ctypes.c_void_p]
             L.il_wants.restype = ctypes.c_int
             L.il_wants.argtypes = [_i64, _i64, _i64]
             L.il_name.restype = ctypes.c_char_p
@@ -180,6 +183,22 @@ def il_matmul(x, t: int, n_in: int, jobs, stream=None) -> int:
         stream = stream.cuda_stream
     return int(lib().il_matmul(ctypes.c_void_p(_ptr(x)), int(t), int(n_in), arr, len(jobs),
                                ctypes.c_void_p(int(stream))))
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def il_matmul_gelu_mul(x, t: int, n_in: int, gate: Weight, up: Weight, n_out: int, y, stream=None) -> int:
+    """y = GELU(x G^T) * (x U^T) in one submission; 1 on success, 0 if
+    nothing was computed (see il_last_error())."""
+    return int(lib().il_matmul_gelu_mul(ctypes.c_void_p(_ptr(x)), int(t), int(n_in),
+                                        gate.handle if gate else None, up.handle if up else None,
+                                        int(n_out), ctypes.c_void_p(_ptr(y)),
+                                        ctypes.c_void_p(int(_stream_handle(stream)))))
 
 
 def il_wants(n_out: int, n_in: int, t: int) -> int:

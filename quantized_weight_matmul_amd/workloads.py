@@ -114,6 +114,22 @@ QUANTIZE = {
 }
 
 
+# Fused gate/up + GELU workloads (il_matmul_gelu_mul): the gate/up pair of the
+# Q8 decode shape, and the same pair as Q4 and bf16; t = 1 (one drafted token).
+GELU_MUL = {
+    "f3_q8_t1": (Q8, 14336, 4096, 1, 7),  # fmt, n_out, n_in, t, cfg
+    "f3_q4_t1": (Q4, 14336, 4096, 1, 7),
+    "f3_bf16_t1": (BF16, 14336, 4096, 1, 7),
+}
+
+
+def make_gelu_mul_inputs(name: str):
+    """(x [t, n_in] f32, gate, up) host-format weights of a GELU_MUL workload."""
+    fmt, n_out, n_in, t, cfg = GELU_MUL[name]
+    x = np.ascontiguousarray(gen_x(cfg, 0, t, n_in))
+    return x, gen_weight(fmt, cfg, 1, n_out, n_in), gen_weight(fmt, cfg, 2, n_out, n_in)
+
+
 def gen_q8_parts(cfg: int, tensor_id: int, n_out: int, n_in: int):
     g = rng_for(cfg, tensor_id)
     codes = g.integers(-127, 128, size=(n_out, n_in), dtype=np.int8)
