@@ -14,7 +14,9 @@ sum_k |x*w| in f64; the acceptance test is |y - y_ref| <= 4e-3 * bound per
 output element.  The arithmetic lives in ``il_oracle.c`` (plain C, gcc -O2);
 this module only marshals numpy arrays.
 
-Also here: ``gelu_mul`` (the fused gate/up feed-forward step, GELU(x G^T) *
+Also here: ``centroid_argmax`` (the centroid-masked LM head: centroid
+logits, top-k clusters, exact scores of their tokens, first-max argmax) with
+``token_score``; ``gelu_mul`` (the fused gate/up feed-forward step, GELU(x G^T) *
 (x U^T), with its propagated error bound; ``gelu`` alone), and, for the
 upload-quantiser row, ``quantize`` (f32 weights -> Q8 / Q4
 host blocks by per-block absmax scaling, rule stated in ``il_oracle.c``) and
@@ -120,6 +122,11 @@ class Oracle:
         lib.orc_gelu_mul_rows.restype = ctypes.c_int
         lib.orc_gelu_mul_rows.argtypes = [_ptr, _i64, _i64, _ptr, _ptr, ctypes.c_int, _i64, _i64, _i64,
                                           _ptr, _ptr, ctypes.c_int]
+        lib.orc_centroid_argmax.restype = ctypes.c_int
+        lib.orc_centroid_argmax.argtypes = [_ptr, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr, _i64,
+                                            _ptr, _ptr, _ptr, _ptr, _ptr]
+        lib.orc_token_score.restype = ctypes.c_double
+        lib.orc_token_score.argtypes = [_ptr, _i64, _ptr, _i64, ctypes.POINTER(ctypes.c_double)]
         lib.orc_check.restype = _i64
         lib.orc_check.argtypes = [_ptr, _ptr, _ptr, _i64, ctypes.c_double,
                                   ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]
@@ -240,6 +247,36 @@ class Oracle:
             raise ValueError("oracle gelu_mul failed")
         return y, bound
 
+    def centroid_argmax(self, x, centroids, embed, ordering, k: int) -> dict:
+        """Centroid-masked LM head per row of x [t, h]: centroids bf16 bits
+        [C, h], embed bf16 bits [V, h], ordering uint32 [V], k clusters.
+        Returns token [t], clusters [t, k] (visiting order), score [t] (f32),
+        cl and cl_bound [t, C] (exact f64 logits and sum |x*w|)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        t, h = x.shape
+        cen = np.ascontiguousarray(centroids, dtype=np.uint16)
+        emb = np.ascontiguousarray(embed, dtype=np.uint16)
+        order = np.ascontiguousarray(ordering, dtype=np.uint32)
+        n_c, vocab = cen.shape[0], emb.shape[0]
+        if cen.shape[1] != h or emb.shape[1] != h or order.shape != (vocab,):
+            raise ValueError("shape mismatch")
+        out = {"token": np.empty(t, np.int32), "clusters": np.empty((t, k), np.int32),
+               "score": np.empty(t, np.float32), "cl": np.empty((t, n_c), np.float64),
+               "cl_bound": np.empty((t, n_c), np.float64)}
+        if self.lib.orc_centroid_argmax(_p(x), t, h, _p(cen), n_c, _p(emb), vocab, _p(order), k,
+                                        _p(out["token"]), _p(out["clusters"]), _p(out["score"]),
+                                        _p(out["cl"]), _p(out["cl_bound"])) != 0:
+            raise ValueError("oracle centroid_argmax failed")
+        return out
+
+    def token_score(self, x_row, embed, tok: int):
+        """(exact f64 score, bound) of one token against one row of x."""
+        x_row = np.ascontiguousarray(x_row, dtype=np.float32)
+        emb = np.ascontiguousarray(embed, dtype=np.uint16)
+        b = ctypes.c_double(0.0)
+        v = self.lib.orc_token_score(_p(x_row), x_row.size, _p(emb), int(tok), ctypes.byref(b))
+        return float(v), float(b.value)
+
     def check(self, y, y_ref, bound, tol: float = TOL) -> dict:
         """Element-wise |y - y_ref| <= tol * bound (NaN/Inf in y fail)."""
         y = np.ascontiguousarray(y, dtype=np.float32)
@@ -298,6 +335,14 @@ def gelu(v):
 
 def gelu_mul(x, gate, up, fmt, n_out, r0=0, r1=None, threads=0):
     return default().gelu_mul(x, gate, up, fmt, n_out, r0, r1, threads)
+
+
+def centroid_argmax(x, centroids, embed, ordering, k):
+    return default().centroid_argmax(x, centroids, embed, ordering, k)
+
+
+def token_score(x_row, embed, tok):
+    return default().token_score(x_row, embed, tok)
 
 
 def f16_bits(values):

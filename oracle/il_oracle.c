@@ -419,6 +419,102 @@ int orc_gelu_mul_rows(const float *x, int64_t t, int64_t n_in, const void *gate,
     return failed ? -1 : 0;
 }
 
+/* ------------------------------------------- centroid-masked LM head
+ * The end of `Drafter::step` on the oxinfer 0.0.1 src/drafter.rs page: for
+ * each row x (length h) of a batch,
+ *   1. centroid logits cl[c] = centroids[c] . x for the C centroids (bf16
+ *      rows, [C, h]);
+ *   2. the k centroids with the largest logits;
+ *   3. for each chosen cluster c and j < per = V / C, the token
+ *      ordering[c * per + j] and its score embed[token] . x (bf16 rows of
+ *      the [V, h] embedding);
+ *   4. the token of the largest score, the first one met winning ties, the
+ *      clusters visited in the order of step 2 and tokens in j order.
+ * The page selects with select_nth_unstable, which leaves the order of the k
+ * clusters (and the choice among equal logits at the k-th place) open; the
+ * reading taken here: clusters ordered by decreasing logit, equal logits by
+ * increasing cluster index.  Logits and scores are exact f64 sums of the f64
+ * products, and each decision is taken on them rounded once to f32 (the
+ * precision the page computes them in).
+ * Outputs per row: the token, the k clusters in visiting order, the f32
+ * score of the token, and for the checks the f64 logits and their bounds
+ * sum |x * w| (cl, cl_bound: [t][C]). */
+static double orc_bf16_dot(const uint16_t *w, const float *x, int64_t h, double *mag)
+{
+    double acc = 0.0, m = 0.0;
+    for (int64_t e = 0; e < h; ++e) {
+        double p = orc_bf16_value(w[e]) * (double)x[e];
+        acc += p;
+        m += fabs(p);
+    }
+    if (mag) *mag = m;
+    return acc;
+}
+
+int orc_centroid_argmax(const float *x, int64_t t, int64_t h, const uint16_t *centroids, int64_t n_c,
+                        const uint16_t *embed, int64_t vocab, const uint32_t *ordering, int64_t k,
+                        int32_t *token, int32_t *clusters, float *score, double *cl, double *cl_bound)
+{
+    if (t < 0 || h <= 0 || n_c <= 0 || k < 1 || k > n_c || vocab < n_c || vocab % n_c) return -1;
+    const int64_t per = vocab / n_c;
+    for (int64_t v = 0; v < vocab; ++v)
+        if (ordering[v] >= (uint64_t)vocab) return -1;
+    int64_t *idx = (int64_t *)malloc((size_t)n_c * sizeof(int64_t));
+    float *clf = (float *)malloc((size_t)n_c * sizeof(float));
+    if (!idx || !clf) {
+        free(idx);
+        free(clf);
+        return -1;
+    }
+    for (int64_t i = 0; i < t; ++i) {
+        const float *xi = x + (size_t)i * (size_t)h;
+        double *cli = cl + (size_t)i * (size_t)n_c;
+        double *cbi = cl_bound + (size_t)i * (size_t)n_c;
+        for (int64_t c = 0; c < n_c; ++c) {
+            cli[c] = orc_bf16_dot(centroids + (size_t)c * (size_t)h, xi, h, &cbi[c]);
+            clf[c] = (float)cli[c];
+            idx[c] = c;
+        }
+        /* the k largest f32 logits, equal logits by increasing index: a
+         * selection sort over the first k places */
+        for (int64_t a = 0; a < k; ++a) {
+            int64_t best = a;
+            for (int64_t b = a + 1; b < n_c; ++b) {
+                float vb = clf[idx[b]], vbest = clf[idx[best]];
+                if (vb > vbest || (vb == vbest && idx[b] < idx[best])) best = b;
+            }
+            int64_t tmp = idx[a];
+            idx[a] = idx[best];
+            idx[best] = tmp;
+        }
+        float best_s = -INFINITY;
+        int32_t best_tok = -1;
+        for (int64_t a = 0; a < k; ++a) {
+            const int64_t c = idx[a];
+            clusters[(size_t)i * (size_t)k + (size_t)a] = (int32_t)c;
+            for (int64_t j = 0; j < per; ++j) {
+                const uint32_t tok = ordering[c * per + j];
+                float sc = (float)orc_bf16_dot(embed + (size_t)tok * (size_t)h, xi, h, NULL);
+                if (best_tok < 0 || sc > best_s) {
+                    best_s = sc;
+                    best_tok = (int32_t)tok;
+                }
+            }
+        }
+        token[i] = best_tok;
+        score[i] = best_s;
+    }
+    free(idx);
+    free(clf);
+    return 0;
+}
+
+/* Exact score (f64) and its bound of one token for row x: embed[tok] . x. */
+double orc_token_score(const float *x, int64_t h, const uint16_t *embed, int64_t tok, double *bound)
+{
+    return orc_bf16_dot(embed + (size_t)tok * (size_t)h, x, h, bound);
+}
+
 /* The acceptance test on n outputs: |y - y_ref| <= tol * bound, element by
  * element; a NaN or Inf in y always fails, and bound == 0 demands y == y_ref.
  * Returns the number of failing elements; *first_bad is the first failing

@@ -308,6 +308,75 @@ def pin_gelu_mul_composition(O):
             assert np.all(np.abs(_lib_gelu(g) * u - y) <= 4e-3 * bound * (1 + 1e-9)), "bound too small"
 
 
+# --------------------------------------------- centroid-masked LM head
+# Top-k centroids by logit, then the first token of largest score over their
+# clusters.  Pinned by integer-valued inputs (every sum exact in f32, so ties
+# are exact and the tie rules are tested) against a brute force in Python
+# integers, and by random inputs against a numpy float64 matmul plus a
+# selection written with numpy's lexsort / argmax.
+def _lm_head_brute(x_int, cen_int, emb_int, ordering, k):
+    t = x_int.shape[0]
+    n_c, vocab = cen_int.shape[0], emb_int.shape[0]
+    per = vocab // n_c
+    toks, clus, scores = [], [], []
+    for i in range(t):
+        cl = [int(np.dot(cen_int[c].astype(np.int64), x_int[i].astype(np.int64))) for c in range(n_c)]
+        sel = sorted(range(n_c), key=lambda c: (-cl[c], c))[:k]
+        best = None
+        for c in sel:
+            for j in range(per):
+                tok = int(ordering[c * per + j])
+                sc = int(np.dot(emb_int[tok].astype(np.int64), x_int[i].astype(np.int64)))
+                if best is None or sc > best[0]:
+                    best = (sc, tok)
+        toks.append(best[1]); clus.append(sel); scores.append(best[0])
+    return np.array(toks), np.array(clus), np.array(scores, dtype=np.float64)
+
+
+def _bf16_of_ints(a):
+    return wl.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def pin_lm_head_integers(O):
+    rng = np.random.default_rng(40)
+    for h, n_c, per, k in ((16, 8, 4, 1), (16, 8, 4, 3), (24, 12, 8, 12), (8, 16, 2, 5)):
+        vocab = n_c * per
+        x = rng.integers(-3, 4, (4, h))
+        cen = rng.integers(-2, 3, (n_c, h))
+        emb = rng.integers(-2, 3, (vocab, h))
+        cen[1] = cen[0]            # equal logits: the lower cluster index goes first
+        emb[5] = emb[2]            # equal scores: the first met wins
+        order = rng.permutation(vocab).astype(np.uint32)
+        r = O.centroid_argmax(x.astype(np.float32), _bf16_of_ints(cen), _bf16_of_ints(emb), order, k)
+        tok, clus, sc = _lm_head_brute(x, cen, emb, order, k)
+        assert np.array_equal(r["clusters"], clus), f"clusters h={h} C={n_c} k={k}"
+        assert np.array_equal(r["token"], tok), f"token h={h} C={n_c} k={k}"
+        assert np.array_equal(r["score"].astype(np.float64), sc), "score"
+
+
+def pin_lm_head_random(O):
+    rng = np.random.default_rng(41)
+    t, h, n_c, per, k = 3, 64, 32, 8, 4
+    vocab = n_c * per
+    x = rng.standard_normal((t, h)).astype(np.float32)
+    cen = wl.f32_to_bf16_bits(rng.standard_normal((n_c, h)).astype(np.float32))
+    emb = wl.f32_to_bf16_bits(rng.standard_normal((vocab, h)).astype(np.float32))
+    order = rng.permutation(vocab).astype(np.uint32)
+    r = O.centroid_argmax(x, cen, emb, order, k)
+    cenf, embf = lib_bf16(cen), lib_bf16(emb)
+    cl = x.astype(np.float64) @ cenf.T
+    assert np.allclose(r["cl"], cl, rtol=1e-12, atol=1e-12), "centroid logits"
+    assert np.allclose(r["cl_bound"], np.abs(x.astype(np.float64)) @ np.abs(cenf).T, rtol=1e-12), "bounds"
+    for i in range(t):
+        cl32 = r["cl"][i].astype(np.float32)
+        sel = np.lexsort((np.arange(n_c), -cl32))[:k]  # decreasing logit, then increasing index
+        assert np.array_equal(r["clusters"][i], sel), "selection rule"
+        cand = np.concatenate([order[c * per:(c + 1) * per] for c in sel])
+        sc = (embf[cand] @ x[i].astype(np.float64)).astype(np.float32)
+        j = int(np.argmax(sc))  # first occurrence of the maximum
+        assert r["token"][i] == cand[j] and r["score"][i] == sc[j], "first-max argmax"
+
+
 # --------------------------------------------------------------- quantiser
 # The upload quantiser (absmax per 32-element block; the rule is stated in
 # il_oracle.c).  Its pins: numpy's float16 cast on every binary16 value, on
@@ -584,6 +653,7 @@ ALL_PINS = [
     pin_numpy_matmul, pin_points_equal_rows, pin_thread_invariance, pin_check_rule,
     pin_f16_rounding, pin_quantize_hand, pin_quantize_roundtrip, pin_quantize_nearest,
     pin_gelu_values, pin_gelu_mul_onehot, pin_gelu_mul_composition,
+    pin_lm_head_integers, pin_lm_head_random,
 ]
 
 

@@ -55,6 +55,11 @@ MUTANTS = {
                                  "double q = floor(a * ldexp(1.0, 24));"),
     "f16_overflow": ("if (be >= 31) return sign", "if (be >= 32) return sign"),
     "gelu_x_row": ("const float *xrow = x + (size_t)i * (size_t)n_in;", "const float *xrow = x;"),
+    "lm_tie_index": ("(vb == vbest && idx[b] < idx[best])", "(vb == vbest && idx[b] > idx[best])"),
+    "lm_select_smallest": ("if (vb > vbest ||", "if (vb < vbest ||"),
+    "lm_last_max": ("if (best_tok < 0 || sc > best_s) {", "if (best_tok < 0 || sc >= best_s) {"),
+    "lm_ordering_index": ("const uint32_t tok = ordering[c * per + j];", "const uint32_t tok = ordering[j * n_c + c];"),
+    "lm_x_row": ("const float *xi = x + (size_t)i * (size_t)h;", "const float *xi = x;"),
     "gelu_half": ("return 0.5 * v * (1.0 + erf(v / sqrt(2.0)));", "return v * (1.0 + erf(v / sqrt(2.0)));"),
     "gelu_erf_argument": ("erf(v / sqrt(2.0))", "erf(v)"),
     "gelu_mul_operand": ("double v = gl * u;", "double v = gl * g;"),
