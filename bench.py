@@ -52,6 +52,7 @@ DESCRIPTIONS = {
     "c4_t32": "Q4 verify, t=32, 2 jobs [17408, 5120]",
     "c5a": "bf16 prefill, t=2048, 2 jobs [4096|14336] x 4096",
     "c5b": "Q4 prefill, t=512, 1 job [14336, 4096]",
+    "f4_lmhead_t1": "centroid-masked LM head, t=1: h=256, 2048 centroids, top 32, vocabulary 2^18 (bf16)",
     "f3_q8_t1": "fused gate/up + GELU, Q8, t=1, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T)",
     "f3_q4_t1": "fused gate/up + GELU, Q4, t=1, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T)",
     "f3_bf16_t1": "fused gate/up + GELU, bf16, t=1, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T)",
@@ -127,6 +128,75 @@ def stats_device_ms(il, path: str) -> float:
         if line.startswith(path + ":"):
             return float(line.split("device_ms=")[1].split()[0])
     raise RuntimeError(f"no {path} line in il_stats")
+
+
+def bench_lm_head(args, name: str) -> int:
+    """The centroid-masked LM head: one il_centroid_argmax per step (centroid
+    logits, top-k, scores of the chosen clusters' tokens, argmax) over
+    embedding / centroid copies rotated past the MALL.  It is latency-bound:
+    value = bytes it touches (centroids + the gathered embedding rows +
+    their ordering entries) per second of wall time."""
+    import torch
+
+    import quantized_weight_matmul_amd as il
+    h, n_c, k, vocab, t, cfg = wl.LM_HEAD[name]
+    per = vocab // n_c
+    log(f"[bench] workload {name}: {DESCRIPTIONS[name]}")
+    x_np, cen, emb, order = wl.make_lm_head_inputs(name)
+    touched = n_c * h * 2 + t * k * per * (h * 2 + 4)
+    n_sets = max(1, -(-ROTATE_BYTES // (vocab * h * 2)))
+    log(f"[bench] uploading {n_sets} embedding copies x {vocab * h * 2 / 1e6:.1f} MB")
+    sets = []
+    for _ in range(n_sets):
+        pair = (il.il_upload(cen, il.IL_BF16, n_c, h), il.il_upload(emb, il.IL_BF16, vocab, h))
+        if None in pair:
+            raise RuntimeError(il.il_last_error())
+        sets.append(pair)
+    x = torch.from_numpy(x_np).cuda()
+    od = torch.from_numpy(order.view(np.int32)).cuda()
+    tok = torch.empty((t,), dtype=torch.int32, device="cuda")
+    ws = torch.empty((il.il_centroid_argmax_workspace(t, n_c, k),), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()  # default priority
+
+    def step(i, s):
+        hc, he = sets[i % n_sets]
+        if il.il_centroid_argmax(x, t, h, hc, he, od, k, tok, None, None, workspace=ws, stream=s) != 1:
+            raise RuntimeError(il.il_last_error())
+
+    ms_per_step, kern_ms, pair_ms = time_steps(step, args, stream, 1)
+    value = touched / (ms_per_step * 1e-3) / 1e9
+    achieved = touched / (kern_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
+                "kernel_ms": round(kern_ms, 6),
+                "timing": "HIP events on the launch stream around the timed region / calls (3 kernels each)",
+                "event_pair_ms_median": round(pair_ms, 6)}
+    log(f"[bench] {ms_per_step * 1e3:.2f} us/call wall, {kern_ms * 1e3:.2f} us device ({achieved:.1f} GB/s touched)")
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.centroid_argmax(x_np, cen, emb, order, k)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or el / reps * (reps + 1) > args.cpu_seconds * 2:
+                break
+        cpu = {"value": round(touched * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} full oracle LM-head passes ({el / reps * 1e3:.2f} ms each)",
+               "seconds": round(el, 2)}
+    out = {
+        "metric": "centroid-masked LM head: GB/s of bytes touched (latency-bound); us per call in ms_per_step",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{name}: {DESCRIPTIONS[name]}", "t": t, "h": h, "centroids": n_c, "top_k": k,
+                   "vocab": vocab, "bytes_touched_per_call": touched, "embedding_copies_rotated": n_sets,
+                   "timing": "eager" if args.no_graph else "hip-graph"},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def bench_gelu_mul(args, name: str) -> int:
@@ -295,7 +365,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="c2",
-                    choices=sorted(wl.SUBMISSIONS) + sorted(wl.QUANTIZE) + sorted(wl.GELU_MUL))
+                    choices=sorted(wl.SUBMISSIONS) + sorted(wl.QUANTIZE) + sorted(wl.GELU_MUL) + sorted(wl.LM_HEAD))
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -330,6 +400,8 @@ def main() -> int:
         return bench_quantize(args, args.workload)
     if args.workload in wl.GELU_MUL:
         return bench_gelu_mul(args, args.workload)
+    if args.workload in wl.LM_HEAD:
+        return bench_lm_head(args, args.workload)
     sub = wl.SUBMISSIONS[args.workload]
     decode = sub.t <= 8
     streaming = sub.t <= STREAMING_MAX_T

@@ -168,6 +168,44 @@ IL_API int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs
 IL_API int il_matmul_gelu_mul(const float *x, int64_t t, int64_t n_in, const il_weight *gate,
                               const il_weight *up, int64_t n_out, float *y, void *hip_stream);
 
+/* Centroid-masked LM head -- for each row x of a batch, the argmax token
+ * over a centroid-selected subset of the vocabulary (the end of
+ * `Drafter::step` on the oxinfer 0.0.1 src/drafter.rs page):
+ *   1. centroid logits cl[c] = centroids[c] . x (c < C);
+ *   2. the top_k centroids of largest logit, visited by decreasing logit and,
+ *      among equal logits, increasing index (the page's select_nth_unstable
+ *      leaves this order open; this is the reading taken);
+ *   3. the score embed[tok] . x of every token tok = ordering[c * V/C + j]
+ *      (j < V/C) of those clusters, and the first token of largest score met
+ *      in visiting order (clusters in step-2 order, tokens in j order).
+ * Logits and scores are f32 sums of bf16 x f32 products; where two logits or
+ * scores are closer than their rounding, either choice is correct.
+ *   x          : DEVICE float[t][h], 16-byte aligned; 1 <= t <= 8.
+ *   centroids  : bf16 handle [C, h];  embed : bf16 handle [V, h], V % C == 0.
+ *   ordering   : DEVICE uint32[V]; entries >= V are skipped (never chosen).
+ *   top_k      : 1 <= top_k <= C; (C + h + 2 * next_pow2(top_k)) * 4 bytes
+ *                must fit in 152 KiB (one workgroup's LDS less 8 KiB).
+ *   token      : DEVICE int32[t]: the chosen token (-1 if every candidate of
+ *                the row was skipped).
+ *   clusters   : DEVICE int32[t][top_k] or NULL: the chosen clusters in
+ *                visiting order.
+ *   score      : DEVICE float[t] or NULL: the chosen token's score.
+ *   workspace  : DEVICE scratch of at least il_centroid_argmax_workspace(t,
+ *                C, top_k) bytes, owned by the caller and not used by
+ *                anything else until the stream has passed this call; or
+ *                NULL, and the library allocates it stream-ordered (slower:
+ *                allocation nodes in graphs, ~15 us per call measured).
+ *   hip_stream : as for il_matmul.
+ * Validation, stream semantics and the 1 / 0 return follow il_matmul. */
+IL_API int il_centroid_argmax(const float *x, int64_t t, int64_t h, const il_weight *centroids,
+                              const il_weight *embed, const uint32_t *ordering, int64_t top_k, int32_t *token,
+                              int32_t *clusters, float *score, void *workspace, int64_t workspace_bytes,
+                              void *hip_stream);
+
+/* Bytes of workspace il_centroid_argmax needs for t rows, C centroids and
+ * top_k clusters (t * (C + 2 * top_k) * 4); -1 for sizes it does not take. */
+IL_API int64_t il_centroid_argmax_workspace(int64_t t, int64_t n_centroids, int64_t top_k);
+
 /* Backend::wants -- whether a matmul of these dimensions is worth running on
  * the GPU (the page: dispatch has a fixed cost, so small ops stay on the
  * CPU).  A pure function of the sizes: 1 if 2 * n_out * n_in * t is at least

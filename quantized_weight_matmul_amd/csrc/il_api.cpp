@@ -639,6 +639,94 @@ int il_matmul_gelu_mul(const float *x, int64_t t, int64_t n_in, const il_weight 
     return 1;
 }
 
+int64_t il_centroid_argmax_workspace(int64_t t, int64_t n_centroids, int64_t top_k) {
+    if (t < 0 || n_centroids < 1 || top_k < 1 || t > il::kGemvMaxT || n_centroids > INT_MAX || top_k > INT_MAX)
+        return -1;
+    return (int64_t)il::lm_head_workspace_bytes((int)t, (int)n_centroids, (int)top_k);
+}
+
+int il_centroid_argmax(const float *x, int64_t t, int64_t h, const il_weight *centroids, const il_weight *embed,
+                       const uint32_t *ordering, int64_t top_k, int32_t *token, int32_t *clusters, float *score,
+                       void *workspace, int64_t workspace_bytes, void *hip_stream) {
+    g_err.clear();
+    if (t < 0) {
+        set_err("il_centroid_argmax: negative t");
+        return 0;
+    }
+    if (t == 0) return 1;
+    if (!x || !centroids || !embed || !ordering || !token) {
+        set_err("il_centroid_argmax: x, centroids, embed, ordering or token is NULL");
+        return 0;
+    }
+    if (t > il::kGemvMaxT) {
+        set_err("il_centroid_argmax: t = %" PRId64 " rows; at most %d", t, il::kGemvMaxT);
+        return 0;
+    }
+    if (centroids->fmt != IL_BF16 || embed->fmt != IL_BF16 || centroids->n_in != h || embed->n_in != h) {
+        set_err("il_centroid_argmax: centroids and embed must be bf16 with n_in = h = %" PRId64, h);
+        return 0;
+    }
+    const int64_t n_c = centroids->n_out, vocab = embed->n_out;
+    if (vocab % n_c) {
+        set_err("il_centroid_argmax: vocabulary %" PRId64 " is not a multiple of the %" PRId64 " centroids", vocab,
+                n_c);
+        return 0;
+    }
+    if (top_k < 1 || top_k > n_c) {
+        set_err("il_centroid_argmax: top_k = %" PRId64 " outside [1, %" PRId64 "]", top_k, n_c);
+        return 0;
+    }
+    if (il::lm_head_lds_bytes((int)n_c, (int)h, (int)top_k) > il::kLmHeadMaxLds) {
+        set_err("il_centroid_argmax: %" PRId64 " centroids and h = %" PRId64 " exceed the LDS of one workgroup", n_c, h);
+        return 0;
+    }
+    if (reinterpret_cast<uintptr_t>(x) % 16) {
+        set_err("il_centroid_argmax: x must be 16-byte aligned");
+        return 0;
+    }
+    if (env_flag("IL_FORCE_FAIL", "matmul")) {
+        set_err("il_centroid_argmax: failure injected by IL_FORCE_FAIL");
+        return 0;
+    }
+    int dev = -1;
+    DeviceCtx *ctx = context(&dev);
+    if (!ctx) return 0;
+    if (centroids->device != dev || embed->device != dev) {
+        set_err("il_centroid_argmax: the weights live on another device than the current %d", dev);
+        return 0;
+    }
+    if (!device_range_ok(x, t * h * 4, "x") || !device_range_ok(ordering, vocab * 4, "ordering") ||
+        !device_range_ok(token, t * 4, "token") ||
+        (clusters && !device_range_ok(clusters, t * top_k * 4, "clusters")) ||
+        (score && !device_range_ok(score, t * 4, "score")))
+        return 0;
+    if (workspace) {
+        const int64_t need = (int64_t)il::lm_head_workspace_bytes((int)t, (int)n_c, (int)top_k);
+        if (workspace_bytes < need) {
+            set_err("il_centroid_argmax: workspace of %" PRId64 " bytes, %" PRId64 " needed", workspace_bytes, need);
+            return 0;
+        }
+        if (!device_range_ok(workspace, need, "workspace")) return 0;
+    }
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const il::KJob cj{centroids->codes, nullptr, nullptr, nullptr, (int)n_c};
+    hipError_t e = il::launch_lm_head(x, (int)t, (int)h, cj, static_cast<const uint16_t *>(embed->codes),
+                                      (int)vocab, ordering, (int)top_k, token, clusters, score, workspace,
+                                      ctx->cu_count, s);
+    if (e != hipSuccess) {
+        set_err("il_centroid_argmax: launch failed: %s", hipGetErrorString(e));
+        g_failed++;
+        return 0;
+    }
+    PathStats &st = g_stats[0];
+    st.calls++;
+    st.launches += 3;
+    st.jobs += 1;
+    st.bytes += (uint64_t)(centroids->host_bytes + t * top_k * (vocab / n_c) * h * 2);
+    st.flops += 2ull * (uint64_t)t * (uint64_t)h * (uint64_t)(n_c + top_k * (vocab / n_c));
+    return 1;
+}
+
 int il_wants(int64_t n_out, int64_t n_in, int64_t t) {
     if (n_out <= 0 || n_in <= 0 || t <= 0) return 0;
     double min_flop = 262144.0;  // 2^18

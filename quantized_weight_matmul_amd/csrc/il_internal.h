@@ -107,4 +107,19 @@ hipError_t launch_verify_mfma(int fmt, const float *x, const uint16_t *xb, int t
 hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
                        int cu_count, hipStream_t s, bool glu = false);
 
+// ---- centroid-masked LM head (il_lmhead.hip) ----
+// x [t][h] (t <= kGemvMaxT); centroids: a bf16 job [C][h]; embed bf16 [V][h]
+// with V % C == 0; ordering [V] (entries < V); 1 <= k <= C.  Writes token[t]
+// and, when not null, clusters[t][k] (visiting order) and score[t].
+// Dynamic LDS budget of the select kernel: 160 KiB less 8 KiB kept for its
+// static arrays (histograms and per-wave results, about 4.2 KiB).
+constexpr size_t kLmHeadMaxLds = 152 * 1024;
+size_t lm_head_lds_bytes(int n_c, int h, int k);
+// workspace: lm_head_workspace_bytes(t, C, k) bytes of device memory, or
+// null for a stream-ordered allocation.
+size_t lm_head_workspace_bytes(int t, int n_c, int k);
+hipError_t launch_lm_head(const float *x, int t, int h, const KJob &centroids, const uint16_t *embed, int vocab,
+                          const uint32_t *ordering, int k, int *token, int *clusters, float *score, void *workspace,
+                          int cu_count, hipStream_t s);
+
 }  // namespace il

@@ -49,6 +49,12 @@ def lib() -> ctypes.CDLL:
             L.il_matmul_gelu_mul.restype = ctypes.c_int
             L.il_matmul_gelu_mul.argtypes = [ctypes.c_void_p, _i64, _i64, ctypes.c_void_p, ctypes.c_void_p, _i64,
                                              ctypes.c_void_p, ctypes.c_void_p]
+            L.il_centroid_argmax.restype = ctypes.c_int
+            L.il_centroid_argmax.argtypes = [ctypes.c_void_p, _i64, _i64, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, _i64, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, _i64, ctypes.c_void_p]
+            L.il_centroid_argmax_workspace.restype = _i64
+            L.il_centroid_argmax_workspace.argtypes = [_i64, _i64, _i64]
             L.il_wants.restype = ctypes.c_int
             L.il_wants.argtypes = [_i64, _i64, _i64]
             L.il_name.restype = ctypes.c_char_p
@@ -199,6 +205,27 @@ def il_matmul_gelu_mul(x, t: int, n_in: int, gate: Weight, up: Weight, n_out: in
                                         gate.handle if gate else None, up.handle if up else None,
                                         int(n_out), ctypes.c_void_p(_ptr(y)),
                                         ctypes.c_void_p(int(_stream_handle(stream)))))
+
+
+def il_centroid_argmax(x, t: int, h: int, centroids: Weight, embed: Weight, ordering, top_k: int, token,
+                       clusters=None, score=None, workspace=None, workspace_bytes: int = 0, stream=None) -> int:
+    """Centroid-masked LM head: token[t] (device int32) per row of x; the
+    chosen clusters [t, top_k] and scores [t] when those buffers are given.
+    ordering is a device uint32 [V] tensor; workspace an optional device
+    buffer of il_centroid_argmax_workspace(t, C, top_k) bytes.  1 on
+    success, 0 otherwise."""
+    if workspace is not None and not workspace_bytes and hasattr(workspace, "numel"):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return int(lib().il_centroid_argmax(ctypes.c_void_p(_ptr(x)), int(t), int(h),
+                                        centroids.handle if centroids else None, embed.handle if embed else None,
+                                        ctypes.c_void_p(_ptr(ordering)), int(top_k), ctypes.c_void_p(_ptr(token)),
+                                        ctypes.c_void_p(_ptr(clusters)), ctypes.c_void_p(_ptr(score)),
+                                        ctypes.c_void_p(_ptr(workspace)), int(workspace_bytes),
+                                        ctypes.c_void_p(int(_stream_handle(stream)))))
+
+
+def il_centroid_argmax_workspace(t: int, n_centroids: int, top_k: int) -> int:
+    return int(lib().il_centroid_argmax_workspace(int(t), int(n_centroids), int(top_k)))
 
 
 def il_wants(n_out: int, n_in: int, t: int) -> int:

@@ -130,6 +130,23 @@ def make_gelu_mul_inputs(name: str):
     return x, gen_weight(fmt, cfg, 1, n_out, n_in), gen_weight(fmt, cfg, 2, n_out, n_in)
 
 
+# Centroid-masked LM head workload: a 256-wide drafter hidden state, 2048
+# centroids, the top 32 visited, a vocabulary of 2^18 tokens (the pages state
+# H, C and k; no vocabulary size, so 2^18 stands for a current LLM's).
+LM_HEAD = {"f4_lmhead_t1": (256, 2048, 32, 1 << 18, 1, 8)}  # h, C, k, V, t, cfg
+
+
+def make_lm_head_inputs(name: str):
+    """(x [t, h] f32, centroids bf16 bits [C, h], embed bf16 bits [V, h],
+    ordering uint32 [V]): N(0, 1) x, N(0, 0.02) rows, a seeded permutation."""
+    h, n_c, k, vocab, t, cfg = LM_HEAD[name]
+    x = np.ascontiguousarray(gen_x(cfg, 0, t, h))
+    cen = gen_bf16(cfg, 1, n_c, h)
+    emb = gen_bf16(cfg, 2, vocab, h)
+    order = rng_for(cfg, 3).permutation(vocab).astype(np.uint32)
+    return x, cen, emb, order
+
+
 def gen_q8_parts(cfg: int, tensor_id: int, n_out: int, n_in: int):
     g = rng_for(cfg, tensor_id)
     codes = g.integers(-127, 128, size=(n_out, n_in), dtype=np.int8)

@@ -23,7 +23,7 @@ def header_symbols():
 def test_header_declares_the_abi():
     assert header_symbols() == sorted([
         "il_upload", "il_upload_quantize", "il_download", "il_free", "il_matmul", "il_matmul_gelu_mul",
-        "il_wants", "il_name", "il_stats", "il_weight_bytes", "il_last_error"])
+        "il_centroid_argmax", "il_centroid_argmax_workspace", "il_wants", "il_name", "il_stats", "il_weight_bytes", "il_last_error"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -186,3 +186,10 @@ def test_upload_quantize_without_a_device_declines():
 def test_download_null_handle():
     assert binding.lib().il_download(None, None, 0) == -1
     assert "NULL" in il.il_last_error()
+
+
+def test_centroid_argmax_workspace_size():
+    assert il.il_centroid_argmax_workspace(1, 2048, 32) == (2048 + 64) * 4
+    assert il.il_centroid_argmax_workspace(8, 100, 3) == 8 * (100 + 6) * 4
+    assert il.il_centroid_argmax_workspace(9, 2048, 32) == -1  # at most 8 rows
+    assert il.il_centroid_argmax_workspace(1, 0, 1) == -1
