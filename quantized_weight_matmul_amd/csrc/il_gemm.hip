@@ -15,12 +15,15 @@
 // (128 f32 accumulators per lane).  The 32x32x16 bf16 MFMA is used because
 // one wave issuing it keeps the matrix core near its peak, which 16x16x32
 // does not; two waves per SIMD let one wave's MFMAs cover the other's waits.
-// Each K step's operand tiles are fetched into registers one step ahead
-// (Q8/Q4 codes are dequantised there), then written to the LDS stage the
-// MFMAs are not reading: two 64 KiB stages, one barrier per step.  Rows of 64
-// bf16 (8 chunks of 16 bytes) are stored with the chunk index XOR-swizzled by
-// the row, so that both the staging writes and the MFMA fragment reads are
-// free of LDS bank conflicts.  Workgroups are mapped to tiles XCD by XCD
+// bf16 weights (gemm_bf16_kernel): each K step's x and W tiles go from L2
+// straight into the LDS stage the MFMAs are not reading (buffer loads with
+// the LDS bit: no staging registers, no LDS write instructions), issued at
+// the start of the step before; two 64 KiB stages, one barrier per step.
+// Q8/Q4 weights (gemm_kernel): the tiles are fetched into registers one step
+// ahead, the codes dequantised there, then written to the idle stage.  Rows
+// of 64 bf16 (8 chunks of 16 bytes) are stored with the chunk index
+// XOR-swizzled by the row, so that the fragment reads (and the staging
+// writes) are free of LDS bank conflicts.  Workgroups are mapped to tiles XCD by XCD
 // (consecutive workgroup ids go to different XCDs), so that each XCD works on
 // one contiguous range of weight-row tiles and its L2 holds the operand slices
 // its workgroups share.
@@ -78,6 +81,29 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // consecutive rows read at one chunk land in 16 distinct (bank-half, slot)
 // pairs (64-bank LDS), and any 8 in 8 distinct slots (32-bank LDS).
 __device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; the other counters are not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the release fence of __syncthreads, which would
+// wait for every load in flight; callers wait for what must have landed
+// first.  The signal fences keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// dst + 16 l (dst is wave-uniform); reads past the buffer write zeros.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint16_t *dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
+}
 
 // x f32 -> bf16 (RNE) pre-pass: 8 elements per thread.
 __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float *__restrict__ x, uint4 *__restrict__ xb,
@@ -325,16 +351,173 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
+// bf16 weights: the tiling, fragments and epilogue of gemm_kernel, with both
+// operand tiles copied from L2 into LDS by the load unit.  A stage holds the
+// A tile (BM rows) then the B tile (BN rows) of one K step, 16-byte chunks
+// swizzled as above; instruction i of wave w fills chunks
+// (w * kLoads + i) * 64 + lane of a tile, whose global address each lane
+// computes once.
+template <int BM, int BN, int WM, int WN, bool GLU>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(GemmParams p) {
+    constexpr int kThreads = 64 * WM * WN;
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+    constexpr bool kQuarter = BM < kBig;
+    constexpr int kCols = GLU ? BN / 2 : BN;
+    constexpr int kLoadsA = BM * BK / 8 / kThreads, kLoadsB = BN * BK / 8 / kThreads;
+    constexpr int kStage = (BM + BN) * BK;  // bf16 elements
+    static_assert(!GLU || TN == 2, "GLU pairs the two 32-column tiles of a wave");
+    static_assert(kLoadsA >= 1 && kLoadsB >= 1, "staging shape");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStage];
+
+    const int b = blockIdx.x;
+    const int unit = (b % kXcds) * p.units_per_xcd + b / kXcds;
+    if (unit >= p.n_units) return;
+    const int tile = p.tile_lo + (kQuarter ? unit >> 2 : unit);
+    const int q = kQuarter ? unit & 3 : 0;
+    const int tn_all = tile / p.tiles_m;
+    const int tm = tile - tn_all * p.tiles_m;
+    int j = 0;
+    if constexpr (!GLU) {
+#pragma unroll
+        for (int jj = 1; jj < kMaxJobs; ++jj)
+            if (jj < p.n_jobs && tn_all >= p.tn0[jj]) j = jj;
+    }
+    const KJob jb = p.job[j];
+    const int m0 = tm * kBig + (q >> 1) * BM;
+    const int n0 = (tn_all - p.tn0[j]) * (GLU ? kBig / 2 : kBig) + (q & 1) * kCols;
+    if (m0 >= p.t || n0 >= jb.n_out) return;  // a quarter past the edge of x or W
+    const int n_in = p.n_in;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    const uint32_t row2 = (uint32_t)n_in * 2u;
+    const int a_rows = min(BM, p.t - m0), b_rows = min(kCols, jb.n_out - n0);
+    const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.xb + (int64_t)m0 * n_in, (uint32_t)a_rows * row2);
+    const __amdgpu_buffer_rsrc_t brs =
+        make_rsrc(static_cast<const uint16_t *>(jb.codes) + (int64_t)n0 * n_in, (uint32_t)b_rows * row2);
+    const __amdgpu_buffer_rsrc_t brs2 =
+        GLU ? make_rsrc(static_cast<const uint16_t *>(p.job[1].codes) + (int64_t)n0 * n_in, (uint32_t)b_rows * row2)
+            : brs;
+
+    // this lane's chunk of each load: tile row r (8 chunks per row), chunk
+    // c = slot ^ key(r); GLU: B-tile row v is row (v / 64) 32 + v % 32 of the
+    // gate ((v / 32) even) or up projection -- 8-row blocks never straddle
+    // a 32-row group, so the choice is uniform per instruction
+    uint32_t offa[kLoadsA], offb[kLoadsB];
+    int ka[kLoadsA], kb[kLoadsB];
+#pragma unroll
+    for (int i = 0; i < kLoadsA; ++i) {
+        const int u = (wave * kLoadsA + i) * 64 + lane, r = u >> 3;
+        ka[i] = ((u & 7) ^ swz_key(r)) * 8;
+        offa[i] = (uint32_t)r * row2 + (uint32_t)ka[i] * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < kLoadsB; ++i) {
+        const int u = (wave * kLoadsB + i) * 64 + lane, v = u >> 3;
+        kb[i] = ((u & 7) ^ swz_key(v)) * 8;
+        const int wr = GLU ? (v >> 6) * 32 + (v & 31) : v;
+        offb[i] = (uint32_t)wr * row2 + (uint32_t)kb[i] * 2u;
+    }
+    auto issue = [&](int st, int k0) {
+        uint16_t *As = lds + st * kStage, *Bs = As + BM * BK;
+#pragma unroll
+        for (int i = 0; i < kLoadsA; ++i)
+            lds_load16(ars, As + (wave * kLoadsA + i) * 64 * 8, k0 + ka[i] < n_in ? offa[i] + (uint32_t)k0 * 2u : kOut);
+#pragma unroll
+        for (int i = 0; i < kLoadsB; ++i) {
+            const bool up = GLU && ((((wave * kLoadsB + i) * 8) >> 5) & 1);
+            lds_load16(up ? brs2 : brs, Bs + (wave * kLoadsB + i) * 64 * 8,
+                       k0 + kb[i] < n_in ? offb[i] + (uint32_t)k0 * 2u : kOut);
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) acc[a][n] = (f32x16){};
+    const int frow = lane & 31;
+    const int fkey = swz_key(frow);
+    const int a_base = (wm * (BM / WM) + frow) * BK;
+    const int b_base = (wn * (BN / WN) + frow) * BK;
+    auto compute = [&](int st) {
+        const uint16_t *As = lds + st * kStage, *Bs = As + BM * BK;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int slot = (kk * 2 + (lane >> 5)) ^ fkey;
+            bf16x8 fa[TM], fb[TN];
+#pragma unroll
+            for (int a = 0; a < TM; ++a) fa[a] = *reinterpret_cast<const bf16x8 *>(As + a_base + a * 32 * BK + slot * 8);
+#pragma unroll
+            for (int n = 0; n < TN; ++n) fb[n] = *reinterpret_cast<const bf16x8 *>(Bs + b_base + n * 32 * BK + slot * 8);
+#pragma unroll
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int n = 0; n < TN; ++n)
+                    acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[n], acc[a][n], 0, 0, 0);
+        }
+    };
+
+    // step ks computes stage ks & 1 while step ks + 1's tiles land in the
+    // other; the wait + barrier at the end of a step publishes them and
+    // frees the stage just read for the next issue
+    const int nk = (n_in + BK - 1) / BK;
+    issue(0, 0);
+    wait_vmcnt<0>();
+    lds_barrier();
+    for (int ks = 0; ks < nk; ++ks) {
+        if (ks + 1 < nk) issue((ks + 1) & 1, (ks + 1) * BK);
+        compute(ks & 1);
+        wait_vmcnt<0>();
+        lds_barrier();
+    }
+
+    // ---- epilogue (as gemm_kernel) ----
+    if constexpr (GLU) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+            const int col = n0 + wn * (BN / WN) / 2 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * (BM / WM) + a * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+                if (row < p.t && col < jb.n_out)
+                    jb.y[(int64_t)row * jb.n_out + col] = gelu(acc[a][0][i]) * acc[a][1][i];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+#pragma unroll
+            for (int n = 0; n < TN; ++n) {
+                const int col = n0 + wn * (BN / WN) + n * 32 + (lane & 31);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int row = m0 + wm * (BM / WM) + a * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+                    if (row < p.t && col < jb.n_out) jb.y[(int64_t)row * jb.n_out + col] = acc[a][n][i];
+                }
+            }
+        }
+    }
+}
+
 template <int FMT, bool GLU>
 hipError_t launch_units(GemmParams p, bool quarter, int tile_lo, int n_units, hipStream_t s) {
     p.tile_lo = tile_lo;
     p.n_units = n_units;
     p.units_per_xcd = (n_units + kXcds - 1) / kXcds;
     const dim3 grid(kXcds * p.units_per_xcd);
-    if (quarter)
-        hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 2, GLU>), grid, dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((gemm_kernel<FMT, kBig, kBig, 2, 4, GLU>), grid, dim3(512), 0, s, p);
+    if constexpr (FMT == FMT_BF16) {
+        if (quarter)
+            hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, GLU>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_bf16_kernel<kBig, kBig, 2, 4, GLU>), grid, dim3(512), 0, s, p);
+    } else {
+        if (quarter)
+            hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 2, GLU>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_kernel<FMT, kBig, kBig, 2, 4, GLU>), grid, dim3(512), 0, s, p);
+    }
     return hipGetLastError();
 }
 
