@@ -519,9 +519,11 @@ hipError_t try_stream(const GemvParams &p, hipStream_t s, bool *taken) {
     const int P = stream_ring(steps);
     // bytes of every buffer descriptor (x and one row) stay far below 2^31
     *taken = (int64_t)T * p.n_in * 4 < (1ll << 31);
-    // rows per wave: enough weight bytes per workgroup next to its copy of x
-    // (with GLU at least one gate/up pair)
-    constexpr int R0 = (FMT == FMT_Q4) ? 4 : (FMT == FMT_Q8) ? 2 : 1;
+    // rows per wave: Q4 rows are short, so 4 give a workgroup enough weight
+    // bytes next to its copy of x; bf16 and Q8 take one (Q8 gate/up shape
+    // under graph replay: 28.0 us with one row per wave, 28.7 with two;
+    // four were ~25 % slower) -- with GLU at least one gate/up pair
+    constexpr int R0 = (FMT == FMT_Q4) ? 4 : 1;
     constexpr int R = GLU && R0 < 2 ? 2 : R0;
     if (P == 8 && *taken && stream_lds_bytes<FMT, 8>(T, p.n_in) <= kStreamMaxLds)
         return launch_stream<FMT, T, R, 8, GLU>(p, s);

@@ -205,6 +205,32 @@ def test_gemm_full_rounds_and_tail(fmt):
         check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_out {n}")
 
 
+@pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
+def test_gemm_unaligned_outputs(fmt):
+    """Prefill epilogue: 16-byte stores only where a job's y rows are 16-byte
+    aligned.  Job 0's y starts one float into its allocation, job 1 has
+    n_out % 4 == 2, job 2 is aligned; the floats around job 0's y stay
+    untouched."""
+    import torch
+    g = np.random.default_rng(1750 + fmt)
+    t, n_in = 600, 64  # 3 x 89 tiles: a round of 256 x 256 tiles and quarters
+    n_outs = [22001, 258, 64]
+    say(f"[gemm unaligned] fmt={FMT_NAME[fmt]} t={t} n_in={n_in} n_outs={n_outs}")
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    ws = [_rand_weight(fmt, g, n, n_in) for n in n_outs]
+    hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
+    buf = torch.full((t * n_outs[0] + 2,), 7.0, dtype=torch.float32, device="cuda")
+    ys = [buf[1:1 + t * n_outs[0]].view(t, n_outs[0])]
+    ys += [torch.full((t, n), float("nan"), dtype=torch.float32, device="cuda") for n in n_outs[1:]]
+    xd = torch.from_numpy(x).cuda()
+    assert il.il_matmul(xd, t, n_in, [(h, n, y) for h, n, y in zip(hs, n_outs, ys)]) == 1, il.il_last_error()
+    torch.cuda.synchronize()
+    edge = buf[[0, -1]].cpu().numpy()
+    assert np.all(edge == 7.0), f"wrote outside y: {edge}"
+    for w, n, y in zip(ws, n_outs, ys):
+        check_full(y.cpu().numpy(), x, w, fmt, n, what=f"fmt {fmt} n_out {n}")
+
+
 # ----------------------------------------------------- closed forms on GPU
 def _onehot(fmt, n_out, n_in, cols):
     if fmt == BF16:
