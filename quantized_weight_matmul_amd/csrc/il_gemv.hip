@@ -509,8 +509,12 @@ hipError_t launch_stream(const GemvParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Ring depth for a row of `steps` 16-byte lane loads.
-inline int stream_ring(int steps) { return steps >= 5 ? 8 : steps >= 3 ? 4 : 2; }
+// Ring depth for a row of `steps` 16-byte lane loads: 4 where it divides the
+// steps, else 2 (rows are padded to whole rings with zero reads).  Measured
+// under graph replay: the fused bf16 decode (8 steps) 11.0 us with 8 loads in
+// flight per row, 10.4 with 4, 11.6 with 2; the Q8 down projection (14
+// steps) 16.5 us with 8, 15.8 with 2.
+inline int stream_ring(int steps) { return steps % 4 == 0 ? 4 : 2; }
 
 template <int FMT, int T, bool GLU = false>
 hipError_t try_stream(const GemvParams &p, hipStream_t s, bool *taken) {
@@ -525,8 +529,6 @@ hipError_t try_stream(const GemvParams &p, hipStream_t s, bool *taken) {
     // four were ~25 % slower) -- with GLU at least one gate/up pair
     constexpr int R0 = (FMT == FMT_Q4) ? 4 : 1;
     constexpr int R = GLU && R0 < 2 ? 2 : R0;
-    if (P == 8 && *taken && stream_lds_bytes<FMT, 8>(T, p.n_in) <= kStreamMaxLds)
-        return launch_stream<FMT, T, R, 8, GLU>(p, s);
     if (P == 4 && *taken && stream_lds_bytes<FMT, 4>(T, p.n_in) <= kStreamMaxLds)
         return launch_stream<FMT, T, R, 4, GLU>(p, s);
     if (P == 2 && *taken && stream_lds_bytes<FMT, 2>(T, p.n_in) <= kStreamMaxLds)
