@@ -179,14 +179,19 @@ struct Planes {
     void *alloc = nullptr;
     char *codes = nullptr, *scales = nullptr, *scales_t = nullptr;
     int64_t tiled_bytes = 0;
+    int64_t code_bytes = 0;
 };
+
+// A Q4 code plane has padding (zero bytes the kernels may read) unless its
+// rows fill whole 16-row tiles and its blocks whole 64-byte segments.
+bool q4_padded(int64_t n_out, int64_t n_in) { return n_out % 16 != 0 || (n_in / il::kBlock) % 4 != 0; }
 
 bool alloc_planes(const char *who, int fmt, int64_t n_out, int64_t n_in, Planes *pl) {
     const int64_t nb = n_in / il::kBlock;
     int64_t code_bytes = 0, scale_size = 0;
     if (fmt == IL_BF16) code_bytes = 2 * n_out * n_in;
     if (fmt == IL_Q8) code_bytes = n_out * n_in, scale_size = 4;
-    if (fmt == IL_Q4) code_bytes = n_out * n_in / 2, scale_size = 2;
+    if (fmt == IL_Q4) code_bytes = il::q4_plane_bytes(n_out, nb), scale_size = 2;
     const int64_t scale_bytes = scale_size * n_out * nb;
     pl->tiled_bytes = scale_size * il::tiled_scale_count(n_out, nb);
     const int64_t code_alloc = (code_bytes + 255) / 256 * 256;
@@ -199,6 +204,7 @@ bool alloc_planes(const char *who, int fmt, int64_t n_out, int64_t n_in, Planes 
         return false;
     }
     pl->codes = static_cast<char *>(pl->alloc);
+    pl->code_bytes = code_bytes;
     pl->scales = scale_bytes ? pl->codes + code_alloc : nullptr;
     pl->scales_t = scale_bytes ? pl->codes + code_alloc + scale_alloc : nullptr;
     return true;
@@ -280,8 +286,10 @@ il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in) {
     } else {
         e = hipMalloc(&staging, (size_t)hb);
         if (e == hipSuccess) e = hipMemcpyAsync(staging, weight, (size_t)hb, hipMemcpyHostToDevice, s);
-        // the tiled plane's padding (rows past n_out, blocks past nb) reads zero
+        // the tiled planes' padding (rows past n_out, blocks past nb) reads zero
         if (e == hipSuccess) e = hipMemsetAsync(scales_t, 0, (size_t)tiled_bytes, s);
+        if (e == hipSuccess && fmt == IL_Q4 && q4_padded(n_out, n_in))
+            e = hipMemsetAsync(codes, 0, (size_t)pl.code_bytes, s);
         if (e == hipSuccess && fmt == IL_Q8)
             e = il::launch_repack_q8(static_cast<const uint8_t *>(staging), reinterpret_cast<int8_t *>(codes),
                                      reinterpret_cast<float *>(scales), reinterpret_cast<float *>(scales_t), n_out,
@@ -343,8 +351,10 @@ il_weight *il_upload_quantize(const void *weight, int src, int fmt, int64_t n_ou
         e = hipMalloc(&staging, (size_t)src_bytes);
         if (e == hipSuccess) e = hipMemcpyAsync(staging, weight, (size_t)src_bytes, hipMemcpyHostToDevice, s);
     }
-    // the tiled plane's padding (rows past n_out, blocks past nb) reads zero
+    // the tiled planes' padding (rows past n_out, blocks past nb) reads zero
     if (e == hipSuccess) e = hipMemsetAsync(pl.scales_t, 0, (size_t)pl.tiled_bytes, s);
+    if (e == hipSuccess && fmt == IL_Q4 && q4_padded(n_out, n_in))
+        e = hipMemsetAsync(pl.codes, 0, (size_t)pl.code_bytes, s);
     const bool timing = timing_on();
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     if (timing) {

@@ -176,8 +176,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
             sc = make_rsrc(static_cast<const float *>(k.scales) + (int64_t)n0 * nb,
                            (uint32_t)b_rows * (uint32_t)nb * 4u);
         } else {
-            c = make_rsrc(static_cast<const uint8_t *>(k.codes) + (int64_t)n0 * (n_in / 2),
-                          (uint32_t)b_rows * (uint32_t)(n_in / 2));
+            // tile-major plane; n0 is a multiple of 16, so the tile's rows
+            // start at a 16-row tile of the plane
+            c = make_rsrc(static_cast<const uint8_t *>(k.codes) + (n0 >> 4) * q4_plane_bytes(16, nb),
+                          (uint32_t)q4_plane_bytes(b_rows, nb));
             sc = make_rsrc(static_cast<const uint16_t *>(k.scales) + (int64_t)n0 * nb,
                            (uint32_t)b_rows * (uint32_t)nb * 2u);
         }
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
                 ssc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                     srs, ok ? ((uint32_t)wr * nb + kh / kBlock) * 4u : kOut, 0, 0));
             } else {
-                sb[0] = bload16(crs, ok ? (uint32_t)wr * (uint32_t)(n_in / 2) + (uint32_t)(kh / 2) : kOut);
+                sb[0] = bload16(crs, ok && wr < b_rows ? (uint32_t)q4_block_offset(wr, kh / kBlock, nb) : kOut);
                 const uint16_t bits = __builtin_amdgcn_raw_buffer_load_b16(
                     srs, ok ? ((uint32_t)wr * nb + kh / kBlock) * 2u : kOut, 0, 0);
                 ssc = (float)__builtin_bit_cast(_Float16, bits) * 0.0625f;  // values carry *16

@@ -67,7 +67,7 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Byte offset of element k within a code row.
+// Byte offset of element k within a bf16 / Q8 code row.
 template <int FMT>
 __device__ __forceinline__ int64_t code_byte(int64_t k) {
     if constexpr (FMT == FMT_BF16) return 2 * k;
@@ -78,6 +78,15 @@ __device__ __forceinline__ int64_t code_byte(int64_t k) {
 template <int FMT>
 __device__ __forceinline__ int64_t row_bytes(int64_t n_in) {
     return code_byte<FMT>(n_in);
+}
+
+// Byte offset of the 16 bytes a lane fetches at element k (a multiple of the
+// lane's elements) of row `local` of a job: row-major for bf16 / Q8, the
+// tile-major block place for Q4.
+template <int FMT>
+__device__ __forceinline__ int64_t code_offset(int64_t local, int64_t k, int64_t n_in) {
+    if constexpr (FMT == FMT_Q4) return q4_block_offset(local, k / kBlock, n_in / kBlock);
+    else return local * row_bytes<FMT>(n_in) + code_byte<FMT>(k);
 }
 
 // Element j (0 <= j < 4) of 4-element group g of a 16-byte weight vector, as
@@ -141,7 +150,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
 
     for (int group = blockIdx.x; group < n_groups; group += gridDim.x) {
         // ---- this wave's rows: (job, local row) and base pointers ----
-        const uint8_t *crow[R];
+        const uint8_t *crow[R];  // the job's code plane
+        int lrow[R];             // row within the job
         const void *srow[R];
         float *yrow[R];
         int ystride[R];
@@ -155,7 +165,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
             for (int q = 1; q < kMaxJobs; ++q)
                 if (q < p.n_jobs && g >= p.row0[q]) j = q;
             int local = valid[r] ? g - p.row0[j] : 0;
-            crow[r] = static_cast<const uint8_t *>(p.job[j].codes) + (int64_t)local * row_bytes<FMT>(n_in);
+            crow[r] = static_cast<const uint8_t *>(p.job[j].codes);
+            lrow[r] = local;
             srow[r] = p.job[j].scales;
             if constexpr (FMT == FMT_Q8)
                 srow[r] = static_cast<const float *>(p.job[j].scales) + (int64_t)local * (n_in / kBlock);
@@ -200,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
             for (int r = 0; r < R; ++r) {
                 int k = k0 + lane * E;
                 bool act = valid[r] && (lane * E < klen);
-                wv[r] = act ? *reinterpret_cast<const uint4 *>(crow[r] + code_byte<FMT>(k))
+                wv[r] = act ? *reinterpret_cast<const uint4 *>(crow[r] + code_offset<FMT>(lrow[r], k, n_in))
                             : make_uint4(0, 0, 0, 0);
             }
             for (int s = 0; s < steps; ++s) {
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
                 for (int r = 0; r < R; ++r) {
                     int kn = kl + STEP;
                     bool a2 = valid[r] && (kn < klen);
-                    nv[r] = a2 ? *reinterpret_cast<const uint4 *>(crow[r] + code_byte<FMT>(k0 + kn))
+                    nv[r] = a2 ? *reinterpret_cast<const uint4 *>(crow[r] + code_offset<FMT>(lrow[r], k0 + kn, n_in))
                                : make_uint4(0, 0, 0, 0);
                 }
                 if (act) {
@@ -373,6 +384,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvParams 
     float *yrow[R];
     int ystride[R];
     bool valid[R];
+    uint32_t rsub[R];  // Q4: the row's 64-byte slot within a segment
     const int row_base = ((int)blockIdx.x * kStreamWaves + wave) * RO;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -385,8 +397,17 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvParams 
                 if (q < p.n_jobs && g >= p.row0[q]) j = q;
         }
         const int local = valid[r] ? g - p.row0[j] : 0;
-        const uint32_t rb = valid[r] ? (uint32_t)row_bytes<FMT>(n_in) : 0u;
-        crs[r] = make_rsrc(static_cast<const uint8_t *>(p.job[j].codes) + (int64_t)local * row_bytes<FMT>(n_in), rb);
+        if constexpr (FMT == FMT_Q4) {
+            // the row's 16-row tile; its segments sit 1 KiB apart
+            const int64_t tb = q4_plane_bytes(16, nb);
+            crs[r] = make_rsrc(static_cast<const uint8_t *>(p.job[j].codes) + (int64_t)(local >> 4) * tb,
+                               valid[r] ? (uint32_t)tb : 0u);
+            rsub[r] = (uint32_t)(local & 15) << 6;
+        } else {
+            const uint32_t rb = valid[r] ? (uint32_t)row_bytes<FMT>(n_in) : 0u;
+            crs[r] = make_rsrc(static_cast<const uint8_t *>(p.job[j].codes) + (int64_t)local * row_bytes<FMT>(n_in),
+                               rb);
+        }
         if constexpr (FMT == FMT_Q8)
             srs[r] = make_rsrc(static_cast<const float *>(p.job[j].scales) + (int64_t)local * nb,
                                valid[r] ? (uint32_t)(nb * 4) : 0u);
@@ -405,9 +426,14 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_kernel(GemvParams 
     auto issue = [&](int u, int s) {
         const int k = s * STEP + lane * E;  // reads at k >= n_in return zeros
         const uint32_t off = (uint32_t)code_byte<FMT>(k);
+        const int blk = k / kBlock;  // Q4: one block per lane
+        const uint32_t qoff = ((uint32_t)(blk >> 2) << 10) + ((uint32_t)(blk & 3) << 4);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            buf[u][r] = buf_load16(crs[r], off);
+            if constexpr (FMT == FMT_Q4)
+                buf[u][r] = buf_load16(crs[r], blk < nb ? qoff + rsub[r] : 0x7FFFFFF0u);
+            else
+                buf[u][r] = buf_load16(crs[r], off);
             if constexpr (FMT != FMT_BF16) sbuf[u][r] = buf_scale<FMT>(srs[r], (uint32_t)(k / kBlock));
         }
     };

@@ -317,10 +317,11 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         ic_nout = jb.n_out;
         const int64_t rows = ic.cnt > 0 ? jb.n_out : 0;
         const uint32_t sbytes = (uint32_t)(tiled_scale_count(rows, nb) * (FMT == FMT_Q8 ? 4 : 2));
-        crs = make_rsrc(jb.codes, (uint32_t)(rows * row_bytes));
+        const uint32_t cbytes = (uint32_t)(FMT == FMT_Q4 ? q4_plane_bytes(rows, nb) : rows * row_bytes);
+        crs = make_rsrc(jb.codes, cbytes);
         srs = make_rsrc(jb.scales_t, sbytes);
         if constexpr (GLU) {
-            crs2 = make_rsrc(p.job[1].codes, (uint32_t)(rows * row_bytes));
+            crs2 = make_rsrc(p.job[1].codes, cbytes);
             srs2 = make_rsrc(p.job[1].scales_t, sbytes);
         }
     };
@@ -356,7 +357,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         const int row = ic.lrow0 + kTile * rt + n;
         const bool row_ok = rt < ic.cnt && row < ic_nout;
         const bool ok = row_ok && (int64_t)kb * 16 < row_bytes;
-        wc[r] = bload16(wrs, ok ? (uint32_t)(row * row_bytes + kb * 16) : kOut);
+        // Q4: the tile's 16 rows x 64 bytes of this step are one 1 KiB run
+        const int64_t woff = FMT == FMT_Q4 ? q4_block_offset(row, kb, nb) : row * row_bytes + kb * 16;
+        wc[r] = bload16(wrs, ok ? (uint32_t)woff : kOut);
         // scales from the tiled plane: a tile's 16 rows x 4 blocks are one run
         if constexpr (FMT == FMT_Q4) {
             // the run of 4 scales of this lane's row (n) for blocks 4s..4s+3
@@ -542,10 +545,11 @@ namespace {
 // every buffer offset a lane forms stays below 2^31
 bool mfma_fits(int fmt, int64_t x_bytes, int n_in, const KJob *jobs, int n_jobs) {
     if (n_in <= 0 || n_in % kBlock || x_bytes >= (1ll << 31) || n_jobs < 1 || n_jobs > kMaxJobs) return false;
-    const int64_t rb = fmt == FMT_BF16 ? 2ll * n_in : fmt == FMT_Q8 ? (int64_t)n_in : n_in / 2;
+    const int64_t rb = fmt == FMT_BF16 ? 2ll * n_in : (int64_t)n_in;
     const int64_t sb = fmt == FMT_Q8 ? 4 : 2;
     for (int j = 0; j < n_jobs; ++j)
-        if ((int64_t)jobs[j].n_out * rb >= (1ll << 31) ||
+        if ((fmt == FMT_Q4 ? q4_plane_bytes(jobs[j].n_out, n_in / kBlock) : (int64_t)jobs[j].n_out * rb) >=
+                (1ll << 31) ||
             tiled_scale_count(jobs[j].n_out, n_in / kBlock) * sb >= (1ll << 31))
             return false;
     return true;

@@ -4,13 +4,18 @@
 //   BF16 : codes  = uint16 [n_out][n_in]          (the host layout, row-major)
 //   Q8   : codes  = int8   [n_out][n_in]          (row-major, K contiguous)
 //          scales = float  [n_out][n_in/32]
-//   Q4   : codes  = uint8  [n_out][n_in/2]        (element 2j in the low nibble
-//                                                  of byte j, stored as
-//                                                  code ^ 8, i.e. the 4-bit
-//                                                  two's complement of code-8)
+//   Q4   : codes  = uint8, tile-major: tiles of 16 rows, each a run of
+//                  64-byte segments per row (128 elements, 4 blocks):
+//                  block b of row r (16 bytes) at q4_block_offset(r, b, nb);
+//                  element 2j of a block in the low nibble of its byte j,
+//                  stored as code ^ 8, i.e. the 4-bit two's complement of
+//                  code - 8; rows padded to 16 and blocks to 4 with zero
+//                  bytes (= code 8, value 0)
 //          scales = uint16 [n_out][n_in/32]       (f16 bits)
-// Every code row starts 16-byte aligned (n_in % 32 == 0), so one lane can
-// fetch 16 bytes of a row with a single global_load_dwordx4.
+// Every bf16 / Q8 code row starts 16-byte aligned (n_in % 32 == 0), so one
+// lane can fetch 16 bytes of a row with a single global_load_dwordx4.  A Q4
+// tile's 16 rows x 64 bytes of one segment are one contiguous 1 KiB: the
+// matrix-core decode kernel's wave fetches it with one instruction.
 // Q8/Q4 also keep a second copy of the scales in tiles of 16 rows x 4 blocks
 // (the order the matrix-core decode kernel reads them in, one 128- or
 // 256-byte run per tile and step):
@@ -48,6 +53,15 @@ __host__ __device__ inline int64_t tiled_scale_index(int64_t row, int64_t b, int
 }
 __host__ __device__ inline int64_t tiled_scale_count(int64_t n_out, int64_t nb) {
     return (n_out + 15) / 16 * ((nb + 3) / 4) * 64;
+}
+
+// Byte offset of Q4 block b of row r (16 bytes) in the tile-major code plane,
+// and the plane's size (nb = blocks per row).
+__host__ __device__ inline int64_t q4_block_offset(int64_t r, int64_t b, int64_t nb) {
+    return (((r >> 4) * ((nb + 3) >> 2) + (b >> 2)) << 10) + ((r & 15) << 6) + ((b & 3) << 4);
+}
+__host__ __device__ inline int64_t q4_plane_bytes(int64_t n_out, int64_t nb) {
+    return (n_out + 15) / 16 * ((nb + 3) / 4) * 1024;
 }
 
 // GELU(v) = v * Phi(v) = 0.5 v (1 + erf(v / sqrt 2)), the activation of the

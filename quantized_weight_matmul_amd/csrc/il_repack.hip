@@ -2,9 +2,9 @@
 // 0.0.0 src/gpu.rs page: "prepares device-side state for a weight matrix").
 //
 // The host bytes are first copied to a device staging buffer; these kernels
-// then split the packed array-of-blocks formats into a K-contiguous code plane
-// and a separate scale plane, plus a tiled copy of the scales (layouts in
-// il_internal.h).  Integer byte moves only: every value is preserved bit for
+// then split the packed array-of-blocks formats into a code plane (Q8 row-major,
+// Q4 tile-major) and a separate scale plane, plus a tiled copy of the scales
+// (layouts in il_internal.h).  Integer byte moves only: every value is preserved bit for
 // bit.  BF16 needs no kernel, its host layout is already the device layout.
 // Also here: the quantiser that builds the Q8 / Q4 planes from f32 or bf16
 // weights on upload, and the inverse repack that writes a weight back in its
@@ -35,9 +35,10 @@ __global__ void repack_q8_kernel(const uint32_t *__restrict__ staging,
 // One thread per 18-byte Q4 block {u16 f16 scale; u8 qs[16]}.  Blocks start
 // 2-byte aligned, so the block is read as 9 halfwords.  Each nibble is stored
 // XOR 8 (two's complement of code - 8), which lets the kernels sign-extend it
-// with one byte-select conversion.
+// with one byte-select conversion; the 16 code bytes go to the block's place
+// in the tile-major plane.
 __global__ void repack_q4_kernel(const uint16_t *__restrict__ staging,
-                                 uint4 *__restrict__ codes, uint16_t *__restrict__ scales,
+                                 uint8_t *__restrict__ codes, uint16_t *__restrict__ scales,
                                  uint16_t *__restrict__ scales_t, int64_t n_blocks, int64_t nb) {
     int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= n_blocks) return;
@@ -51,7 +52,7 @@ __global__ void repack_q4_kernel(const uint16_t *__restrict__ staging,
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         w[i] = ((uint32_t)h[1 + 2 * i] | ((uint32_t)h[2 + 2 * i] << 16)) ^ 0x88888888u;
-    codes[b] = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4 *>(codes + q4_block_offset(b / nb, b % nb, nb)) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // ---- quantise on upload: full-precision weights -> the Q8 / Q4 planes ----
@@ -117,9 +118,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
             if (s != 0.f) q = fminf(fmaxf(rintf(v[i] / s), -8.f), 7.f);
             nib |= ((uint32_t)(int)q & 0xFu) << (4 * i);
         }
-        // elements 4 part + i sit in bytes 2 part (i < 2) and 2 part + 1,
-        // element 2j in the low nibble of byte j
-        *reinterpret_cast<uint16_t *>(codes + e0 / 2) = (uint16_t)nib;
+        // elements 4 part + i sit in bytes 2 part (i < 2) and 2 part + 1 of
+        // the block, element 2j in the low nibble of byte j
+        *reinterpret_cast<uint16_t *>(codes + q4_block_offset(row, blk, nb) + 2 * part) = (uint16_t)nib;
         if (part == 0) {
             static_cast<uint16_t *>(scales)[b] = sb;
             static_cast<uint16_t *>(scales_t)[ti] = sb;
@@ -140,11 +141,11 @@ __global__ void unrepack_q8_kernel(const uint4 *__restrict__ codes, const float 
     dst[5] = c1.x, dst[6] = c1.y, dst[7] = c1.z, dst[8] = c1.w;
 }
 
-__global__ void unrepack_q4_kernel(const uint4 *__restrict__ codes, const uint16_t *__restrict__ scales,
-                                   uint16_t *__restrict__ out, int64_t n_blocks) {
+__global__ void unrepack_q4_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                                   uint16_t *__restrict__ out, int64_t n_blocks, int64_t nb) {
     int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= n_blocks) return;
-    const uint4 c = codes[b];
+    const uint4 c = *reinterpret_cast<const uint4 *>(codes + q4_block_offset(b / nb, b % nb, nb));
     const uint32_t w[4] = {c.x ^ 0x88888888u, c.y ^ 0x88888888u, c.z ^ 0x88888888u, c.w ^ 0x88888888u};
     uint16_t *dst = out + b * 9;
     dst[0] = scales[b];
@@ -184,8 +185,9 @@ hipError_t launch_unrepack(int fmt, const void *codes, const void *scales, uint8
         hipLaunchKernelGGL(unrepack_q8_kernel, g, t, 0, s, static_cast<const uint4 *>(codes),
                            static_cast<const float *>(scales), reinterpret_cast<uint32_t *>(out), n_blocks);
     else if (fmt == FMT_Q4)
-        hipLaunchKernelGGL(unrepack_q4_kernel, g, t, 0, s, static_cast<const uint4 *>(codes),
-                           static_cast<const uint16_t *>(scales), reinterpret_cast<uint16_t *>(out), n_blocks);
+        hipLaunchKernelGGL(unrepack_q4_kernel, g, t, 0, s, static_cast<const uint8_t *>(codes),
+                           static_cast<const uint16_t *>(scales), reinterpret_cast<uint16_t *>(out), n_blocks,
+                           n_in / kBlock);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -206,8 +208,8 @@ hipError_t launch_repack_q4(const uint8_t *staging, uint8_t *codes, uint16_t *sc
     const int64_t n_blocks = n_out * (n_in / kBlock);
     const int64_t grid = (n_blocks + 255) / 256;
     hipLaunchKernelGGL(repack_q4_kernel, dim3((unsigned)grid), dim3(256), 0, s,
-                       reinterpret_cast<const uint16_t *>(staging), reinterpret_cast<uint4 *>(codes), scales,
-                       scales_t, n_blocks, n_in / kBlock);
+                       reinterpret_cast<const uint16_t *>(staging), codes, scales, scales_t, n_blocks,
+                       n_in / kBlock);
     return hipGetLastError();
 }
 
