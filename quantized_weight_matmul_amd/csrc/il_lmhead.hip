@@ -18,23 +18,19 @@
 // an LDS histogram of the keys that still match, then the byte whose bin
 // holds the k-th; then every logit above it and the lowest-index ties at it,
 // placed by prefix sums; then a bitonic sort of those k into visiting
-// order), takes its own cluster and scores its `per` tokens, one wave per
-// token dot, 16 tokens' rows in flight at a time, keeping the first maximum
-// -- then final_kernel, one wave per row, which takes the first maximum over
-// the k clusters in visiting order.  The histogram counts are the only
-// atomics and integer: results are deterministic.
+// order, in one wave's registers when k <= 64), takes its own cluster and
+// scores its `per` tokens, each wave 16 at a time (their ordering entries,
+// then their rows, fetched together; the 16 partial dots reduced by a
+// transposed butterfly), keeping the first maximum -- then final_kernel,
+// one wave per row, which takes the first maximum over the k clusters in
+// visiting order.  The histogram counts are the only atomics and integer:
+// results are deterministic.
 #include "il_internal.h"
 
 namespace il {
 namespace {
 
 constexpr int kSelThreads = 512;
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
 
 // (a before b) in visiting order: larger logit first, equal logits by index.
 __device__ __forceinline__ bool before(float va, int ia, float vb, int ib) {
@@ -59,7 +55,7 @@ struct LmParams {  // (n_pow2: the next power of two >= k, the size of the final
     int h, n_c, n_pow2, per, k, vocab;
 };
 
-// (v, i) of the lane at `src` (wave-uniform).
+// v of the lane at `src` (wave-uniform).
 __device__ __forceinline__ int read_lane(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
 __global__ __launch_bounds__(kSelThreads) void select_score_kernel(LmParams p) {
