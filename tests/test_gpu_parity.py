@@ -120,6 +120,26 @@ def test_odd_shapes(fmt, t, path, monkeypatch):
             check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_in {n_in} n_out {n}")
 
 
+@pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+@pytest.mark.parametrize("t,n_in", [(1, 41024), (3, 13664), (8, 5152)])
+def test_x_past_the_lds_limit(fmt, path, t, n_in, monkeypatch):
+    """t * n_in * 4 bytes of x just past one workgroup's 160 KiB of LDS: the
+    streaming kernel declines, and the decode runs on the kernel that stages
+    x in K chunks (or on the matrix-core kernel, which keeps x in registers)."""
+    _pin(monkeypatch, path)
+    g = np.random.default_rng(1900 + 7 * t + fmt)
+    n_outs = [65, 300]
+    say(f"[lds limit] fmt={FMT_NAME[fmt]} path={path} t={t} n_in={n_in} n_outs={n_outs}")
+    assert t * n_in * 4 > 160 * 1024
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    ws = [_rand_weight(fmt, g, n, n_in) for n in n_outs]
+    hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
+    ys = run(x, hs, n_outs)
+    for w, n, y in zip(ws, n_outs, ys):
+        check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_in {n_in} n_out {n}")
+
+
 def test_mixed_formats_one_call():
     g = np.random.default_rng(5)
     n_in = 256
