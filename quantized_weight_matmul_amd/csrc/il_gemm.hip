@@ -561,13 +561,18 @@ hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *job
 
     // mid-size t: the matrix-core decode kernel's wide mode, which rounds x
     // itself up to kWideF32MaxT tokens and reads the bf16 copy made below
-    // beyond (IL_PREFILL=gemm|verify pins the kernel)
-    bool verify = t <= kVerifyMaxT;
+    // beyond.  Q4 weights take it up to kVerifySliceMaxT tokens, as even
+    // slices of at most kVerifyMaxT (the Q4 GEMM tiles are dequantised by
+    // few waves and measured ~220 us per call on 2 x [17408, 5120] from
+    // t = 33 to 128).  IL_PREFILL=gemm|verify pins the kernel.
+    bool verify = t <= kVerifyMaxT || (fmt == FMT_Q4 && t <= kVerifySliceMaxT);
     if (const char *force = getenv("IL_PREFILL")) {
         if (!strcmp(force, "gemm")) verify = false;
-        if (!strcmp(force, "verify")) verify = true;
+        if (!strcmp(force, "verify")) verify = t <= kVerifySliceMaxT;
     }
-    verify = verify && verify_mfma_fits(fmt, t, n_in, jobs, n_jobs);
+    const int n_slices = (t + kVerifyMaxT - 1) / kVerifyMaxT;
+    const int slice = (t + n_slices - 1) / n_slices;  // tokens per slice, > kWideF32MaxT when t > kVerifyMaxT
+    verify = verify && verify_mfma_fits(fmt, slice, n_in, jobs, n_jobs);
     if (verify && t <= kWideF32MaxT)
         return launch_verify_mfma(fmt, x, nullptr, t, n_in, jobs, n_jobs, cu_count, s, glu);
 
@@ -581,8 +586,20 @@ hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *job
     e = hipGetLastError();
     if (e == hipSuccess) {
         p.xb = static_cast<const uint16_t *>(xb);
-        if (verify) e = launch_verify_mfma(fmt, x, p.xb, t, n_in, jobs, n_jobs, cu_count, s, glu);
-        else switch (fmt) {
+        if (verify) {
+            // one launch per slice of tokens; slice i's x rows and y rows
+            // start slice * i rows in
+            for (int t0 = 0; t0 < t && e == hipSuccess; t0 += slice) {
+                const int tt = min(slice, t - t0);
+                KJob js[kMaxJobs];
+                for (int j = 0; j < n_jobs; ++j) {
+                    js[j] = jobs[j];
+                    js[j].y = jobs[j].y + (int64_t)t0 * jobs[j].n_out;
+                }
+                e = launch_verify_mfma(fmt, x + (int64_t)t0 * n_in, p.xb + (int64_t)t0 * n_in, tt, n_in, js, n_jobs,
+                                       cu_count, s, glu);
+            }
+        } else switch (fmt) {
             case FMT_BF16: e = glu ? launch_plan<FMT_BF16, true>(p, tiles, cu_count, s)
                                    : launch_plan<FMT_BF16>(p, tiles, cu_count, s); break;
             case FMT_Q8: e = glu ? launch_plan<FMT_Q8, true>(p, tiles, cu_count, s)

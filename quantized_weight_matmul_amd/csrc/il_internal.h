@@ -34,6 +34,7 @@ constexpr int kBlock = 32;     // quantisation block (elements)
 constexpr int kMaxJobs = 8;    // jobs per kernel launch (kernarg table)
 constexpr int kGemvMaxT = 8;   // t <= kGemvMaxT runs the decode kernels
 constexpr int kVerifyMaxT = 32;  // largest t the matrix-core decode kernel takes in wide mode
+constexpr int kVerifySliceMaxT = 128;  // Q4: wide mode in slices of <= kVerifyMaxT tokens up to here
 
 struct Weight {
     int fmt;

@@ -44,7 +44,8 @@ def _hi_lo(a):
 def _paths(t):
     if t <= 8:
         return ("valu", "mfma")
-    return ("verify", "gemm") if t <= 32 else ("gemm",)
+    # the matrix-core wide mode takes up to 128 tokens (in slices of <= 32)
+    return ("verify", "gemm") if t <= 128 else ("gemm",)
 
 
 def _decode_cases(ts):
@@ -190,11 +191,12 @@ def test_mfma_decode_many_tiles(fmt, t, monkeypatch):
 
 
 @pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
-@pytest.mark.parametrize("t", [9, 16, 17, 32])
+@pytest.mark.parametrize("t", [9, 16, 17, 32, 33, 64, 100])
 def test_verify_wide_many_tiles(fmt, t, monkeypatch):
     """Mid-size t on the matrix-core kernel's wide mode: one or two groups of
-    16 tokens per weight operand, several chunks per workgroup, a job
-    boundary inside a workgroup's range and ragged tiles and K."""
+    16 tokens per weight operand (t > 32: slices of at most 32 tokens, one
+    launch each), several chunks per workgroup, a job boundary inside a
+    workgroup's range and ragged tiles and K."""
     _pin(monkeypatch, "verify")
     g = np.random.default_rng(1800 + 10 * t + fmt)
     n_in = 1056
