@@ -205,7 +205,8 @@ class Submission:
 
 
 def _c4(t):
-    return Submission(f"c4_t{t}", 4, t, 5120, 0, 32, (Job(Q4, 17408, 1), Job(Q4, 17408, 2)))
+    # x rows are drawn in order, so every t sees the same first rows
+    return Submission(f"c4_t{t}", 4, t, 5120, 0, 128, (Job(Q4, 17408, 1), Job(Q4, 17408, 2)))
 
 
 SUBMISSIONS = {
@@ -220,8 +221,8 @@ SUBMISSIONS = {
         Submission("c3a", 3, 1, 4096, 0, 1, (Job(Q8, 14336, 1), Job(Q8, 14336, 2))),
         Submission("c3b", 3, 1, 14336, 99, 1, (Job(Q8, 4096, 3),)),
         # 4: Q4 small-batch verify at t = 1, 2, 4, 8 (x rows are shared across t),
-        # and at t = 16, 32 (mid-size verify batches)
-        _c4(1), _c4(2), _c4(4), _c4(8), _c4(16), _c4(32),
+        # and at t = 16, 32, 64, 128 (mid-size verify batches)
+        _c4(1), _c4(2), _c4(4), _c4(8), _c4(16), _c4(32), _c4(64), _c4(128),
         # 5: prefill: two bf16 jobs at t = 2048, a Q4 job on the first 512 rows
         Submission("c5a", 5, 2048, 4096, 0, 2048, (Job(BF16, 4096, 1), Job(BF16, 14336, 2))),
         Submission("c5b", 5, 512, 4096, 0, 2048, (Job(Q4, 14336, 3),)),

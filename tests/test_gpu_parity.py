@@ -80,7 +80,7 @@ def test_workload_full(name):
         say(f"  job {j.tensor_id}: {r['n']} outputs ok, worst |err|/bound = {r['worst']:.2e}")
 
 
-@pytest.mark.parametrize("name", ["c5a", "c5b"])
+@pytest.mark.parametrize("name", ["c4_t64", "c4_t128", "c5a", "c5b"])
 def test_workload_sampled(name):
     sub = wl.SUBMISSIONS[name]
     say(f"[parity] {name}: t={sub.t} n_in={sub.n_in} jobs={[(FMT_NAME[j.fmt], j.n_out) for j in sub.jobs]}")
