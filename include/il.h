@@ -138,10 +138,14 @@ IL_API void il_free(il_weight *w);
  *   jobs    : HOST array of n_jobs job descriptors (read during the call).
  *   hip_stream : hipStream_t to enqueue on (NULL = the null stream).
  * Validates every job first; any invalid job fails the whole call before
- * anything is enqueued (all or nothing).  t <= 8 runs the decode GEMV
- * kernels, t > 8 the MFMA GEMM; all jobs of one format share one kernel
- * launch.  Asynchronous: returns after enqueueing, results are valid once
- * the stream has reached that point.
+ * anything is enqueued (all or nothing).  Paths by t: t <= 8 the decode
+ * GEMV kernels (f32 streaming or matrix-core, by format and t), one launch
+ * per weight format present; 8 < t <= 32 (Q4 weights: <= 128, in even
+ * slices of at most 32 tokens, one launch each) the matrix-core kernel's
+ * wide mode; beyond, the MFMA GEMM (an x -> bf16 pre-pass, then whole
+ * rounds of 256 x 256 tiles and the rest as 128 x 128 tiles).  All jobs of
+ * one format share each launch.  Asynchronous: returns after enqueueing,
+ * results are valid once the stream has reached that point.
  * Returns 1 on success, 0 if nothing was computed (the page's `false`: the
  * caller then runs the whole batch elsewhere).  On a validation failure the
  * y buffers are untouched; if a launch itself fails their contents are
