@@ -19,8 +19,11 @@
 // straight into the LDS stage the MFMAs are not reading (buffer loads with
 // the LDS bit: no staging registers, no LDS write instructions), issued at
 // the start of the step before; two 64 KiB stages, one barrier per step.
-// Q8/Q4 weights (gemm_kernel): the tiles are fetched into registers one step
-// ahead, the codes dequantised there, then written to the idle stage.  Rows
+// Q8/Q4 weights (gemm_kernel): x's tile is copied into LDS the same way;
+// the weight tile is fetched into registers two steps ahead, dequantised
+// there, then written to the idle stage.  With fewer 256 x 256 tiles than
+// compute units, Q8/Q4 run 256 x 128 halves on 8 waves (the other formats
+// and the leftover of whole rounds run 128 x 128 quarters on 4).  Rows
 // of 64 bf16 (8 chunks of 16 bytes) are stored with the chunk index
 // XOR-swizzled by the row, so that the fragment reads (and the staging
 // writes) are free of LDS bank conflicts.  Workgroups are mapped to tiles XCD by XCD
@@ -61,6 +64,7 @@ struct GemmParams {
     int units_per_xcd;  // ceil(n_units / kXcds)
     KJob job[kMaxJobs];
     int tn0[kMaxJobs + 1];  // prefix sums of kBig-column tiles per job
+    int half;               // Q8/Q4 small units: 256 x 128 halves instead of quarters
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -115,6 +119,11 @@ __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float *__restrict_
     xb[i] = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
 }
 
+// Q8/Q4 weights.  x's tile goes from L2 straight into LDS (buffer loads with
+// the LDS bit, issued at the start of the step before); the weight tile is
+// fetched into registers two steps ahead, dequantised, and written to the
+// idle LDS stage after the MFMAs.  Steps end with explicit waits and a
+// fence-free barrier, so the register prefetch stays in flight across it.
 // GLU: jobs 0 and 1 are the gate and up projections.  A tile covers BN / 2
 // output columns; B-tile rows come in groups of 32 alternating between the
 // two weights (virtual row v holds row (v / 64) * 32 + v % 32 of the gate if
@@ -123,23 +132,25 @@ __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float *__restrict_
 // writes GELU(gate) * up from registers.
 template <int FMT, int BM, int BN, int WM, int WN, bool GLU = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
+    static_assert(FMT == FMT_Q8 || FMT == FMT_Q4, "bf16 weights use gemm_bf16_kernel");
     constexpr int kThreads = 64 * WM * WN;
     constexpr int kChunksA = BM * BK / 8 / kThreads;  // 16-byte chunks per thread, A tile
-    constexpr int kChunksB = BN * BK / 8 / kThreads;  // same, bf16 B tile
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 MFMA tiles per wave
-    constexpr bool kQuarter = BM < kBig;
     constexpr int kCols = GLU ? BN / 2 : BN;  // output columns of a tile
     static_assert(!GLU || TN == 2, "GLU pairs the two 32-column tiles of a wave");
-    static_assert(kThreads == 2 * BN, "Q8/Q4 staging: two threads per B row");
-    static_assert(kChunksA >= 1 && kChunksB >= 1 && (kThreads / 8) % 16 == 0, "staging shape");
+    constexpr int TPR = kThreads / BN;  // Q8/Q4 staging threads per B row
+    static_assert(TPR == 2 || TPR == 4, "Q8/Q4 staging: two or four threads per B row");
+    constexpr int EPT = BK / TPR;       // elements of a B row per thread and step
+    constexpr int kSplitM = kBig / BM, kSplitN = (GLU ? kBig / 2 : kBig) / kCols;  // units per big tile
+    static_assert(kChunksA >= 1, "staging shape");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][(BM > BN ? BM : BN) * BK];  // [stage][A|B]
 
     // ---- workgroup -> work unit, XCD by XCD ----
     const int b = blockIdx.x;
     const int unit = (b % kXcds) * p.units_per_xcd + b / kXcds;
     if (unit >= p.n_units) return;
-    const int tile = p.tile_lo + (kQuarter ? unit >> 2 : unit);
-    const int q = kQuarter ? unit & 3 : 0;
+    const int tile = p.tile_lo + unit / (kSplitM * kSplitN);
+    const int q = unit % (kSplitM * kSplitN);
     const int tn_all = tile / p.tiles_m;
     const int tm = tile - tn_all * p.tiles_m;
     int j = 0;
@@ -149,8 +160,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
             if (jj < p.n_jobs && tn_all >= p.tn0[jj]) j = jj;
     }
     const KJob jb = p.job[j];
-    const int m0 = tm * kBig + (q >> 1) * BM;
-    const int n0 = (tn_all - p.tn0[j]) * (GLU ? kBig / 2 : kBig) + (q & 1) * kCols;
+    const int m0 = tm * kBig + (q / kSplitN) * BM;
+    const int n0 = (tn_all - p.tn0[j]) * (GLU ? kBig / 2 : kBig) + (q % kSplitN) * kCols;
     if (m0 >= p.t || n0 >= jb.n_out) return;  // a quarter past the edge of x or W
     const int n_in = p.n_in;
     const int nb = n_in / kBlock;
@@ -167,10 +178,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.xb + (int64_t)m0 * n_in, (uint32_t)a_rows * row2);
     // B descriptors over the tile's weight rows [n0, n0 + b_rows) of job k
     auto b_rsrc = [&](const KJob &k, __amdgpu_buffer_rsrc_t &c, __amdgpu_buffer_rsrc_t &sc) {
-        if constexpr (FMT == FMT_BF16) {
-            c = make_rsrc(static_cast<const uint16_t *>(k.codes) + (int64_t)n0 * n_in, (uint32_t)b_rows * row2);
-            sc = c;
-        } else if constexpr (FMT == FMT_Q8) {
+        if constexpr (FMT == FMT_Q8) {
             c = make_rsrc(static_cast<const int8_t *>(k.codes) + (int64_t)n0 * n_in,
                           (uint32_t)b_rows * (uint32_t)n_in);
             sc = make_rsrc(static_cast<const float *>(k.scales) + (int64_t)n0 * nb,
@@ -189,82 +197,59 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     if constexpr (GLU) b_rsrc(p.job[1], brs2, bss2);
     else brs2 = brs, bss2 = bss;
 
-    // bf16 staging: chunk i of this thread is row crow0 + (threads / 8) i,
-    // 16-byte chunk cc, so 8 consecutive threads read one 128-byte row
-    // segment.  Q8/Q4
-    // staging: this thread owns row tid / 2, elements 32 (tid % 2) .. +31 of
-    // the step (one quantisation block).
-    const int crow0 = tid >> 3, cc = tid & 7;
-    const int cslot = cc ^ swz_key(crow0);  // rows crow0 + (threads / 8) i share the key
-    const int qr = tid >> 1, qh = tid & 1;
+    // weight staging: TPR threads per B row; this thread owns row qr and
+    // elements EPT qh .. EPT qh + EPT - 1 of the step (a quantisation block
+    // or half of one)
+    const int qr = tid / TPR, qh = tid % TPR;
     const int qkey = swz_key(qr);
 
-    uint4 sa[kChunksA];
-    uint4 sb[FMT == FMT_BF16 ? kChunksB : (FMT == FMT_Q8 ? 2 : 1)];
+    uint4 sb[FMT == FMT_Q8 ? EPT / 16 : 1];
     float ssc = 0.f;
     auto fetch = [&](int k0) {
-        const int k = k0 + cc * 8;
-        const bool kok = k < n_in;
-#pragma unroll
-        for (int i = 0; i < kChunksA; ++i)
-            sa[i] = bload16(ars, kok ? (uint32_t)(crow0 + (kThreads / 8) * i) * row2 + (uint32_t)k * 2u : kOut);
-        if constexpr (FMT == FMT_BF16) {
-#pragma unroll
-            for (int i = 0; i < kChunksB; ++i) {
-                const int v = crow0 + (kThreads / 8) * i;  // B-tile row
-                if constexpr (GLU) {
-                    // gate or up: (v / 32) % 2, the same for the whole wave
-                    const bool up = ((wave >> 2) + ((kThreads / 8) * i >> 5)) & 1;
-                    const int wr = (v >> 6) * 32 + (v & 31);
-                    sb[i] = bload16(up ? brs2 : brs, kok ? (uint32_t)wr * row2 + (uint32_t)k * 2u : kOut);
-                } else {
-                    sb[i] = bload16(brs, kok ? (uint32_t)v * row2 + (uint32_t)k * 2u : kOut);
-                }
-            }
-        }
-        if constexpr (FMT != FMT_BF16) {
-            const int kh = k0 + 32 * qh;
+        {
+            const int kh = k0 + EPT * qh;
             const bool ok = kh < n_in;
-            // GLU: B-tile row qr is row wr of the gate (wave even) or up (odd)
-            const bool up = GLU && (wave & 1);
+            // GLU: B-tile row qr is row wr of the gate ((qr / 32) even) or up
+            const bool up = GLU && ((qr >> 5) & 1);
             const int wr = GLU ? (qr >> 6) * 32 + (qr & 31) : qr;
             const __amdgpu_buffer_rsrc_t crs = up ? brs2 : brs, srs = up ? bss2 : bss;
             if constexpr (FMT == FMT_Q8) {
                 const uint32_t off = ok ? (uint32_t)wr * (uint32_t)n_in + (uint32_t)kh : kOut;
-                sb[0] = bload16(crs, off);
-                sb[1] = bload16(crs, ok ? off + 16u : kOut);
+#pragma unroll
+                for (int c = 0; c < EPT / 16; ++c) sb[c] = bload16(crs, ok ? off + 16u * c : kOut);
                 ssc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                     srs, ok ? ((uint32_t)wr * nb + kh / kBlock) * 4u : kOut, 0, 0));
             } else {
-                sb[0] = bload16(crs, ok && wr < b_rows ? (uint32_t)q4_block_offset(wr, kh / kBlock, nb) : kOut);
+                const uint32_t qoff = (uint32_t)q4_block_offset(wr, kh / kBlock, nb) + (uint32_t)((kh % kBlock) / 2);
+                if constexpr (EPT == 32) {
+                    sb[0] = bload16(crs, ok && wr < b_rows ? qoff : kOut);
+                } else {
+                    const uint2 h = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(crs, ok && wr < b_rows ? qoff : kOut, 0, 0));
+                    sb[0] = make_uint4(h.x, h.y, 0u, 0u);
+                }
                 const uint16_t bits = __builtin_amdgcn_raw_buffer_load_b16(
                     srs, ok ? ((uint32_t)wr * nb + kh / kBlock) * 2u : kOut, 0, 0);
                 ssc = (float)__builtin_bit_cast(_Float16, bits) * 0.0625f;  // values carry *16
             }
         }
     };
-    auto store = [&](uint16_t *As, uint16_t *Bs) {
-#pragma unroll
-        for (int i = 0; i < kChunksA; ++i)
-            *reinterpret_cast<uint4 *>(As + (crow0 + (kThreads / 8) * i) * BK + cslot * 8) = sa[i];
-        if constexpr (FMT == FMT_BF16) {
-#pragma unroll
-            for (int i = 0; i < kChunksB; ++i)
-                *reinterpret_cast<uint4 *>(Bs + (crow0 + (kThreads / 8) * i) * BK + cslot * 8) = sb[i];
-        }
-        if constexpr (FMT != FMT_BF16) {
-            uint32_t o[16];
+    auto store = [&](uint16_t *Bs) {
+        {
+            uint32_t o[EPT / 2];
             if constexpr (FMT == FMT_Q8) {
-                const uint32_t w[8] = {sb[0].x, sb[0].y, sb[0].z, sb[0].w, sb[1].x, sb[1].y, sb[1].z, sb[1].w};
+                uint32_t w[EPT / 4];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int c = 0; c < EPT / 16; ++c)
+                    w[4 * c] = sb[c].x, w[4 * c + 1] = sb[c].y, w[4 * c + 2] = sb[c].z, w[4 * c + 3] = sb[c].w;
+#pragma unroll
+                for (int i = 0; i < EPT / 4; ++i) {
                     o[2 * i] = pack_bf16((float)(int8_t)(w[i]) * ssc, (float)(int8_t)(w[i] >> 8) * ssc);
                     o[2 * i + 1] = pack_bf16((float)(int8_t)(w[i] >> 16) * ssc, (float)(int8_t)(w[i] >> 24) * ssc);
                 }
             } else {
                 const uint32_t w[4] = {sb[0].x, sb[0].y, sb[0].z, sb[0].w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < EPT / 8; ++i) {
                     const uint32_t lo = (w[i] << 4) & 0xF0F0F0F0u;  // elements 0, 2, 4, 6 (code ^ 8)
                     const uint32_t hi = w[i] & 0xF0F0F0F0u;         // elements 1, 3, 5, 7
 #pragma unroll
@@ -273,8 +258,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<uint4 *>(Bs + qr * BK + ((4 * qh + i) ^ qkey) * 8) =
+            for (int i = 0; i < EPT / 8; ++i)
+                *reinterpret_cast<uint4 *>(Bs + qr * BK + (((EPT / 8) * qh + i) ^ qkey) * 8) =
                     make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
         }
     };
@@ -310,18 +295,42 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     };
 
     const int nk = (n_in + BK - 1) / BK;
+    uint32_t offa[kChunksA];
+    int ka[kChunksA];
+#pragma unroll
+    for (int i = 0; i < kChunksA; ++i) {
+        const int u = (wave * kChunksA + i) * 64 + lane, r = u >> 3;
+        ka[i] = ((u & 7) ^ swz_key(r)) * 8;
+        offa[i] = (uint32_t)r * row2 + (uint32_t)ka[i] * 2u;
+    }
+    auto issue_a = [&](uint16_t *As, int k0) {
+#pragma unroll
+        for (int i = 0; i < kChunksA; ++i)
+            lds_load16(ars, As + (wave * kChunksA + i) * 64 * 8, k0 + ka[i] < n_in ? offa[i] + (uint32_t)k0 * 2u : kOut);
+    };
+    // B register loads per fetch (codes, then the scale): the waits below let
+    // these, issued after a step's x copy, stay in flight across the barrier
+    constexpr int kBLoads = FMT == FMT_Q8 ? EPT / 16 + 1 : 2;
+    issue_a(lds[0][0], 0);
     fetch(0);
-    store(lds[0][0], lds[0][1]);
-    if (nk > 1) fetch(BK);
-    __syncthreads();
+    store(lds[0][1]);
+    const bool f1 = nk > 1;
+    if (f1) fetch(BK);
+    if (f1) wait_vmcnt<kBLoads>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's LDS writes are done
+    lds_barrier();
     for (int ks = 0; ks < nk; ++ks) {
         const int cur = ks & 1;
+        if (ks + 1 < nk) issue_a(lds[cur ^ 1][0], (ks + 1) * BK);
         compute(lds[cur][0], lds[cur][1]);
+        bool fetched = false;
         if (ks + 1 < nk) {
-            store(lds[cur ^ 1][0], lds[cur ^ 1][1]);  // step ks+1 (its loads were in flight)
-            if (ks + 2 < nk) fetch((ks + 2) * BK);
+            store(lds[cur ^ 1][1]);  // B of step ks + 1 (its loads were in flight)
+            if (ks + 2 < nk) fetch((ks + 2) * BK), fetched = true;
         }
-        __syncthreads();
+        if (fetched) wait_vmcnt<kBLoads>(); else wait_vmcnt<0>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        lds_barrier();
     }
 
     // ---- epilogue: 32x32 tile, lane holds rows 8 (i / 4) + 4 (lane / 32) + i % 4
@@ -515,6 +524,12 @@ hipError_t launch_units(GemmParams p, bool quarter, int tile_lo, int n_units, hi
         else
             hipLaunchKernelGGL((gemm_bf16_kernel<kBig, kBig, 2, 4, GLU>), grid, dim3(512), 0, s, p);
     } else {
+        if constexpr (!GLU) {
+            if (quarter && p.half) {
+                hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 2, 4, false>), grid, dim3(512), 0, s, p);
+                return hipGetLastError();
+            }
+        }
         if (quarter)
             hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 2, GLU>), grid, dim3(256), 0, s, p);
         else
@@ -531,6 +546,19 @@ hipError_t launch_plan(const GemmParams &p, int tiles, int cu_count, hipStream_t
     const int full = tiles >= cu_count ? tiles / cu_count * cu_count : 0;
     hipError_t e = hipSuccess;
     if (full > 0) e = launch_units<FMT, GLU>(p, false, 0, full, s);
+    // Q8/Q4 with fewer big tiles than compute units: 256 x 128 halves on 8
+    // waves (the Q4 prefill's 112 tiles: 224 halves in one round, 92 us,
+    // against 448 quarters in 1.75 rounds, ~101 us) -- whole rounds of them,
+    // and the tiles left over as quarters
+    if (FMT != FMT_BF16 && !GLU && full == 0) {
+        const int halves = 2 * tiles;
+        const int h = halves <= cu_count ? halves : halves / cu_count * cu_count / 2 * 2;
+        GemmParams q = p;
+        q.half = 1;
+        e = launch_units<FMT, GLU>(q, true, 0, h, s);
+        if (e == hipSuccess && h < halves) e = launch_units<FMT, GLU>(p, true, h / 2, 4 * (tiles - h / 2), s);
+        return e;
+    }
     if (e == hipSuccess && tiles > full) e = launch_units<FMT, GLU>(p, true, full, 4 * (tiles - full), s);
     return e;
 }

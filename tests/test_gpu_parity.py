@@ -227,6 +227,23 @@ def test_gemm_full_rounds_and_tail(fmt):
         check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_out {n}")
 
 
+@pytest.mark.parametrize("fmt", [Q8, Q4], ids=lambda f: FMT_NAME[f])
+def test_gemm_halves_and_quarters(fmt):
+    """Quantised prefill with fewer 256 x 256 tiles than compute units:
+    2 x 70 = 140 tiles run as a round of 256 x 128 halves (128 tiles) and the
+    other 12 as 128 x 128 quarters; ragged edges in t and n_out."""
+    g = np.random.default_rng(1760 + fmt)
+    t, n_in = 300, 64
+    n_outs = [17000, 700]
+    say(f"[gemm halves] fmt={FMT_NAME[fmt]} t={t} n_in={n_in} n_outs={n_outs}")
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    ws = [_rand_weight(fmt, g, n, n_in) for n in n_outs]
+    hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
+    ys = run(x, hs, n_outs)
+    for w, n, y in zip(ws, n_outs, ys):
+        check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_out {n}")
+
+
 @pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
 def test_gemm_unaligned_outputs(fmt):
     """Prefill epilogue: 16-byte stores only where a job's y rows are 16-byte
