@@ -270,6 +270,61 @@ def test_gemm_unaligned_outputs(fmt):
         check_full(y.cpu().numpy(), x, w, fmt, n, what=f"fmt {fmt} n_out {n}")
 
 
+def test_concurrent_calls_from_threads():
+    """Host threads share the weight handles and the library's context: each
+    uploads and frees a weight of its own and runs repeated submissions (decode
+    and prefill, all formats) on its own stream; every result equals the
+    single-threaded one bit for bit (the kernels are deterministic)."""
+    import threading
+    import torch
+    g = np.random.default_rng(77)
+    n_in = 512
+    fmts, n_outs = [BF16, Q8, Q4], [3000, 1500, 2200]
+    ws = [_rand_weight(f, g, n, n_in) for f, n in zip(fmts, n_outs)]
+    hs = upload_all(ws, fmts, n_outs, n_in)
+    xs = {t: torch.from_numpy(g.standard_normal((t, n_in)).astype(np.float32)).cuda() for t in (1, 5, 40)}
+    ref = {}
+    for t, x in xs.items():
+        ys = [torch.empty(t, n, device="cuda") for n in n_outs]
+        assert il.il_matmul(x, t, n_in, list(zip(hs, n_outs, ys))) == 1, il.il_last_error()
+        torch.cuda.synchronize()
+        ref[t] = [y.cpu().numpy() for y in ys]
+    n_threads, reps = 8, 10
+    streams = [torch.cuda.Stream() for _ in range(n_threads)]
+    errors = []
+
+    def worker(k):
+        try:
+            extra = il.il_upload(_rand_weight(Q8, np.random.default_rng(k), 64, n_in), Q8, 64, n_in)
+            assert extra is not None, il.il_last_error()
+            out = {}
+            with torch.cuda.stream(streams[k]):
+                for r in range(reps):
+                    for t, x in xs.items():
+                        ys = [torch.empty(t, n, device="cuda") for n in n_outs]
+                        if il.il_matmul(x, t, n_in, list(zip(hs, n_outs, ys)), streams[k]) != 1:
+                            errors.append(f"thread {k}: {il.il_last_error()}")
+                            return
+                        out[(r, t)] = ys
+            streams[k].synchronize()
+            il.il_free(extra)
+            for (r, t), ys in out.items():
+                for j, y in enumerate(ys):
+                    if not np.array_equal(y.cpu().numpy(), ref[t][j]):
+                        errors.append(f"thread {k} rep {r} t {t} job {j} differs")
+        except Exception as e:  # reported below
+            errors.append(f"thread {k}: {e!r}")
+
+    say(f"[threads] {n_threads} threads x {reps} reps x t in {sorted(xs)}")
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(n_threads)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=90)
+    assert not any(th.is_alive() for th in threads), "a worker thread did not finish"
+    assert not errors, errors[:5]
+
+
 # ----------------------------------------------------- closed forms on GPU
 def _onehot(fmt, n_out, n_in, cols):
     if fmt == BF16:
