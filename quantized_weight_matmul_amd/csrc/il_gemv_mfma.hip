@@ -1,5 +1,7 @@
 // il_gemv_mfma.hip -- decode GEMV on the bf16 matrix cores (small t > 1),
-// and its "wide" mode for mid-size t (speculative-verify batches, 8 < t <= 32).
+// and its "wide" mode for mid-size t (speculative-verify batches, 8 < t <= 32
+// per launch; the prefill dispatch runs Q4 weights in slices of up to 32
+// tokens to t = 128).
 //
 // Computes the same sums as the streaming decode kernel,
 //   y[i][r] = sum_b s_rb * sum_{k in block b} (q_rk - z) * x_ik
@@ -37,7 +39,8 @@
 //     tiles.
 //
 // Loads: a wave fetches 16 bytes per lane, 64 bytes of each of 16 rows (one
-// bf16 block, two Q8 blocks or four Q4 blocks per row: one "step").  Lane
+// bf16 block, two Q8 blocks or four Q4 blocks per row: one "step"; for Q4,
+// whose code plane is tile-major, one contiguous KiB).  Lane
 // group g (lanes 16g..16g+15) holds row bytes [16g, 16g + 16) of the step;
 // the MFMA wants lane group g to hold the g-th quarter of each block, which
 // for Q8/Q4 is a 4 x 4 transpose of dwords across the lane groups (two
