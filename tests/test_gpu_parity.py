@@ -156,12 +156,12 @@ def test_mixed_formats_one_call():
             check_full(y, x, w, f, n, what=f"mixed t {t} fmt {f}")
 
 
-@pytest.mark.parametrize("path", ["valu", "mfma"])
-def test_many_jobs_one_call(path, monkeypatch):
-    """More jobs than one launch's job table holds."""
+@pytest.mark.parametrize("t,path", [(2, "valu"), (2, "mfma"), (20, "verify"), (40, "gemm")])
+def test_many_jobs_one_call(t, path, monkeypatch):
+    """More jobs than one launch's job table holds, on every path."""
     _pin(monkeypatch, path)
     g = np.random.default_rng(6)
-    n_in, t = 64, 2
+    n_in = 64
     n_outs = [3 + 5 * i for i in range(19)]
     x = g.standard_normal((t, n_in)).astype(np.float32)
     ws = [_rand_weight(BF16, g, n, n_in) for n in n_outs]
