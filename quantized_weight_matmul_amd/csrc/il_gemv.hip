@@ -542,6 +542,8 @@ hipError_t launch_stream(const GemvParams &p, hipStream_t s) {
 // steps) 16.5 us with 8, 15.8 with 2.
 inline int stream_ring(int steps) { return steps % 4 == 0 ? 4 : 2; }
 
+constexpr int kStreamLongRow = 8192;  // inputs per row from which bf16 / Q8 rows go two per wave
+
 template <int FMT, int T, bool GLU = false>
 hipError_t try_stream(const GemvParams &p, hipStream_t s, bool *taken) {
     constexpr int STEP = 64 * FmtTraits<FMT>::E;
@@ -552,12 +554,24 @@ hipError_t try_stream(const GemvParams &p, hipStream_t s, bool *taken) {
     // rows per wave: Q4 rows are short, so 4 give a workgroup enough weight
     // bytes next to its copy of x; bf16 and Q8 take one (Q8 gate/up shape
     // under graph replay: 28.0 us with one row per wave, 28.7 with two;
-    // four were ~25 % slower) -- with GLU at least one gate/up pair
+    // four were ~25 % slower) -- with GLU at least one gate/up pair.  Rows
+    // of kStreamLongRow inputs or more take two, which halves the copies of
+    // the (long) x per weight row: the Q8 down projection [4096 x 14336]
+    // 15.6 -> 14.95 us; four rows 19.5 us.
     constexpr int R0 = (FMT == FMT_Q4) ? 4 : 1;
     constexpr int R = GLU && R0 < 2 ? 2 : R0;
-    if (P == 4 && *taken && stream_lds_bytes<FMT, 4>(T, p.n_in) <= kStreamMaxLds)
+    if (!*taken) return hipSuccess;
+    if constexpr (R == 1) {
+        if (p.n_in >= kStreamLongRow) {
+            if (P == 4 && stream_lds_bytes<FMT, 4>(T, p.n_in) <= kStreamMaxLds)
+                return launch_stream<FMT, T, 2, 4, GLU>(p, s);
+            if (P == 2 && stream_lds_bytes<FMT, 2>(T, p.n_in) <= kStreamMaxLds)
+                return launch_stream<FMT, T, 2, 2, GLU>(p, s);
+        }
+    }
+    if (P == 4 && stream_lds_bytes<FMT, 4>(T, p.n_in) <= kStreamMaxLds)
         return launch_stream<FMT, T, R, 4, GLU>(p, s);
-    if (P == 2 && *taken && stream_lds_bytes<FMT, 2>(T, p.n_in) <= kStreamMaxLds)
+    if (P == 2 && stream_lds_bytes<FMT, 2>(T, p.n_in) <= kStreamMaxLds)
         return launch_stream<FMT, T, R, 2, GLU>(p, s);
     *taken = false;
     return hipSuccess;

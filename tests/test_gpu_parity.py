@@ -141,6 +141,25 @@ def test_x_past_the_lds_limit(fmt, path, t, n_in, monkeypatch):
         check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_in {n_in} n_out {n}")
 
 
+@pytest.mark.parametrize("fmt", [BF16, Q8], ids=lambda f: FMT_NAME[f])
+@pytest.mark.parametrize("t", [1, 2, 4])
+@pytest.mark.parametrize("n_in", [8160, 8192, 8224, 14336])
+def test_long_rows_two_per_wave(fmt, t, n_in, monkeypatch):
+    """Rows of 8192 inputs or more stream two per wave on the f32 kernel:
+    either side of that threshold, row counts that leave the last
+    workgroup's waves partly or wholly without a row."""
+    _pin(monkeypatch, "valu")
+    g = np.random.default_rng(2300 + 11 * t + fmt + n_in)
+    n_outs = [1, 17, 263]
+    say(f"[long rows] fmt={FMT_NAME[fmt]} t={t} n_in={n_in} n_outs={n_outs}")
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    ws = [_rand_weight(fmt, g, n, n_in) for n in n_outs]
+    hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
+    ys = run(x, hs, n_outs)
+    for w, n, y in zip(ws, n_outs, ys):
+        check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_in {n_in} n_out {n}")
+
+
 def test_mixed_formats_one_call():
     g = np.random.default_rng(5)
     n_in = 256
