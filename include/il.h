@@ -143,7 +143,9 @@ IL_API void il_free(il_weight *w);
  * per weight format present; 8 < t <= 32 (Q4 weights: <= 128, in even
  * slices of at most 32 tokens, one launch each) the matrix-core kernel's
  * wide mode; beyond, the MFMA GEMM (an x -> bf16 pre-pass, then whole
- * rounds of 256 x 256 tiles and the rest as 128 x 128 tiles).  All jobs of
+ * rounds of 256 x 256 tiles and the rest as 128 x 128 tiles; Q8/Q4 with
+ * fewer 256 x 256 tiles than compute units run whole rounds of 256 x 128
+ * halves first).  All jobs of
  * one format share each launch.  Asynchronous: returns after enqueueing,
  * results are valid once the stream has reached that point.
  * Returns 1 on success, 0 if nothing was computed (the page's `false`: the
