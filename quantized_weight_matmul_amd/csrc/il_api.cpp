@@ -522,7 +522,9 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
     uint64_t launches = 0, bytes = 0;
     for (int fmt = 0; fmt < 3; ++fmt) {
         std::vector<il::KJob> batch;
+        int64_t batch_rows = 0;  // the kernels count a launch's rows in 32-bit ints
         auto flush = [&]() -> bool {
+            batch_rows = 0;
             if (batch.empty()) return true;
             hipError_t e = decode ? il::launch_gemv(fmt, x, (int)t, (int)n_in, batch.data(),
                                                     (int)batch.size(), ctx->cu_count, s)
@@ -539,7 +541,12 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
         for (int64_t j = 0; j < n_jobs; ++j) {
             const il_weight *w = jobs[j].w;
             if (w->fmt != fmt) continue;
+            if (batch_rows + w->n_out > INT_MAX && !flush()) {  // n_out <= INT_MAX on its own
+                g_failed++;
+                return 0;
+            }
             batch.push_back(il::KJob{w->codes, w->scales, w->scales_t, jobs[j].y, (int)w->n_out});
+            batch_rows += w->n_out;
             bytes += (uint64_t)w->host_bytes;
             if ((int)batch.size() == il::kMaxJobs && !flush()) {
                 g_failed++;
