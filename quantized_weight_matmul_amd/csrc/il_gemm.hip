@@ -18,7 +18,10 @@
 // bf16 weights (gemm_bf16_kernel): each K step's x and W tiles go from L2
 // straight into the LDS stage the MFMAs are not reading (buffer loads with
 // the LDS bit: no staging registers, no LDS write instructions), issued at
-// the start of the step before; two 64 KiB stages, one barrier per step.
+// the start of the step before, on the 256 x 256 tile by four of its eight
+// waves (one per SIMD, so that the other wave there keeps the matrix core
+// busy while the issuing one waits on the load unit); two 64 KiB stages,
+// one barrier per step.
 // Q8/Q4 weights (gemm_kernel): x's tile is copied into LDS the same way;
 // the weight tile is fetched into registers two steps ahead, dequantised
 // there, then written to the idle stage.  With fewer 256 x 256 tiles than
@@ -415,30 +418,42 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(GemmParams p
     // c = slot ^ key(r); GLU: B-tile row v is row (v / 64) 32 + v % 32 of the
     // gate ((v / 32) even) or up projection -- 8-row blocks never straddle
     // a 32-row group, so the choice is uniform per instruction
-    uint32_t offa[kLoadsA], offb[kLoadsB];
-    int ka[kLoadsA], kb[kLoadsB];
+    // Who copies: a wave stalls while the CU's load unit drains the copies it
+    // issues (~850 cycles of a ~3400-cycle K step when all 8 waves issue
+    // theirs at once after the barrier), and its SIMD's matrix core idles
+    // if the other wave there is stalled too.  So on the 8-wave tile only
+    // waves 0..3, one per SIMD, issue the copies (twice as many each) while
+    // waves 4..7 start on their MFMAs: 3459 -> 3159 cycles per K step.
+    constexpr int kIssuers = kQuarter ? WM * WN : 4;
+    constexpr int kLA = kLoadsA * WM * WN / kIssuers, kLB = kLoadsB * WM * WN / kIssuers;
+    static_assert(kLA * kIssuers == kLoadsA * WM * WN && kLB * kIssuers == kLoadsB * WM * WN, "copy split");
+    const bool issuer = wave < kIssuers;
+    const int iw = issuer ? wave : 0;
+    uint32_t offa[kLA], offb[kLB];
+    int ka[kLA], kb[kLB];
 #pragma unroll
-    for (int i = 0; i < kLoadsA; ++i) {
-        const int u = (wave * kLoadsA + i) * 64 + lane, r = u >> 3;
+    for (int i = 0; i < kLA; ++i) {
+        const int u = (iw * kLA + i) * 64 + lane, r = u >> 3;
         ka[i] = ((u & 7) ^ swz_key(r)) * 8;
         offa[i] = (uint32_t)r * row2 + (uint32_t)ka[i] * 2u;
     }
 #pragma unroll
-    for (int i = 0; i < kLoadsB; ++i) {
-        const int u = (wave * kLoadsB + i) * 64 + lane, v = u >> 3;
+    for (int i = 0; i < kLB; ++i) {
+        const int u = (iw * kLB + i) * 64 + lane, v = u >> 3;
         kb[i] = ((u & 7) ^ swz_key(v)) * 8;
         const int wr = GLU ? (v >> 6) * 32 + (v & 31) : v;
         offb[i] = (uint32_t)wr * row2 + (uint32_t)kb[i] * 2u;
     }
     auto issue = [&](int st, int k0) {
+        if (!issuer) return;
         uint16_t *As = lds + st * kStage, *Bs = As + BM * BK;
 #pragma unroll
-        for (int i = 0; i < kLoadsA; ++i)
-            lds_load16(ars, As + (wave * kLoadsA + i) * 64 * 8, k0 + ka[i] < n_in ? offa[i] + (uint32_t)k0 * 2u : kOut);
+        for (int i = 0; i < kLA; ++i)
+            lds_load16(ars, As + (iw * kLA + i) * 64 * 8, k0 + ka[i] < n_in ? offa[i] + (uint32_t)k0 * 2u : kOut);
 #pragma unroll
-        for (int i = 0; i < kLoadsB; ++i) {
-            const bool up = GLU && ((((wave * kLoadsB + i) * 8) >> 5) & 1);
-            lds_load16(up ? brs2 : brs, Bs + (wave * kLoadsB + i) * 64 * 8,
+        for (int i = 0; i < kLB; ++i) {
+            const bool up = GLU && ((((iw * kLB + i) * 8) >> 5) & 1);
+            lds_load16(up ? brs2 : brs, Bs + (iw * kLB + i) * 64 * 8,
                        k0 + kb[i] < n_in ? offb[i] + (uint32_t)k0 * 2u : kOut);
         }
     };
