@@ -352,23 +352,36 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
             }
         }
     };
+    // Q4: a lane's code and scale offsets are a uniform segment index (tile
+    // of the plane * nb4 + step) shifted, plus these per-lane constants
+    const uint32_t q4_code_lane = ((uint32_t)n << 6) + ((uint32_t)g << 4);
+    const uint32_t q4_scale_lane = (uint32_t)n << 3;
     auto issue_w = [&](int r) {
         const int kb = 4 * is + g;  // 16-byte chunk of the row this lane fetches
         const int rt = r % TCh;     // tile of its job
         const bool up = GLU && r >= TCh;
         const __amdgpu_buffer_rsrc_t wrs = up ? crs2 : crs, qrs = up ? srs2 : srs;
+        if constexpr (FMT == FMT_Q4) {
+            // The code plane and the tiled scale plane are padded to whole
+            // 16-row tiles and 4-block segments (zero codes decode to 0,
+            // padded scales are 0), so no lane needs a row or block check:
+            // only whether the chunk has this tile.  The step's segment of
+            // the tile is one 1 KiB run of codes and one 128-byte run of
+            // scales (16 rows x 4 blocks x 2 bytes).
+            const bool ok = rt < ic.cnt;
+            const uint32_t seg = (uint32_t)((ic.lrow0 >> 4) + rt) * (uint32_t)nb4 + (uint32_t)is;
+            wc[r] = bload16(wrs, ok ? (seg << 10) + q4_code_lane : kOut);
+            ws[r] = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_raw_buffer_load_b64(qrs, ok ? (seg << 7) + q4_scale_lane : kOut, 0, 0));
+            return;
+        }
+        // bf16 / Q8: row-major planes, not padded -- per-lane row and block checks
         const int row = ic.lrow0 + kTile * rt + n;
         const bool row_ok = rt < ic.cnt && row < ic_nout;
         const bool ok = row_ok && (int64_t)kb * 16 < row_bytes;
-        // Q4: the tile's 16 rows x 64 bytes of this step are one 1 KiB run
-        const int64_t woff = FMT == FMT_Q4 ? q4_block_offset(row, kb, nb) : row * row_bytes + kb * 16;
-        wc[r] = bload16(wrs, ok ? (uint32_t)woff : kOut);
+        wc[r] = bload16(wrs, ok ? (uint32_t)(row * row_bytes + kb * 16) : kOut);
         // scales from the tiled plane: a tile's 16 rows x 4 blocks are one run
-        if constexpr (FMT == FMT_Q4) {
-            // the run of 4 scales of this lane's row (n) for blocks 4s..4s+3
-            ws[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                qrs, row_ok && 4 * is < nb ? (uint32_t)(tiled_scale_index(row, 4 * is, nb4) * 2) : kOut, 0, 0));
-        } else if constexpr (FMT == FMT_Q8) {
+        if constexpr (FMT == FMT_Q8) {
             // this lane's 16 bytes are half of block 2s + g/2
             const int blk = 2 * is + (g >> 1);
             ws[r] = __builtin_amdgcn_raw_buffer_load_b32(
