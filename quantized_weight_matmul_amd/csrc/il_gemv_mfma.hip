@@ -255,12 +255,6 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     const int n = lane & 15;  // weight row within the tile (B column) = A row
     const int g = lane >> 4;  // lane group: quarter of the K slice
 
-    if constexpr (FMT == FMT_Q4) {
-        // the code table: wave w fills byte values w, w + 8, ..., one column per lane
-#pragma unroll 4
-        for (int i = 0; i < 32; ++i) lut[(8 * i + wave) * 64 + lane] = q4_pair_bf16(8 * i + wave);
-        __syncthreads();
-    }
     const int t = p.t, nb = p.nb, n_in = p.n_in;
     const int nb4 = (nb + 3) / 4;
     const int64_t row_bytes = mfma_row_bytes<FMT>(n_in);
@@ -509,19 +503,33 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         }
     };
 
+    // Units (chunk, step) in order; the loads of the next unit are issued
+    // while the current one is consumed: x first, then each tile's weights
+    // right after that tile's registers are consumed.  No branch surrounds a
+    // load in the loop, so the in-order vector-memory counter keeps a whole
+    // step of loads in flight.  The first unit's loads go out before the Q4
+    // code table is built, so that building it overlaps their latency.
+    if (Sw > 0) {
+        issue_x();
+#pragma unroll
+        for (int r = 0; r < TC; ++r) issue_w(r);
+    }
+    if constexpr (FMT == FMT_Q4) {
+        // the code table: wave w fills byte values w, w + 8, ..., one column
+        // per lane; then this wave's LDS writes are waited for and the
+        // workgroup meets at a barrier without __syncthreads' release fence,
+        // which would also wait for the loads above
+#pragma unroll 4
+        for (int i = 0; i < 32; ++i) lut[(8 * i + wave) * 64 + lane] = q4_pair_bf16(8 * i + wave);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
     if (Sw == 0) {
         for (Chunk c = chunk_at(ta); c.cnt > 0; c = chunk_at(c.start + c.cnt)) reduce(c);
         return;
     }
-
-    // Units (chunk, step) in order; the loads of the next unit are issued
-    // while the current one is consumed: x first, then each tile's weights
-    // right after that tile's registers are consumed.  No branch surrounds a
-    // load, so the in-order vector-memory counter keeps a whole step of
-    // loads in flight.
-    issue_x();
-#pragma unroll
-    for (int r = 0; r < TC; ++r) issue_w(r);
     Chunk cc = ic;
     int cs = is;
     advance(ic, is);
