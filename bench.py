@@ -31,6 +31,17 @@ import numpy as np  # noqa: E402
 from quantized_weight_matmul_amd import workloads as wl  # noqa: E402
 
 METRIC = "weight GB/s (decode GEMV, % HBM peak); TFLOP/s (prefill GEMM, % MFMA peak)"
+
+def path_dtype(fmts, t):
+    """Arithmetic of the kernel family il_matmul runs for these weight formats
+    at t tokens (the dispatch in csrc/il_gemv.hip and il_gemm.hip): f32 FMAs on
+    the streaming decode kernel (bf16 weights, and Q8 below t = 4); bf16
+    matrix-core products with f32 accumulation otherwise (the decode kernel's
+    x as two bf16 parts, hi + lo; bf16(x) on the mid-size and GEMM paths)."""
+    if t <= 8 and all(f == "bf16" or (f == "q8" and t < 4) for f in fmts):
+        return "f32"
+    return "bf16"
+
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk, dense
 ROTATE_BYTES = 1 << 30
@@ -281,7 +292,7 @@ def bench_gelu_mul(args, name: str) -> int:
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if t <= 8 else "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": path_dtype([wl.FMT_NAMES[fmt]], t), "data": "synthetic",
         "config": {"workload": f"{name}: {DESCRIPTIONS[name]}", "t": t, "n_in": n_in,
                    "jobs": [[wl.FMT_NAMES[fmt], n_out], [wl.FMT_NAMES[fmt], n_out]],
                    "weight_bytes_per_step": per_set, "flops_per_step": flops, "weight_sets_rotated": n_sets,
@@ -537,7 +548,7 @@ def report(args, sub, per_set, n_sets, ms_per_step, kern_ms, pair_ms, x_np, weig
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if decode else "bf16",
+        "dtype": path_dtype([wl.FMT_NAMES[j.fmt] for j in sub.jobs], sub.t),
         "data": "synthetic",
         "config": {
             "workload": f"{sub.name}: {DESCRIPTIONS[sub.name]}",
