@@ -65,12 +65,15 @@ __global__ void repack_q4_kernel(const uint16_t *__restrict__ staging,
 //       nibble holds q's 4-bit two's complement (= code ^ 8, code = q + 8);
 //   a zero scale stores 0 and all-zero values.
 // Divisions are the correctly rounded f32 division, rint rounds half to even.
-// Eight lanes share a block, four consecutive elements each (one 16-byte
-// load of f32, 8 bytes of bf16), and find amax with three lane exchanges.
+// Q8 (quantize_kernel): eight lanes share a block, four consecutive elements
+// each (one 16-byte load of f32, 8 bytes of bf16), and find amax with three
+// lane exchanges; the row-major code plane takes their 4-byte stores in
+// order.  Q4: quantize_q4_kernel below.
 template <int FMT, int SRC>
 __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ src, uint8_t *__restrict__ codes,
                                                        void *__restrict__ scales, void *__restrict__ scales_t,
                                                        int64_t n_blocks, int64_t nb) {
+    static_assert(FMT == FMT_Q8, "Q4 uses quantize_q4_kernel");
     const int64_t b = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
     const int part = threadIdx.x & 7;  // elements 4 part .. 4 part + 3 of the block
     const bool live = b < n_blocks;
@@ -93,39 +96,78 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
     if (!live) return;
     const int64_t row = b / nb, blk = b - row * nb;
     const int64_t ti = tiled_scale_index(row, blk, (nb + 3) / 4);
-    if constexpr (FMT == FMT_Q8) {
-        const float s = amax / 127.0f;
-        uint32_t packed = 0;
+    const float s = amax / 127.0f;
+    uint32_t packed = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float q = 0.f;
-            if (s != 0.f) q = fminf(fmaxf(rintf(v[i] / s), -127.f), 127.f);
-            packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * i);
-        }
-        *reinterpret_cast<uint32_t *>(codes + e0) = packed;
-        if (part == 0) {
-            static_cast<float *>(scales)[b] = s;
-            static_cast<float *>(scales_t)[ti] = s;
+    for (int i = 0; i < 4; ++i) {
+        float q = 0.f;
+        if (s != 0.f) q = fminf(fmaxf(rintf(v[i] / s), -127.f), 127.f);
+        packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * i);
+    }
+    *reinterpret_cast<uint32_t *>(codes + e0) = packed;
+    if (part == 0) {
+        static_cast<float *>(scales)[b] = s;
+        static_cast<float *>(scales_t)[ti] = s;
+    }
+}
+
+// Q4, in the order of the tile-major plane: workgroup (16-row tile, group of
+// 4 segments); wave w takes segment 4 group + w, lane l the block of row l / 4
+// and segment slot l % 4, all 32 of its elements (one thread per block, amax
+// without lane exchanges), so that the wave's code stores are one contiguous
+// 1 KiB run of the plane and its tiled scales one 128-byte run.  Measured on
+// f32 [17408, 5120]: 101 -> 88 us against 8 lanes per block in row order,
+// whose stores landed in 64-byte runs.  Same rule and arithmetic as above.
+template <int SRC>
+__global__ __launch_bounds__(256) void quantize_q4_kernel(const void *__restrict__ src, uint8_t *__restrict__ codes,
+                                                          uint16_t *__restrict__ scales, uint16_t *__restrict__ scales_t,
+                                                          int64_t n_out, int64_t nb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t nb4 = (nb + 3) / 4;
+    const int64_t ngroups = (nb4 + 3) / 4;
+    const int64_t tile = blockIdx.x / ngroups, grp = blockIdx.x - tile * ngroups;
+    const int64_t seg = grp * 4 + wave;
+    const int64_t row = tile * 16 + (lane >> 2);
+    const int64_t blk = seg * 4 + (lane & 3);
+    if (seg >= nb4 || row >= n_out || blk >= nb) return;  // padding: the planes were cleared
+    const int64_t e0 = (row * nb + blk) * kBlock;
+    float v[kBlock];
+    if constexpr (SRC == SRC_F32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 f = static_cast<const float4 *>(src)[e0 / 4 + i];
+            v[4 * i] = f.x, v[4 * i + 1] = f.y, v[4 * i + 2] = f.z, v[4 * i + 3] = f.w;
         }
     } else {
-        uint16_t sb = __builtin_bit_cast(uint16_t, (_Float16)(amax / 7.0f));
-        if (sb == 0x7C00u) sb = 0x7BFFu;
-        const float s = (float)__builtin_bit_cast(_Float16, sb);
-        uint32_t nib = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float q = 0.f;
-            if (s != 0.f) q = fminf(fmaxf(rintf(v[i] / s), -8.f), 7.f);
-            nib |= ((uint32_t)(int)q & 0xFu) << (4 * i);
-        }
-        // elements 4 part + i sit in bytes 2 part (i < 2) and 2 part + 1 of
-        // the block, element 2j in the low nibble of byte j
-        *reinterpret_cast<uint16_t *>(codes + q4_block_offset(row, blk, nb) + 2 * part) = (uint16_t)nib;
-        if (part == 0) {
-            static_cast<uint16_t *>(scales)[b] = sb;
-            static_cast<uint16_t *>(scales_t)[ti] = sb;
+            const uint4 h = static_cast<const uint4 *>(src)[e0 / 8 + i];  // bf16 -> f32 is exact
+            const uint32_t w[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[8 * i + 2 * k] = __builtin_bit_cast(float, w[k] << 16);
+                v[8 * i + 2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xFFFF0000u);
+            }
         }
     }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    uint16_t sb = __builtin_bit_cast(uint16_t, (_Float16)(amax / 7.0f));
+    if (sb == 0x7C00u) sb = 0x7BFFu;
+    const float sc = (float)__builtin_bit_cast(_Float16, sb);
+    // element 2j in the low nibble of byte j; the nibble is q's 4-bit two's
+    // complement (= code ^ 8)
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) {
+        float q = 0.f;
+        if (sc != 0.f) q = fminf(fmaxf(rintf(v[i] / sc), -8.f), 7.f);
+        w[i >> 3] |= ((uint32_t)(int)q & 0xFu) << (4 * (i & 7));
+    }
+    *reinterpret_cast<uint4 *>(codes + q4_block_offset(row, blk, nb)) = make_uint4(w[0], w[1], w[2], w[3]);
+    scales[row * nb + blk] = sb;
+    scales_t[tiled_scale_index(row, blk, nb4)] = sb;
 }
 
 // ---- download: the device planes back to the host block formats ----
@@ -168,11 +210,16 @@ hipError_t launch_quantize(int fmt, int src_type, const void *src, uint8_t *code
         hipLaunchKernelGGL((quantize_kernel<FMT_Q8, SRC_F32>), g, t, 0, s, src, codes, scales, scales_t, n_blocks, nb);
     else if (fmt == FMT_Q8 && src_type == SRC_BF16)
         hipLaunchKernelGGL((quantize_kernel<FMT_Q8, SRC_BF16>), g, t, 0, s, src, codes, scales, scales_t, n_blocks, nb);
-    else if (fmt == FMT_Q4 && src_type == SRC_F32)
-        hipLaunchKernelGGL((quantize_kernel<FMT_Q4, SRC_F32>), g, t, 0, s, src, codes, scales, scales_t, n_blocks, nb);
-    else if (fmt == FMT_Q4 && src_type == SRC_BF16)
-        hipLaunchKernelGGL((quantize_kernel<FMT_Q4, SRC_BF16>), g, t, 0, s, src, codes, scales, scales_t, n_blocks, nb);
-    else
+    else if (fmt == FMT_Q4 && (src_type == SRC_F32 || src_type == SRC_BF16)) {
+        // one workgroup per (16-row tile, group of 4 segments)
+        const int64_t nb4 = (nb + 3) / 4, tiles = (n_out + 15) / 16;
+        const dim3 gq((unsigned)(tiles * ((nb4 + 3) / 4)));
+        uint16_t *sc = static_cast<uint16_t *>(scales), *sct = static_cast<uint16_t *>(scales_t);
+        if (src_type == SRC_F32)
+            hipLaunchKernelGGL((quantize_q4_kernel<SRC_F32>), gq, t, 0, s, src, codes, sc, sct, n_out, nb);
+        else
+            hipLaunchKernelGGL((quantize_q4_kernel<SRC_BF16>), gq, t, 0, s, src, codes, sc, sct, n_out, nb);
+    } else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
