@@ -65,73 +65,12 @@ __global__ void repack_q4_kernel(const uint16_t *__restrict__ staging,
 //       nibble holds q's 4-bit two's complement (= code ^ 8, code = q + 8);
 //   a zero scale stores 0 and all-zero values.
 // Divisions are the correctly rounded f32 division, rint rounds half to even.
-// Q8 (quantize_kernel): eight lanes share a block, four consecutive elements
-// each (one 16-byte load of f32, 8 bytes of bf16), and find amax with three
-// lane exchanges; the row-major code plane takes their 4-byte stores in
-// order.  Q4: quantize_q4_kernel below.
-template <int FMT, int SRC>
-__global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ src, uint8_t *__restrict__ codes,
-                                                       void *__restrict__ scales, void *__restrict__ scales_t,
-                                                       int64_t n_blocks, int64_t nb) {
-    static_assert(FMT == FMT_Q8, "Q4 uses quantize_q4_kernel");
-    const int64_t b = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
-    const int part = threadIdx.x & 7;  // elements 4 part .. 4 part + 3 of the block
-    const bool live = b < n_blocks;
-    const int64_t e0 = b * kBlock + 4 * part;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (live) {
-        if constexpr (SRC == SRC_F32) {
-            const float4 f = static_cast<const float4 *>(src)[e0 / 4];
-            v[0] = f.x, v[1] = f.y, v[2] = f.z, v[3] = f.w;
-        } else {
-            const uint2 h = static_cast<const uint2 *>(src)[e0 / 4];  // bf16 -> f32 is exact
-            v[0] = __builtin_bit_cast(float, h.x << 16), v[1] = __builtin_bit_cast(float, h.x & 0xFFFF0000u);
-            v[2] = __builtin_bit_cast(float, h.y << 16), v[3] = __builtin_bit_cast(float, h.y & 0xFFFF0000u);
-        }
-    }
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-    if (!live) return;
-    const int64_t row = b / nb, blk = b - row * nb;
-    const int64_t ti = tiled_scale_index(row, blk, (nb + 3) / 4);
-    const float s = amax / 127.0f;
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float q = 0.f;
-        if (s != 0.f) q = fminf(fmaxf(rintf(v[i] / s), -127.f), 127.f);
-        packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * i);
-    }
-    *reinterpret_cast<uint32_t *>(codes + e0) = packed;
-    if (part == 0) {
-        static_cast<float *>(scales)[b] = s;
-        static_cast<float *>(scales_t)[ti] = s;
-    }
-}
-
-// Q4, in the order of the tile-major plane: workgroup (16-row tile, group of
-// 4 segments); wave w takes segment 4 group + w, lane l the block of row l / 4
-// and segment slot l % 4, all 32 of its elements (one thread per block, amax
-// without lane exchanges), so that the wave's code stores are one contiguous
-// 1 KiB run of the plane and its tiled scales one 128-byte run.  Measured on
-// f32 [17408, 5120]: 101 -> 88 us against 8 lanes per block in row order,
-// whose stores landed in 64-byte runs.  Same rule and arithmetic as above.
+// One thread per block, all 32 of its elements (eight 16-byte loads of f32,
+// four of bf16), so amax needs no lane exchanges.  Q8: in row order, so that
+// a wave's code stores are one contiguous 2 KiB run (8 lanes per block, 4
+// elements each, measured 64.9 against 63.6 us on f32 [14336, 4096]).
 template <int SRC>
-__global__ __launch_bounds__(256) void quantize_q4_kernel(const void *__restrict__ src, uint8_t *__restrict__ codes,
-                                                          uint16_t *__restrict__ scales, uint16_t *__restrict__ scales_t,
-                                                          int64_t n_out, int64_t nb) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t nb4 = (nb + 3) / 4;
-    const int64_t ngroups = (nb4 + 3) / 4;
-    const int64_t tile = blockIdx.x / ngroups, grp = blockIdx.x - tile * ngroups;
-    const int64_t seg = grp * 4 + wave;
-    const int64_t row = tile * 16 + (lane >> 2);
-    const int64_t blk = seg * 4 + (lane & 3);
-    if (seg >= nb4 || row >= n_out || blk >= nb) return;  // padding: the planes were cleared
-    const int64_t e0 = (row * nb + blk) * kBlock;
-    float v[kBlock];
+__device__ __forceinline__ void load_block(const void *__restrict__ src, int64_t e0, float (&v)[kBlock]) {
     if constexpr (SRC == SRC_F32) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -150,6 +89,62 @@ __global__ __launch_bounds__(256) void quantize_q4_kernel(const void *__restrict
             }
         }
     }
+}
+
+template <int SRC>
+__global__ __launch_bounds__(256) void quantize_q8_kernel(const void *__restrict__ src, int8_t *__restrict__ codes,
+                                                          float *__restrict__ scales, float *__restrict__ scales_t,
+                                                          int64_t n_blocks, int64_t nb) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= n_blocks) return;
+    const int64_t e0 = b * kBlock;
+    float v[kBlock];
+    load_block<SRC>(src, e0, v);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float s = amax / 127.0f;
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float q = 0.f;
+            if (s != 0.f) q = fminf(fmaxf(rintf(v[4 * j + i] / s), -127.f), 127.f);
+            packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * i);
+        }
+        w[j] = packed;
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(codes + e0);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    scales[b] = s;
+    scales_t[tiled_scale_index(b / nb, b % nb, (nb + 3) / 4)] = s;
+}
+
+// Q4, in the order of the tile-major plane: workgroup (16-row tile, group of
+// 4 segments); wave w takes segment 4 group + w, lane l the block of row l / 4
+// and segment slot l % 4, all 32 of its elements (one thread per block, amax
+// without lane exchanges), so that the wave's code stores are one contiguous
+// 1 KiB run of the plane and its tiled scales one 128-byte run (in row
+// order the stores landed in 64-byte runs: 101 against 88 us on f32
+// [17408, 5120]).
+template <int SRC>
+__global__ __launch_bounds__(256) void quantize_q4_kernel(const void *__restrict__ src, uint8_t *__restrict__ codes,
+                                                          uint16_t *__restrict__ scales, uint16_t *__restrict__ scales_t,
+                                                          int64_t n_out, int64_t nb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t nb4 = (nb + 3) / 4;
+    const int64_t ngroups = (nb4 + 3) / 4;
+    const int64_t tile = blockIdx.x / ngroups, grp = blockIdx.x - tile * ngroups;
+    const int64_t seg = grp * 4 + wave;
+    const int64_t row = tile * 16 + (lane >> 2);
+    const int64_t blk = seg * 4 + (lane & 3);
+    if (seg >= nb4 || row >= n_out || blk >= nb) return;  // padding: the planes were cleared
+    const int64_t e0 = (row * nb + blk) * kBlock;
+    float v[kBlock];
+    load_block<SRC>(src, e0, v);
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < kBlock; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -203,14 +198,17 @@ __global__ void unrepack_q4_kernel(const uint8_t *__restrict__ codes, const uint
 hipError_t launch_quantize(int fmt, int src_type, const void *src, uint8_t *codes, void *scales, void *scales_t,
                            int64_t n_out, int64_t n_in, hipStream_t s) {
     const int64_t n_blocks = n_out * (n_in / kBlock);
-    const int64_t grid = (n_blocks * 8 + 255) / 256;
     const int64_t nb = n_in / kBlock;
-    const dim3 g((unsigned)grid), t(256);
-    if (fmt == FMT_Q8 && src_type == SRC_F32)
-        hipLaunchKernelGGL((quantize_kernel<FMT_Q8, SRC_F32>), g, t, 0, s, src, codes, scales, scales_t, n_blocks, nb);
-    else if (fmt == FMT_Q8 && src_type == SRC_BF16)
-        hipLaunchKernelGGL((quantize_kernel<FMT_Q8, SRC_BF16>), g, t, 0, s, src, codes, scales, scales_t, n_blocks, nb);
-    else if (fmt == FMT_Q4 && (src_type == SRC_F32 || src_type == SRC_BF16)) {
+    const dim3 t(256);
+    if (fmt == FMT_Q8 && (src_type == SRC_F32 || src_type == SRC_BF16)) {
+        const dim3 g((unsigned)((n_blocks + 255) / 256));
+        int8_t *c = reinterpret_cast<int8_t *>(codes);
+        float *sc = static_cast<float *>(scales), *sct = static_cast<float *>(scales_t);
+        if (src_type == SRC_F32)
+            hipLaunchKernelGGL((quantize_q8_kernel<SRC_F32>), g, t, 0, s, src, c, sc, sct, n_blocks, nb);
+        else
+            hipLaunchKernelGGL((quantize_q8_kernel<SRC_BF16>), g, t, 0, s, src, c, sc, sct, n_blocks, nb);
+    } else if (fmt == FMT_Q4 && (src_type == SRC_F32 || src_type == SRC_BF16)) {
         // one workgroup per (16-row tile, group of 4 segments)
         const int64_t nb4 = (nb + 3) / 4, tiles = (n_out + 15) / 16;
         const dim3 gq((unsigned)(tiles * ((nb4 + 3) / 4)));
