@@ -520,9 +520,16 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
         (void)hipEventRecord(ev0, s);
     }
     uint64_t launches = 0, bytes = 0;
+    // rows per launch: the kernels count them in 32-bit ints; IL_LAUNCH_ROWS
+    // lowers the limit (tests force multi-launch splits with small weights)
+    int64_t max_rows = INT_MAX;
+    if (const char *v = getenv("IL_LAUNCH_ROWS")) {
+        const long long r = atoll(v);
+        if (r >= 1 && r < INT_MAX) max_rows = r;
+    }
     for (int fmt = 0; fmt < 3; ++fmt) {
         std::vector<il::KJob> batch;
-        int64_t batch_rows = 0;  // the kernels count a launch's rows in 32-bit ints
+        int64_t batch_rows = 0;
         auto flush = [&]() -> bool {
             batch_rows = 0;
             if (batch.empty()) return true;
@@ -541,7 +548,7 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
         for (int64_t j = 0; j < n_jobs; ++j) {
             const il_weight *w = jobs[j].w;
             if (w->fmt != fmt) continue;
-            if (batch_rows + w->n_out > INT_MAX && !flush()) {  // n_out <= INT_MAX on its own
+            if (!batch.empty() && batch_rows + w->n_out > max_rows && !flush()) {  // a job alone may exceed it
                 g_failed++;
                 return 0;
             }

@@ -160,6 +160,30 @@ def test_long_rows_two_per_wave(fmt, t, n_in, monkeypatch):
         check_full(y, x, w, fmt, n, what=f"fmt {fmt} t {t} n_in {n_in} n_out {n}")
 
 
+@pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
+@pytest.mark.parametrize("t,path", [(2, "valu"), (2, "mfma"), (20, "verify"), (300, "gemm")])
+def test_jobs_split_across_launches(fmt, t, path, monkeypatch):
+    """il_matmul starts a new launch before one launch's rows would pass a
+    limit (2^31 - 1: the kernels count rows in 32-bit ints; IL_LAUNCH_ROWS
+    lowers it for tests).  Splitting the jobs over several launches leaves
+    every result bitwise unchanged."""
+    _pin(monkeypatch, path)
+    g = np.random.default_rng(2400 + 10 * t + fmt)
+    n_in = 512
+    n_outs = [300, 17, 129, 256, 64, 200]
+    say(f"[split] fmt={FMT_NAME[fmt]} t={t} path={path} n_outs={n_outs}")
+    x = g.standard_normal((t, n_in)).astype(np.float32)
+    ws = [_rand_weight(fmt, g, n, n_in) for n in n_outs]
+    hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
+    whole = run(x, hs, n_outs)
+    monkeypatch.setenv("IL_LAUNCH_ROWS", "320")  # launches of 300 + 17 | 129 | 256 + 64 | 200 rows
+    split = run(x, hs, n_outs)
+    for k, (a, b) in enumerate(zip(whole, split)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"job {k} differs when split"
+    for w, n, y in zip(ws, n_outs, split):
+        check_full(y, x, w, fmt, n, what=f"split fmt {fmt} t {t} n_out {n}")
+
+
 def test_mixed_formats_one_call():
     g = np.random.default_rng(5)
     n_in = 256
