@@ -308,10 +308,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     Chunk ic = chunk_at(ta);
     int is = wave;
     __amdgpu_buffer_rsrc_t crs, srs, crs2, srs2;  // *2: the up projection (GLU)
-    int ic_nout;  // rows of the issue chunk's job
     auto set_rsrc = [&]() {
         const KJob &jb = p.job[ic.j];
-        ic_nout = jb.n_out;
         const int64_t rows = ic.cnt > 0 ? jb.n_out : 0;
         const uint32_t sbytes = (uint32_t)(tiled_scale_count(rows, nb) * (FMT == FMT_Q8 ? 4 : 2));
         const uint32_t cbytes = (uint32_t)(FMT == FMT_Q4 ? q4_plane_bytes(rows, nb) : rows * row_bytes);
@@ -350,8 +348,12 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     // of the plane * nb4 + step) shifted, plus these per-lane constants
     const uint32_t q4_code_lane = ((uint32_t)n << 6) + ((uint32_t)g << 4);
     const uint32_t q4_scale_lane = (uint32_t)n << 3;
+    // bf16 / Q8: a lane's code offset is the tile's first row + the step's 64
+    // bytes (uniform) plus its row and 16-byte chunk; its Q8 scale index the
+    // tiled plane's uniform part plus row n and block half g / 2
+    const uint32_t rm_code_lane = (uint32_t)n * (uint32_t)row_bytes + ((uint32_t)g << 4);
+    const uint32_t q8_scale_lane = ((uint32_t)n << 2) + (uint32_t)(g >> 1);
     auto issue_w = [&](int r) {
-        const int kb = 4 * is + g;  // 16-byte chunk of the row this lane fetches
         const int rt = r % TCh;     // tile of its job
         const bool up = GLU && r >= TCh;
         const __amdgpu_buffer_rsrc_t wrs = up ? crs2 : crs, qrs = up ? srs2 : srs;
@@ -369,17 +371,19 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
                 uint2, __builtin_amdgcn_raw_buffer_load_b64(qrs, ok ? (seg << 7) + q4_scale_lane : kOut, 0, 0));
             return;
         }
-        // bf16 / Q8: row-major planes, not padded -- per-lane row and block checks
-        const int row = ic.lrow0 + kTile * rt + n;
-        const bool row_ok = rt < ic.cnt && row < ic_nout;
-        const bool ok = row_ok && (int64_t)kb * 16 < row_bytes;
-        wc[r] = bload16(wrs, ok ? (uint32_t)(row * row_bytes + kb * 16) : kOut);
-        // scales from the tiled plane: a tile's 16 rows x 4 blocks are one run
+        // bf16 / Q8, row-major planes: no per-lane checks either.  A row past
+        // the job's last lies past its plane's descriptor and reads zeros; a
+        // Q8 chunk past the end of a row (the last step, when the row has an
+        // odd number of blocks) reads the next row's codes, which meet zero x
+        // (x past n_in reads zeros) and the zero padded scale, so it adds 0.
+        const bool ok = rt < ic.cnt;
+        const uint32_t row0 = (uint32_t)(ic.lrow0 + kTile * rt);
+        wc[r] = bload16(wrs, ok ? row0 * (uint32_t)row_bytes + ((uint32_t)is << 6) + rm_code_lane : kOut);
         if constexpr (FMT == FMT_Q8) {
-            // this lane's 16 bytes are half of block 2s + g/2
-            const int blk = 2 * is + (g >> 1);
-            ws[r] = __builtin_amdgcn_raw_buffer_load_b32(
-                qrs, row_ok && blk < nb ? (uint32_t)(tiled_scale_index(row, blk, nb4) * 4) : kOut, 0, 0);
+            // this lane's 16 bytes are half of block 2s + g/2: scale index
+            // ((tile * nb4 + s/2) * 64) + 4 n + 2 (s % 2) + g/2 in the tiled plane
+            const uint32_t tq = ((row0 >> 4) * (uint32_t)nb4 + ((uint32_t)is >> 1)) * 64u + (((uint32_t)is & 1u) << 1);
+            ws[r] = __builtin_amdgcn_raw_buffer_load_b32(qrs, ok ? (tq + q8_scale_lane) * 4u : kOut, 0, 0);
         }
     };
     auto advance = [&](Chunk &c, int &s) {
