@@ -377,6 +377,32 @@ def pin_lm_head_random(O):
         assert r["token"][i] == cand[j] and r["score"][i] == sc[j], "first-max argmax"
 
 
+def pin_token_score(O):
+    """One token's score embed[tok] . x and its bound sum |embed[tok] * x|
+    (the `dot_bf16(row, xr)` of the candidate scan in `Drafter::step` on the
+    oxinfer 0.0.1 src/drafter.rs page) against numpy float64 on torch-decoded
+    bf16 rows: first, last and inner tokens, several rows of x, mixed signs
+    so that a signed bound or a shifted row cannot agree by chance."""
+    rng = np.random.default_rng(42)
+    for h, vocab in ((64, 37), (256, 300), (32, 2)):
+        emb = wl.f32_to_bf16_bits(rng.standard_normal((vocab, h)).astype(np.float32))
+        embf = lib_bf16(emb)
+        xs = rng.standard_normal((3, h)).astype(np.float32)
+        for x in xs:
+            for tok in sorted({0, 1, vocab // 2, vocab - 2, vocab - 1}):
+                v, b = O.token_score(x, emb, tok)
+                want = float(embf[tok] @ x.astype(np.float64))
+                want_b = float(np.abs(embf[tok]) @ np.abs(x.astype(np.float64)))
+                assert abs(v - want) <= 1e-12 * want_b, f"score h={h} tok={tok}: {v} vs {want}"
+                assert abs(b - want_b) <= 1e-12 * want_b, f"bound h={h} tok={tok}: {b} vs {want_b}"
+    # an exact case: integer rows, whose dot products are exact in both
+    emb_i = np.array([[1, -2, 3, 0], [4, 0, -1, 2], [-3, 3, 3, -3]], np.int64)
+    x_i = np.array([2.0, -1.0, 0.5, 4.0], np.float32)
+    for tok, (want, want_b) in enumerate(((5.5, 5.5), (15.5, 16.5), (-19.5, 22.5))):
+        v, b = O.token_score(x_i, _bf16_of_ints(emb_i), tok)
+        assert (v, b) == (want, want_b), f"integer row {tok}: ({v}, {b})"
+
+
 # --------------------------------------------------------------- quantiser
 # The upload quantiser (absmax per 32-element block; the rule is stated in
 # il_oracle.c).  Its pins: numpy's float16 cast on every binary16 value, on
@@ -653,7 +679,7 @@ ALL_PINS = [
     pin_numpy_matmul, pin_points_equal_rows, pin_thread_invariance, pin_check_rule,
     pin_f16_rounding, pin_quantize_hand, pin_quantize_roundtrip, pin_quantize_nearest,
     pin_gelu_values, pin_gelu_mul_onehot, pin_gelu_mul_composition,
-    pin_lm_head_integers, pin_lm_head_random,
+    pin_lm_head_integers, pin_lm_head_random, pin_token_score,
 ]
 
 
