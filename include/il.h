@@ -142,11 +142,17 @@ IL_API void il_free(il_weight *w);
  * GEMV kernels (f32 streaming or matrix-core, by format and t), one launch
  * per weight format present; 8 < t <= 32 (Q4 weights: <= 128, in even
  * slices of at most 32 tokens, one launch each) the matrix-core kernel's
- * wide mode; beyond, the MFMA GEMM (an x -> bf16 pre-pass, then whole
- * rounds of 256 x 256 tiles and the rest as 128 x 128 tiles; Q8/Q4 with
- * fewer 256 x 256 tiles than compute units run whole rounds of 256 x 128
- * halves first).  All jobs of
- * one format share each launch.  Asynchronous: returns after enqueueing,
+ * wide mode; beyond, the MFMA GEMM: an x -> bf16 pre-pass, then one launch
+ * per format (bf16: whole rounds of 256 x 256 tiles and the rest as
+ * 128 x 128 quarters; Q8/Q4: 256 x 128 halves and 128 x 128 quarters, the
+ * codes exact and each block's scale applied to its f32 partial sum).  All
+ * jobs of one format share each launch.  The bf16 copy of x lives in a
+ * buffer the library keeps per stream (grown when a call needs more, kept
+ * until the process ends; while the stream is being captured into a graph
+ * and that buffer is too small, the call allocates stream-ordered memory
+ * instead).  A graph that captured a prefill call reads the buffer of the
+ * stream it was captured on: do not replay it concurrently with other
+ * prefill calls on that stream.  Asynchronous: returns after enqueueing,
  * results are valid once the stream has reached that point.
  * Returns 1 on success, 0 if nothing was computed (the page's `false`: the
  * caller then runs the whole batch elsewhere).  On a validation failure the

@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -59,12 +60,30 @@ bool env_flag(const char *name, const char *value) {
 // ---------------------------------------------------------------- context
 constexpr int kMaxDevices = 64;
 
+// Scratch of the prefill path (the bf16 copy of x its GEMM units read), one
+// buffer per stream.  A call holds its stream's entry locked while it
+// enqueues the pre-pass that writes the buffer and the launch that reads it,
+// so calls on one stream (from any thread) use it in stream order, and calls
+// on different streams never share it.  A buffer grows (by at least half)
+// when a call needs more; the one it replaces may still be read by work in
+// flight or by a graph that captured it, so it is kept, like every buffer,
+// until the process ends.
+struct StreamScratch {
+    hipStream_t stream = nullptr;
+    void *ptr = nullptr;
+    size_t bytes = 0;
+    std::mutex m;
+};
+
 struct DeviceCtx {
     std::once_flag once;
     bool ok = false;
     std::string err;
     int cu_count = 0;
     hipStream_t upload_stream = nullptr;
+    std::mutex scratch_m;  // guards the two vectors below
+    std::vector<std::unique_ptr<StreamScratch>> scratch;
+    std::vector<void *> retired;
 };
 
 DeviceCtx g_dev[kMaxDevices];
@@ -106,6 +125,70 @@ DeviceCtx *context(int *device_out) {
     }
     if (device_out) *device_out = dev;
     return &c;
+}
+
+// The stream's scratch entry (created on first use), returned locked.
+std::unique_lock<std::mutex> stream_scratch(DeviceCtx *ctx, hipStream_t s, StreamScratch **out) {
+    StreamScratch *e = nullptr;
+    {
+        std::lock_guard<std::mutex> g(ctx->scratch_m);
+        for (auto &p : ctx->scratch)
+            if (p->stream == s) e = p.get();
+        if (!e) {
+            ctx->scratch.push_back(std::make_unique<StreamScratch>());
+            e = ctx->scratch.back().get();
+            e->stream = s;
+        }
+    }
+    *out = e;
+    return std::unique_lock<std::mutex>(e->m);
+}
+
+// Makes e hold at least `need` bytes.  While the stream is being captured
+// into a graph no buffer is allocated (an allocation is not a stream
+// operation): *fallback is set and the caller allocates stream-ordered memory
+// instead, which the graph then records as allocation nodes.
+hipError_t grow_scratch(DeviceCtx *ctx, StreamScratch *e, size_t need, bool *fallback) {
+    *fallback = false;
+    if (e->bytes >= need) return hipSuccess;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t err = hipStreamIsCapturing(e->stream, &cs);
+    if (err != hipSuccess) return err;
+    if (cs != hipStreamCaptureStatusNone) {
+        *fallback = true;
+        return hipSuccess;
+    }
+    const size_t want = need > e->bytes + e->bytes / 2 ? need : e->bytes + e->bytes / 2;
+    void *p = nullptr;
+    err = hipMalloc(&p, want);
+    if (err != hipSuccess) return err;
+    if (e->ptr) {
+        std::lock_guard<std::mutex> g(ctx->scratch_m);
+        ctx->retired.push_back(e->ptr);
+    }
+    e->ptr = p;
+    e->bytes = want;
+    return hipSuccess;
+}
+
+// One prefill launch group (pre-pass + GEMM, or the wide-mode launches) with
+// its scratch from the stream's cache.
+hipError_t run_gemm(DeviceCtx *ctx, int fmt, const float *x, int t, int n_in, const il::KJob *jobs, int n_jobs,
+                    hipStream_t s, bool glu) {
+    const size_t need = il::gemm_scratch_bytes(fmt, t, n_in, jobs, n_jobs);
+    if (need == 0) return il::launch_gemm(fmt, x, nullptr, t, n_in, jobs, n_jobs, ctx->cu_count, s, glu);
+    StreamScratch *e = nullptr;
+    std::unique_lock<std::mutex> lock = stream_scratch(ctx, s, &e);
+    bool fallback = false;
+    hipError_t err = grow_scratch(ctx, e, need, &fallback);
+    if (err != hipSuccess) return err;
+    if (!fallback) return il::launch_gemm(fmt, x, e->ptr, t, n_in, jobs, n_jobs, ctx->cu_count, s, glu);
+    void *tmp = nullptr;
+    err = hipMallocAsync(&tmp, need, s);
+    if (err != hipSuccess) return err;
+    err = il::launch_gemm(fmt, x, tmp, t, n_in, jobs, n_jobs, ctx->cu_count, s, glu);
+    const hipError_t fe = hipFreeAsync(tmp, s);
+    return err != hipSuccess ? err : fe;
 }
 
 // ------------------------------------------------------------------ stats
@@ -535,8 +618,8 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
             if (batch.empty()) return true;
             hipError_t e = decode ? il::launch_gemv(fmt, x, (int)t, (int)n_in, batch.data(),
                                                     (int)batch.size(), ctx->cu_count, s)
-                                  : il::launch_gemm(fmt, x, (int)t, (int)n_in, batch.data(),
-                                                    (int)batch.size(), ctx->cu_count, s);
+                                  : run_gemm(ctx, fmt, x, (int)t, (int)n_in, batch.data(), (int)batch.size(), s,
+                                             false);
             batch.clear();
             if (e != hipSuccess) {
                 set_err("il_matmul: kernel launch failed: %s", hipGetErrorString(e));
@@ -641,7 +724,7 @@ int il_matmul_gelu_mul(const float *x, int64_t t, int64_t n_in, const il_weight 
     const il::KJob jobs[2] = {il::KJob{gate->codes, gate->scales, gate->scales_t, y, (int)n_out},
                               il::KJob{up->codes, up->scales, up->scales_t, y, (int)n_out}};
     hipError_t e = decode ? il::launch_gemv(gate->fmt, x, (int)t, (int)n_in, jobs, 2, ctx->cu_count, s, true)
-                          : il::launch_gemm(gate->fmt, x, (int)t, (int)n_in, jobs, 2, ctx->cu_count, s, true);
+                          : run_gemm(ctx, gate->fmt, x, (int)t, (int)n_in, jobs, 2, s, true);
     if (timing) {
         (void)hipEventRecord(ev1, s);
         (void)hipEventSynchronize(ev1);

@@ -119,7 +119,14 @@ hipError_t launch_verify_mfma(int fmt, const float *x, const uint16_t *xb, int t
                               int n_jobs, int cu_count, hipStream_t s, bool glu = false);
 
 // ---- prefill GEMM, t > kGemvMaxT (il_gemm.hip) ----
-hipError_t launch_gemm(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
+// Bytes of device scratch launch_gemm needs for this call (the bf16 copy of
+// x its units read), 0 when the call takes a path that rounds x itself.
+size_t gemm_scratch_bytes(int fmt, int t, int n_in, const KJob *jobs, int n_jobs);
+// xb_scratch: gemm_scratch_bytes(...) bytes of device memory, 256-byte
+// aligned, that nothing else uses until the stream has passed this call (may
+// be null when that size is 0).  Enqueues the x -> bf16 pre-pass and one GEMM
+// launch (or the wide-mode launches of mid-size t).
+hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_in, const KJob *jobs, int n_jobs,
                        int cu_count, hipStream_t s, bool glu = false);
 
 // ---- centroid-masked LM head (il_lmhead.hip) ----
