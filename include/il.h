@@ -161,6 +161,26 @@ IL_API void il_free(il_weight *w);
 IL_API int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64_t n_jobs,
               void *hip_stream);
 
+/* il_matmul for callers that cannot allocate device memory: code being
+ * captured into a HIP graph that must hold no allocation nodes, serving loops
+ * that may not call hipMalloc, harnesses that forbid it.  Same arguments,
+ * validation, kernels, results and 1 / 0 return as il_matmul, but the call
+ * allocates nothing (no device memory, no events): the bf16 copy of x that
+ * the prefill path (t > 8) reads lives in a static buffer of 32 MiB per
+ * device, built into the library and held until the process ends.
+ *   - Limit: a prefill call that needs that copy needs t * n_in * 2 bytes
+ *     (rounded up to 256); when that exceeds 32 MiB (t * n_in > 16777216)
+ *     the call fails before enqueueing anything, y untouched, with the sizes
+ *     in il_last_error().  Decode calls (t <= 8) and the mid-size calls that
+ *     round x themselves (t <= 16) use no scratch.
+ *   - Every call on a device shares that device's buffer: calls that overlap
+ *     on one device (from several streams, or a replayed graph next to other
+ *     work) race on it; order them on one stream or synchronize between them.
+ *   - The first call on a device looks up the buffer's address (no
+ *     allocation); the device must be current, as for il_matmul. */
+IL_API int il_matmul_noalloc(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64_t n_jobs,
+                             void *hip_stream);
+
 /* Fused feed-forward gate/up step -- in one submission,
  *     y[t][n_out] = GELU(x * G^T) (.) (x * U^T)        (element-wise product)
  * the `matmul_multi` over the gate and up projections followed by

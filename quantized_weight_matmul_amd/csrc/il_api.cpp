@@ -515,32 +515,80 @@ void il_free(il_weight *w) {
     delete w;
 }
 
-int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64_t n_jobs,
-              void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// One launch group of a call: jobs of one format, at most kMaxJobs of them
+// and at most `max_rows` output rows (a single job may exceed it).
+struct Batch {
+    int fmt;
+    std::vector<il::KJob> jobs;
+};
+
+std::vector<Batch> plan_batches(const il_job *jobs, int64_t n_jobs) {
+    // rows per launch: the kernels count them in 32-bit ints; IL_LAUNCH_ROWS
+    // lowers the limit (tests force multi-launch splits with small weights)
+    int64_t max_rows = INT_MAX;
+    if (const char *v = getenv("IL_LAUNCH_ROWS")) {
+        const long long r = atoll(v);
+        if (r >= 1 && r < INT_MAX) max_rows = r;
+    }
+    std::vector<Batch> out;
+    for (int fmt = 0; fmt < 3; ++fmt) {
+        Batch b{fmt, {}};
+        int64_t rows = 0;
+        for (int64_t j = 0; j < n_jobs; ++j) {
+            const il_weight *w = jobs[j].w;
+            if (w->fmt != fmt) continue;
+            if (!b.jobs.empty() && rows + w->n_out > max_rows) {
+                out.push_back(b);
+                b.jobs.clear();
+                rows = 0;
+            }
+            b.jobs.push_back(il::KJob{w->codes, w->scales, w->scales_t, jobs[j].y, (int)w->n_out});
+            rows += w->n_out;
+            if ((int)b.jobs.size() == il::kMaxJobs) {
+                out.push_back(b);
+                b.jobs.clear();
+                rows = 0;
+            }
+        }
+        if (!b.jobs.empty()) out.push_back(b);
+    }
+    return out;
+}
+
+// il_matmul and il_matmul_noalloc: validation, then one launch group per
+// batch.  noalloc: the prefill scratch is the device's static array, no
+// event or allocation is made, and a call that would need more scratch than
+// the array holds fails before anything is enqueued.
+int matmul_impl(const char *who, const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64_t n_jobs,
+                void *hip_stream, bool noalloc) {
     g_err.clear();
     if (t < 0 || n_jobs < 0) {
-        set_err("il_matmul: negative t (%" PRId64 ") or n_jobs (%" PRId64 ")", t, n_jobs);
+        set_err("%s: negative t (%" PRId64 ") or n_jobs (%" PRId64 ")", who, t, n_jobs);
         return 0;
     }
     if (t == 0 || n_jobs == 0) return 1;  // nothing to do
     if (!jobs) {
-        set_err("il_matmul: jobs is NULL");
+        set_err("%s: jobs is NULL", who);
         return 0;
     }
     if (!x) {
-        set_err("il_matmul: x is NULL");
+        set_err("%s: x is NULL", who);
         return 0;
     }
     if (t > INT_MAX || n_in < il::kBlock || n_in % il::kBlock || n_in > INT_MAX) {
-        set_err("il_matmul: bad sizes t = %" PRId64 ", n_in = %" PRId64, t, n_in);
+        set_err("%s: bad sizes t = %" PRId64 ", n_in = %" PRId64, who, t, n_in);
         return 0;
     }
     if (reinterpret_cast<uintptr_t>(x) % 16) {
-        set_err("il_matmul: x must be 16-byte aligned");
+        set_err("%s: x must be 16-byte aligned", who);
         return 0;
     }
     if (env_flag("IL_FORCE_FAIL", "matmul")) {
-        set_err("il_matmul: failure injected by IL_FORCE_FAIL");
+        set_err("%s: failure injected by IL_FORCE_FAIL", who);
         return 0;
     }
     int dev = -1;
@@ -554,25 +602,23 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
         const il_job &jb = jobs[j];
         const il_weight *w = jb.w;
         if (!w) {
-            set_err("il_matmul: job %" PRId64 " has no weight", j);
+            set_err("%s: job %" PRId64 " has no weight", who, j);
             return 0;
         }
         if (w->n_in != n_in) {
-            set_err("il_matmul: job %" PRId64 ": weight n_in %" PRId64 " != %" PRId64, j, w->n_in, n_in);
+            set_err("%s: job %" PRId64 ": weight n_in %" PRId64 " != %" PRId64, who, j, w->n_in, n_in);
             return 0;
         }
         if (jb.n_out != w->n_out) {
-            set_err("il_matmul: job %" PRId64 ": n_out %" PRId64 " != weight's %" PRId64, j, jb.n_out,
-                    w->n_out);
+            set_err("%s: job %" PRId64 ": n_out %" PRId64 " != weight's %" PRId64, who, j, jb.n_out, w->n_out);
             return 0;
         }
         if (w->device != dev) {
-            set_err("il_matmul: job %" PRId64 ": weight lives on device %d, current is %d", j,
-                    w->device, dev);
+            set_err("%s: job %" PRId64 ": weight lives on device %d, current is %d", who, j, w->device, dev);
             return 0;
         }
         if (!jb.y || reinterpret_cast<uintptr_t>(jb.y) % 4) {
-            set_err("il_matmul: job %" PRId64 ": y is NULL or misaligned", j);
+            set_err("%s: job %" PRId64 ": y is NULL or misaligned", who, j);
             return 0;
         }
         char what[32];
@@ -580,22 +626,44 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
         const int64_t y_bytes = t * jb.n_out * (int64_t)sizeof(float);
         if (!device_range_ok(jb.y, y_bytes, what)) return 0;
         if (overlaps(jb.y, y_bytes, x, x_bytes)) {
-            set_err("il_matmul: job %" PRId64 ": y overlaps x", j);
+            set_err("%s: job %" PRId64 ": y overlaps x", who, j);
             return 0;
         }
         for (int64_t q = 0; q < j; ++q) {
             if (overlaps(jb.y, y_bytes, jobs[q].y, t * jobs[q].n_out * (int64_t)sizeof(float))) {
-                set_err("il_matmul: jobs %" PRId64 " and %" PRId64 " write overlapping y", q, j);
+                set_err("%s: jobs %" PRId64 " and %" PRId64 " write overlapping y", who, q, j);
+                return 0;
+            }
+        }
+    }
+    const bool decode = t <= il::kGemvMaxT;
+    const std::vector<Batch> batches = plan_batches(jobs, n_jobs);
+    void *static_xb = nullptr;
+    if (noalloc && !decode) {
+        size_t need = 0;
+        for (const Batch &b : batches) {
+            const size_t n = il::gemm_scratch_bytes(b.fmt, (int)t, (int)n_in, b.jobs.data(), (int)b.jobs.size());
+            if (n > need) need = n;
+        }
+        if (need > il::static_scratch_bytes()) {
+            set_err("%s: t * n_in = %" PRId64 " needs %zu bytes of scratch for the bf16 copy of x; the static "
+                    "buffer holds %zu (t * n_in <= %zu)",
+                    who, t * n_in, need, il::static_scratch_bytes(), il::static_scratch_bytes() / 2);
+            return 0;
+        }
+        if (need > 0) {
+            const hipError_t e = il::static_scratch(dev, &static_xb);
+            if (e != hipSuccess) {
+                set_err("%s: address of the static scratch: %s", who, hipGetErrorString(e));
                 return 0;
             }
         }
     }
 
-    // ---- one launch per format present (kMaxJobs jobs per launch) ----
+    // ---- one launch group per batch (a format, <= kMaxJobs jobs) ----
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const bool decode = t <= il::kGemvMaxT;
     PathStats &st = g_stats[decode ? 0 : 1];
-    const bool timing = getenv("IL_TIMING") && strcmp(getenv("IL_TIMING"), "1") == 0;
+    const bool timing = !noalloc && timing_on();
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
     if (timing) {
         (void)hipEventCreate(&ev0);
@@ -603,51 +671,23 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
         (void)hipEventRecord(ev0, s);
     }
     uint64_t launches = 0, bytes = 0;
-    // rows per launch: the kernels count them in 32-bit ints; IL_LAUNCH_ROWS
-    // lowers the limit (tests force multi-launch splits with small weights)
-    int64_t max_rows = INT_MAX;
-    if (const char *v = getenv("IL_LAUNCH_ROWS")) {
-        const long long r = atoll(v);
-        if (r >= 1 && r < INT_MAX) max_rows = r;
-    }
-    for (int fmt = 0; fmt < 3; ++fmt) {
-        std::vector<il::KJob> batch;
-        int64_t batch_rows = 0;
-        auto flush = [&]() -> bool {
-            batch_rows = 0;
-            if (batch.empty()) return true;
-            hipError_t e = decode ? il::launch_gemv(fmt, x, (int)t, (int)n_in, batch.data(),
-                                                    (int)batch.size(), ctx->cu_count, s)
-                                  : run_gemm(ctx, fmt, x, (int)t, (int)n_in, batch.data(), (int)batch.size(), s,
-                                             false);
-            batch.clear();
-            if (e != hipSuccess) {
-                set_err("il_matmul: kernel launch failed: %s", hipGetErrorString(e));
-                return false;
-            }
-            ++launches;
-            return true;
-        };
-        for (int64_t j = 0; j < n_jobs; ++j) {
-            const il_weight *w = jobs[j].w;
-            if (w->fmt != fmt) continue;
-            if (!batch.empty() && batch_rows + w->n_out > max_rows && !flush()) {  // a job alone may exceed it
-                g_failed++;
-                return 0;
-            }
-            batch.push_back(il::KJob{w->codes, w->scales, w->scales_t, jobs[j].y, (int)w->n_out});
-            batch_rows += w->n_out;
-            bytes += (uint64_t)w->host_bytes;
-            if ((int)batch.size() == il::kMaxJobs && !flush()) {
-                g_failed++;
-                return 0;
-            }
-        }
-        if (!flush()) {
+    for (const Batch &b : batches) {
+        const int nb = (int)b.jobs.size();
+        hipError_t e;
+        if (decode)
+            e = il::launch_gemv(b.fmt, x, (int)t, (int)n_in, b.jobs.data(), nb, ctx->cu_count, s);
+        else if (noalloc)
+            e = il::launch_gemm(b.fmt, x, static_xb, (int)t, (int)n_in, b.jobs.data(), nb, ctx->cu_count, s);
+        else
+            e = run_gemm(ctx, b.fmt, x, (int)t, (int)n_in, b.jobs.data(), nb, s, false);
+        if (e != hipSuccess) {
+            set_err("%s: kernel launch failed: %s", who, hipGetErrorString(e));
             g_failed++;
             return 0;
         }
+        ++launches;
     }
+    for (int64_t j = 0; j < n_jobs; ++j) bytes += (uint64_t)jobs[j].w->host_bytes;
     if (timing) {
         (void)hipEventRecord(ev1, s);
         (void)hipEventSynchronize(ev1);
@@ -664,6 +704,19 @@ int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64
     st.bytes += bytes;
     st.flops += flops;
     return 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64_t n_jobs, void *hip_stream) {
+    return matmul_impl("il_matmul", x, t, n_in, jobs, n_jobs, hip_stream, false);
+}
+
+int il_matmul_noalloc(const float *x, int64_t t, int64_t n_in, const il_job *jobs, int64_t n_jobs,
+                      void *hip_stream) {
+    return matmul_impl("il_matmul_noalloc", x, t, n_in, jobs, n_jobs, hip_stream, true);
 }
 
 int il_matmul_gelu_mul(const float *x, int64_t t, int64_t n_in, const il_weight *gate, const il_weight *up,

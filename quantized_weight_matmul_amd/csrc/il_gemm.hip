@@ -42,6 +42,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 namespace il {
@@ -628,7 +629,32 @@ Route route(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
     return {verify, slice};
 }
 
+// The buffer of il_matmul_noalloc's prefill path: one per device, for
+// callers that cannot allocate.  `scratch` names the host-side stand-in of
+// the array; kernels get its device address from static_scratch().
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+struct StaticScratch {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+StaticScratch g_static_scratch[kMaxScratchDevices];
+
 }  // namespace
+
+size_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t static_scratch(int device, void **ptr) {
+    *ptr = nullptr;
+    if (device < 0 || device >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    StaticScratch &st = g_static_scratch[device];
+    // once per device, with that device current (the caller's)
+    std::call_once(st.once, [&] { st.err = hipGetSymbolAddress(&st.ptr, HIP_SYMBOL(scratch)); });
+    if (st.err == hipSuccess) *ptr = st.ptr;
+    return st.err;
+}
 
 size_t gemm_scratch_bytes(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
     if (t <= kGemvMaxT || n_jobs < 1) return 0;

@@ -128,6 +128,11 @@ size_t gemm_scratch_bytes(int fmt, int t, int n_in, const KJob *jobs, int n_jobs
 // launch (or the wide-mode launches of mid-size t).
 hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_in, const KJob *jobs, int n_jobs,
                        int cu_count, hipStream_t s, bool glu = false);
+// The device's static scratch of il_matmul_noalloc (static_scratch_bytes()
+// bytes, 256-byte aligned, shared by every call on that device): its device
+// address, looked up on the first call for the device, which must be current.
+size_t static_scratch_bytes();
+hipError_t static_scratch(int device, void **ptr);
 
 // ---- centroid-masked LM head (il_lmhead.hip) ----
 // x [t][h] (t <= kGemvMaxT); centroids: a bf16 job [C][h]; embed bf16 [V][h]

@@ -46,6 +46,9 @@ def lib() -> ctypes.CDLL:
             L.il_matmul.restype = ctypes.c_int
             L.il_matmul.argtypes = [ctypes.c_void_p, _i64, _i64, ctypes.POINTER(il_job), _i64,
                                     ctypes.c_void_p]
+            L.il_matmul_noalloc.restype = ctypes.c_int
+            L.il_matmul_noalloc.argtypes = [ctypes.c_void_p, _i64, _i64, ctypes.POINTER(il_job), _i64,
+                                            ctypes.c_void_p]
             L.il_matmul_gelu_mul.restype = ctypes.c_int
             L.il_matmul_gelu_mul.argtypes = [ctypes.c_void_p, _i64, _i64, ctypes.c_void_p, ctypes.c_void_p, _i64,
                                              ctypes.c_void_p, ctypes.c_void_p]
@@ -162,6 +165,19 @@ def il_free(w: Weight) -> None:
     w.free()
 
 
+def _job_array(jobs):
+    arr = (il_job * max(1, len(jobs)))()
+    keep = []
+    for i, (w, n_out, y) in enumerate(jobs):
+        if w is None or not isinstance(w, Weight):
+            arr[i].w = None
+        else:
+            arr[i].w = w.handle
+        arr[i].n_out = int(n_out)
+        arr[i].y = _ptr(y)
+    return arr
+
+
 def il_matmul(x, t: int, n_in: int, jobs, stream=None) -> int:
     """Run every job over x in one submission.
 
@@ -172,23 +188,16 @@ def il_matmul(x, t: int, n_in: int, jobs, stream=None) -> int:
              current stream
     Returns 1 on success, 0 if nothing was computed (see il_last_error()).
     """
-    arr = (il_job * max(1, len(jobs)))()
-    keep = []
-    for i, (w, n_out, y) in enumerate(jobs):
-        if w is None or not isinstance(w, Weight):
-            arr[i].w = None
-        else:
-            arr[i].w = w.handle
-        arr[i].n_out = int(n_out)
-        arr[i].y = _ptr(y)
-        keep.append(y)
-    if stream is None:
-        import torch
-        stream = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
-    return int(lib().il_matmul(ctypes.c_void_p(_ptr(x)), int(t), int(n_in), arr, len(jobs),
-                               ctypes.c_void_p(int(stream))))
+    return int(lib().il_matmul(ctypes.c_void_p(_ptr(x)), int(t), int(n_in), _job_array(jobs), len(jobs),
+                               ctypes.c_void_p(int(_stream_handle(stream)))))
+
+
+def il_matmul_noalloc(x, t: int, n_in: int, jobs, stream=None) -> int:
+    """il_matmul that allocates nothing: the prefill path's bf16 copy of x
+    lives in the library's static 32 MiB buffer per device (t * n_in <= 2^24
+    where a copy is needed), shared by every call on the device."""
+    return int(lib().il_matmul_noalloc(ctypes.c_void_p(_ptr(x)), int(t), int(n_in), _job_array(jobs), len(jobs),
+                                       ctypes.c_void_p(int(_stream_handle(stream)))))
 
 
 def _stream_handle(stream):
