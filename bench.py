@@ -1,25 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the accelerator linear layer on one MI355X.
 
-One step = one il_matmul submission of the chosen workload (default: the
-fused bf16 decode, t = 1, three jobs [4096 | 1024 | 1024] x 4096 sharing one
-x).  Weights are uploaded once, off the timed path, as enough copies that one
-rotation through them exceeds 1 GiB, so every step streams its weights from
-HBM rather than from the 256 MiB last-level cache.  The K timed steps are
-captured in one HIP graph and replayed, bracketed by synchronisations, so the
-host's launch cost does not enter the per-step time.
+Default line (no --workload): the bf16 prefill, 2048 tokens of x through
+two bf16 weights [4096 | 14336] x 4096 in one il_matmul submission -- the
+largest configuration that fits one GPU.  One step = one such call.  The K
+timed steps are eager calls bracketed by synchronisations (host validation
+and launches included); weight copies are rotated so that one rotation
+exceeds 1 GiB and every step reads its weights from HBM, not from the
+256 MiB last-level cache.  value = TFLOP/s of whole calls.  `roofline` takes
+the GEMM kernel alone (HIP events the library records on the launch stream
+around each of the call's two kernels) against 2.5 PFLOP/s dense bf16; the
+same line carries the call's device time, the graph-replay time per call,
+the eager per-call cost beside the pages' ~0.15 ms dispatch figure, the
+inputs' SHA-256, the host CPU and the shader clock sampled under the load,
+a `cpu_baseline` (the oracle on the host cores, on the first 16 rows of x)
+and a `decode` object: weight GB/s against 8 TB/s of the decode workloads
+(fused bf16 t = 1, Q8 gate/up and down t = 1, Q4 t = 1, 2, 4, 8), each timed
+in a HIP graph of calls, with its eager per-call cost.
 
-Prints one JSON line: the weight GB/s of the decode path (or TFLOP/s for the
-prefill workloads), a `roofline` object for the kernel (HIP-event timing of
-each launch on its stream, against the 8 TB/s HBM or 2.5 PFLOP/s bf16 MFMA
-peak) and a `cpu_baseline` object (the oracle on the host cores, on a bounded
-sample of the same workload).
+--workload NAME times one workload alone (graph replay, or eager with
+--no-graph) and prints its own line in the same form.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -381,15 +388,310 @@ def bench_quantize(args, name: str) -> int:
     return 0
 
 
+# ------------------------------------------------------------ headline line
+DECODE_SET = ["c2", "c3a", "c3b", "c4_t1", "c4_t2", "c4_t4", "c4_t8"]
+PAGES_DISPATCH_US = 150.0  # Backend::wants doc comment, oxinfer 0.0.0 src/gpu.rs page (Metal)
+
+
+def host_info() -> dict:
+    model = ""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    return {"cpu_model": model, "nproc": os.cpu_count(), "oracle_threads": threads}
+
+
+def smi_clocks() -> dict:
+    """The GPU's current shader (sclk) and memory clocks from amd-smi, or
+    rocm-smi if amd-smi is missing; {} when neither answers."""
+    import re
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        except (OSError, subprocess.SubprocessError):
+            continue
+        if r.returncode != 0 or not r.stdout.strip():
+            continue
+        txt = r.stdout
+        out = {"tool": cmd[0]}
+        try:
+            d = json.loads(txt)
+        except ValueError:
+            d = None
+        # amd-smi: {"gpu_data": [{"gpu": 0, "clock": {"gfx_0": {"clk": {"value": 1805, "unit": "MHz"},
+        # ...}, ... one gfx_N per XCD, "mem_0": ...}}]}
+        if isinstance(d, dict) and isinstance(d.get("gpu_data"), list):
+            d = d["gpu_data"]
+        if isinstance(d, list) and d and isinstance(d[0], dict) and isinstance(d[0].get("clock"), dict):
+            clk = d[0]["clock"]
+
+            def vals(prefix):
+                v = [c.get("clk", {}).get("value") for k, c in clk.items() if k.startswith(prefix) and isinstance(c, dict)]
+                return [x for x in v if isinstance(x, (int, float))]
+            gfx, mem = vals("gfx"), vals("mem")
+            if gfx:
+                out["sclk_mhz"] = round(sum(gfx) / len(gfx), 1)
+                out["sclk_mhz_min_max"] = [min(gfx), max(gfx)]
+                out["xcds"] = len(gfx)
+            if mem:
+                out["mclk_mhz"] = max(mem)
+        if "sclk_mhz" not in out:
+            m = re.findall(r'sclk[^0-9]{0,40}?(\d{3,4})\s*Mhz', txt, flags=re.I)
+            if m:
+                out["sclk_mhz"] = max(int(v) for v in m)
+        if "sclk_mhz" in out:
+            return out
+        out["raw"] = txt[:300]
+        return out
+    return {}
+
+
+def clock_under_load(burst, seconds: float) -> dict:
+    """Shader clock while the GPU runs `burst` (a function that enqueues
+    calls for about `seconds`) in a background thread."""
+    import threading
+    th = threading.Thread(target=burst)
+    th.start()
+    time.sleep(min(0.5, seconds / 4))
+    c = smi_clocks()
+    th.join()
+    c["sampled"] = "during a burst of eager calls of the headline workload"
+    return c
+
+
+class Rig:
+    """One submission set up on the GPU: n_sets weight copies (rotated so a
+    rotation exceeds the last-level cache), x and y resident in HBM."""
+
+    def __init__(self, il, sub, x_np, weights, n_sets, cache=None):
+        import torch
+        self.il, self.sub = il, sub
+        self.sets = []
+        for k in range(n_sets):
+            key = (sub.cfg, sub.n_in, tuple(sub.jobs), k)
+            if cache is not None and key in cache:
+                self.sets.append(cache[key])
+                continue
+            hs = [il.il_upload(w, j.fmt, j.n_out, sub.n_in) for w, j in zip(weights, sub.jobs)]
+            if any(h is None for h in hs):
+                raise RuntimeError(il.il_last_error())
+            self.sets.append(hs)
+            if cache is not None:
+                cache[key] = hs
+        self.x = torch.from_numpy(x_np).cuda()
+        self.ys = [torch.empty((sub.t, j.n_out), dtype=torch.float32, device="cuda") for j in sub.jobs]
+
+    def step(self, i, s):
+        hs = self.sets[i % len(self.sets)]
+        jobs = [(h, j.n_out, y) for h, j, y in zip(hs, self.sub.jobs, self.ys)]
+        if self.il.il_matmul(self.x, self.sub.t, self.sub.n_in, jobs, s) != 1:
+            raise RuntimeError(self.il.il_last_error())
+
+
+def time_eager(step, steps: int, warmup: int, stream):
+    """K eager calls bracketed by synchronisations: (wall ms per call, device
+    ms per call from HIP events on the launch stream around the burst)."""
+    import torch
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(steps):
+            step(i, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def time_graph(step, steps: int, warmup: int, stream):
+    """K calls captured in one HIP graph and replayed: (wall ms per call,
+    device ms per call from HIP events around the replay)."""
+    import torch
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i, stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream, capture_error_mode="relaxed"):
+        for i in range(steps):
+            step(i, torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del g
+    return wall * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def prefill_kernel_split(il, step, calls: int, stream):
+    """Device time per call of the x -> bf16 pre-pass and of the GEMM launch,
+    from HIP events the library records on the launch stream around each of
+    them (IL_TIMING=1, eager calls)."""
+    import torch
+
+    def read():
+        for line in il.il_stats().splitlines():
+            if line.startswith("prefill_gemm:"):
+                f = dict(kv.split("=") for kv in line.split(":", 1)[1].split())
+                return float(f["device_ms"]), float(f["prepass_ms"]), int(f["split_calls"])
+        raise RuntimeError("no prefill_gemm line in il_stats")
+
+    os.environ["IL_TIMING"] = "1"
+    try:
+        d0, p0, n0 = read()
+        with torch.cuda.stream(stream):
+            for i in range(calls):
+                step(i, stream)
+        torch.cuda.synchronize()
+        d1, p1, n1 = read()
+    finally:
+        del os.environ["IL_TIMING"]
+    n = n1 - n0
+    if n != calls:
+        raise RuntimeError(f"{n} of {calls} timed prefill calls were split")
+    pre = (p1 - p0) / n
+    return (d1 - d0) / n - pre, pre
+
+
+def input_digests(sub, x_np, weights) -> dict:
+    import hashlib
+    h = lambda a: hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()[:16]
+    d = {"x": h(x_np)}
+    for j, w in zip(sub.jobs, weights):
+        d[f"w{j.tensor_id}"] = h(w)
+    return d
+
+
+def decode_entry(il, name: str, args, stream, cache) -> dict:
+    sub = wl.SUBMISSIONS[name]
+    x_np = wl.make_x(sub)
+    weights = wl.make_weights(sub)
+    n_sets = max(1, -(-ROTATE_BYTES // sub.weight_bytes))
+    rig = Rig(il, sub, x_np, weights, n_sets, cache)
+    steps = max(200, args.steps)
+    wall_g, dev_g = time_graph(rig.step, steps, 20, stream)
+    wall_e, _ = time_eager(rig.step, steps, 20, stream)
+    launches = len({j.fmt for j in sub.jobs})
+    achieved = sub.weight_bytes / (dev_g * 1e-3) / 1e9
+    e = {"workload": DESCRIPTIONS[name], "t": sub.t, "weight_bytes": sub.weight_bytes,
+         "kernel_ms": round(dev_g / launches, 6), "launches_per_call": launches,
+         "achieved_gbs": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBS, 4),
+         "traffic": measured_traffic(name), "graph_us_per_call": round(wall_g * 1e3, 3),
+         "eager_us_per_call": round(wall_e * 1e3, 3), "weight_sets_rotated": n_sets,
+         "dtype": path_dtype([wl.FMT_NAMES[j.fmt] for j in sub.jobs], sub.t),
+         "input_sha256_16": input_digests(sub, x_np, weights)}
+    log(f"[bench] {name}: kernel {e['kernel_ms'] * 1e3:.2f} us ({achieved:.0f} GB/s, {e['frac']:.3f} of HBM), "
+        f"graph {e['graph_us_per_call']:.2f} us/call, eager {e['eager_us_per_call']:.2f} us/call")
+    del rig
+    return e
+
+
+def bench_headline(args) -> int:
+    """The default line: the bf16 prefill (2048 tokens through [4096 | 14336]
+    x 4096, the largest configuration that fits one GPU) as TFLOP/s, with the
+    decode workloads' weight GB/s in a `decode` object beside it."""
+    import torch
+
+    import quantized_weight_matmul_amd as il
+    name = "c5a"
+    sub = wl.SUBMISSIONS[name]
+    log(f"[bench] headline workload {name}: {DESCRIPTIONS[name]}")
+    x_np = wl.make_x(sub)
+    weights = wl.make_weights(sub)
+    n_sets = max(1, -(-ROTATE_BYTES // sub.weight_bytes))
+    log(f"[bench] uploading {n_sets} weight sets x {sub.weight_bytes / 1e6:.1f} MB")
+    rig = Rig(il, sub, x_np, weights, n_sets)
+    stream = torch.cuda.Stream()  # default priority
+
+    # ---- timed region: K eager calls (host validation and launch included) ----
+    ms_per_step, dev_ms = time_eager(rig.step, args.steps, args.warmup, stream)
+    wall_g, dev_g = time_graph(rig.step, args.steps, args.warmup, stream)
+    gemm_ms, pre_ms = prefill_kernel_split(il, rig.step, max(20, min(args.steps, 100)), stream)
+    value = sub.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = sub.flops / (gemm_ms * 1e-3) / 1e12
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/call eager ({value:.1f} TFLOP/s), graph {wall_g * 1e3:.1f} us/call; "
+        f"GEMM kernel {gemm_ms * 1e3:.1f} us ({achieved:.1f} TFLOP/s), pre-pass {pre_ms * 1e3:.1f} us")
+
+    # ---- shader clock while the GEMM runs ----
+    def burst():
+        with torch.cuda.stream(stream):
+            for i in range(int(2.5 / max(dev_ms * 1e-3, 1e-4))):
+                rig.step(i, stream)
+        torch.cuda.synchronize()
+    clock = clock_under_load(burst, 2.5) if not args.no_clock else {}
+    log(f"[bench] clock under load: {clock}")
+    digests = input_digests(sub, x_np, weights)
+    del rig
+
+    decode = {}
+    if not args.no_decode:
+        cache = {}
+        for dn in DECODE_SET:
+            decode[dn] = decode_entry(il, dn, args, stream, cache)
+        cache.clear()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"[bench] oracle on the host cores for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(sub, x_np, weights, args.cpu_seconds)
+
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(name),
+                "kernel": "gemm_bf16_kernel", "kernel_ms": round(gemm_ms, 6), "prepass_ms": round(pre_ms, 6),
+                "call_device_ms": round(dev_ms, 6),
+                "call_frac": round(sub.flops / (dev_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "timing": "kernel_ms / prepass_ms: HIP events the library records on the launch stream around "
+                          "each of the call's two kernels (IL_TIMING=1, eager); call_device_ms: HIP events on "
+                          "the launch stream around the timed burst / calls"}
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: {DESCRIPTIONS[name]}", "t": sub.t, "n_in": sub.n_in,
+                   "jobs": [[wl.FMT_NAMES[j.fmt], j.n_out] for j in sub.jobs],
+                   "weight_bytes_per_step": sub.weight_bytes, "flops_per_step": sub.flops,
+                   "weight_sets_rotated": n_sets,
+                   "timing": "eager il_matmul calls, host validation and launches included",
+                   "eager_us_per_call": round(ms_per_step * 1e3, 3),
+                   "graph_us_per_call": round(wall_g * 1e3, 3),
+                   "pages_dispatch_cost_us": PAGES_DISPATCH_US,
+                   "input_sha256_16": digests, "host": host_info(), "gpu_clock": clock},
+        "roofline": roofline, "cpu_baseline": cpu, "decode": decode,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="c2",
-                    choices=sorted(wl.SUBMISSIONS) + sorted(wl.QUANTIZE) + sorted(wl.GELU_MUL) + sorted(wl.LM_HEAD))
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None,
+                    choices=sorted(wl.SUBMISSIONS) + sorted(wl.QUANTIZE) + sorted(wl.GELU_MUL) + sorted(wl.LM_HEAD),
+                    help="time one workload alone (default: the headline line, bf16 prefill c5a with the "
+                         "decode workloads beside it)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget (0: skip)")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--no-graph", action="store_true", help="single workload: time eager launches, not a graph")
+    ap.add_argument("--no-decode", action="store_true", help="headline line without the decode object")
+    ap.add_argument("--no-clock", action="store_true", help="headline line without sampling the shader clock")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -418,6 +720,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.workload is None:
+        return bench_headline(args)
     if args.workload in wl.QUANTIZE:
         return bench_quantize(args, args.workload)
     if args.workload in wl.GELU_MUL:
@@ -425,32 +729,16 @@ def main() -> int:
     if args.workload in wl.LM_HEAD:
         return bench_lm_head(args, args.workload)
     sub = wl.SUBMISSIONS[args.workload]
-    decode = sub.t <= 8
     streaming = sub.t <= STREAMING_MAX_T
     log(f"[bench] workload {sub.name}: {DESCRIPTIONS[sub.name]}")
     x_np = wl.make_x(sub)
     weights = wl.make_weights(sub)
     per_set = sub.weight_bytes
-    n_sets = max(1, -(-ROTATE_BYTES // per_set)) if streaming else 2
+    n_sets = max(1, -(-ROTATE_BYTES // per_set)) if streaming else max(2, -(-ROTATE_BYTES // per_set))
     log(f"[bench] uploading {n_sets} weight sets x {per_set / 1e6:.1f} MB")
-    sets = []
-    for _ in range(n_sets):
-        hs = [il.il_upload(w, j.fmt, j.n_out, sub.n_in) for w, j in zip(weights, sub.jobs)]
-        if any(h is None for h in hs):
-            raise RuntimeError(il.il_last_error())
-        sets.append(hs)
-    x = torch.from_numpy(x_np).cuda()
-    ys = [torch.empty((sub.t, j.n_out), dtype=torch.float32, device="cuda") for j in sub.jobs]
+    rig = Rig(il, sub, x_np, weights, n_sets)
     stream = torch.cuda.Stream()  # default priority
-
-    def step(i, s):
-        hs = sets[i % n_sets]
-        rc = il.il_matmul(x, sub.t, sub.n_in, [(h, j.n_out, y) for h, j, y in zip(hs, sub.jobs, ys)], s)
-        if rc != 1:
-            raise RuntimeError(il.il_last_error())
-
-    ms_per_step, kern_ms, pair_ms = time_steps(step, args, stream, len({j.fmt for j in sub.jobs}))
-    launches_per_step = len({j.fmt for j in sub.jobs})
+    ms_per_step, kern_ms, pair_ms = time_steps(rig.step, args, stream, len({j.fmt for j in sub.jobs}))
     return report(args, sub, per_set, n_sets, ms_per_step, kern_ms, pair_ms, x_np, weights)
 
 

@@ -174,7 +174,7 @@ hipError_t grow_scratch(DeviceCtx *ctx, StreamScratch *e, size_t need, bool *fal
 // One prefill launch group (pre-pass + GEMM, or the wide-mode launches) with
 // its scratch from the stream's cache.
 hipError_t run_gemm(DeviceCtx *ctx, int fmt, const float *x, int t, int n_in, const il::KJob *jobs, int n_jobs,
-                    hipStream_t s, bool glu) {
+                    hipStream_t s, bool glu, hipEvent_t after_prepass = nullptr) {
     const size_t need = il::gemm_scratch_bytes(fmt, t, n_in, jobs, n_jobs);
     if (need == 0) return il::launch_gemm(fmt, x, nullptr, t, n_in, jobs, n_jobs, ctx->cu_count, s, glu);
     StreamScratch *e = nullptr;
@@ -182,11 +182,11 @@ hipError_t run_gemm(DeviceCtx *ctx, int fmt, const float *x, int t, int n_in, co
     bool fallback = false;
     hipError_t err = grow_scratch(ctx, e, need, &fallback);
     if (err != hipSuccess) return err;
-    if (!fallback) return il::launch_gemm(fmt, x, e->ptr, t, n_in, jobs, n_jobs, ctx->cu_count, s, glu);
+    if (!fallback) return il::launch_gemm(fmt, x, e->ptr, t, n_in, jobs, n_jobs, ctx->cu_count, s, glu, after_prepass);
     void *tmp = nullptr;
     err = hipMallocAsync(&tmp, need, s);
     if (err != hipSuccess) return err;
-    err = il::launch_gemm(fmt, x, tmp, t, n_in, jobs, n_jobs, ctx->cu_count, s, glu);
+    err = il::launch_gemm(fmt, x, tmp, t, n_in, jobs, n_jobs, ctx->cu_count, s, glu, after_prepass);
     const hipError_t fe = hipFreeAsync(tmp, s);
     return err != hipSuccess ? err : fe;
 }
@@ -194,6 +194,9 @@ hipError_t run_gemm(DeviceCtx *ctx, int fmt, const float *x, int t, int n_in, co
 // ------------------------------------------------------------------ stats
 struct PathStats {
     std::atomic<uint64_t> calls{0}, launches{0}, jobs{0}, bytes{0}, flops{0}, timed_ns{0};
+    // prefill calls of one launch group timed with IL_TIMING=1: their count
+    // and the device time of the x -> bf16 pre-pass within timed_ns
+    std::atomic<uint64_t> split_calls{0}, prepass_ns{0};
 };
 PathStats g_stats[3];  // 0: decode GEMV, 1: prefill GEMM, 2: upload quantiser
 std::atomic<uint64_t> g_uploads{0}, g_upload_bytes{0}, g_failed{0};
@@ -664,10 +667,15 @@ int matmul_impl(const char *who, const float *x, int64_t t, int64_t n_in, const 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     PathStats &st = g_stats[decode ? 0 : 1];
     const bool timing = !noalloc && timing_on();
-    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    // a prefill call of one launch group also times its pre-pass apart
+    const bool split = timing && !decode && batches.size() == 1 &&
+                       il::gemm_scratch_bytes(batches[0].fmt, (int)t, (int)n_in, batches[0].jobs.data(),
+                                              (int)batches[0].jobs.size()) > 0;
+    hipEvent_t ev0 = nullptr, ev1 = nullptr, evm = nullptr;
     if (timing) {
         (void)hipEventCreate(&ev0);
         (void)hipEventCreate(&ev1);
+        if (split) (void)hipEventCreate(&evm);
         (void)hipEventRecord(ev0, s);
     }
     uint64_t launches = 0, bytes = 0;
@@ -679,7 +687,7 @@ int matmul_impl(const char *who, const float *x, int64_t t, int64_t n_in, const 
         else if (noalloc)
             e = il::launch_gemm(b.fmt, x, static_xb, (int)t, (int)n_in, b.jobs.data(), nb, ctx->cu_count, s);
         else
-            e = run_gemm(ctx, b.fmt, x, (int)t, (int)n_in, b.jobs.data(), nb, s, false);
+            e = run_gemm(ctx, b.fmt, x, (int)t, (int)n_in, b.jobs.data(), nb, s, false, evm);
         if (e != hipSuccess) {
             set_err("%s: kernel launch failed: %s", who, hipGetErrorString(e));
             g_failed++;
@@ -693,8 +701,14 @@ int matmul_impl(const char *who, const float *x, int64_t t, int64_t n_in, const 
         (void)hipEventSynchronize(ev1);
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, ev0, ev1) == hipSuccess) st.timed_ns += (uint64_t)(ms * 1e6);
+        float pms = 0.f;
+        if (split && hipEventElapsedTime(&pms, ev0, evm) == hipSuccess) {
+            st.split_calls++;
+            st.prepass_ns += (uint64_t)(pms * 1e6);
+        }
         (void)hipEventDestroy(ev0);
         (void)hipEventDestroy(ev1);
+        if (evm) (void)hipEventDestroy(evm);
     }
     uint64_t flops = 0;
     for (int64_t j = 0; j < n_jobs; ++j) flops += 2ull * (uint64_t)t * (uint64_t)jobs[j].n_out * (uint64_t)n_in;
@@ -902,15 +916,16 @@ const char *il_name(void) { return "il-hip-gfx950"; }
 
 int64_t il_stats(char *buf, int64_t cap) {
     std::string s;
-    char line[256];
+    char line[512];
     const char *names[3] = {"decode_gemv", "prefill_gemm", "upload_quantize"};
     for (int i = 0; i < 3; ++i) {
         const PathStats &p = g_stats[i];
         snprintf(line, sizeof line,
                  "%s: calls=%" PRIu64 " launches=%" PRIu64 " jobs=%" PRIu64 " weight_bytes=%" PRIu64
-                 " flops=%" PRIu64 " device_ms=%.3f\n",
+                 " flops=%" PRIu64 " device_ms=%.3f split_calls=%" PRIu64 " prepass_ms=%.3f\n",
                  names[i], (uint64_t)p.calls, (uint64_t)p.launches, (uint64_t)p.jobs,
-                 (uint64_t)p.bytes, (uint64_t)p.flops, (double)p.timed_ns / 1e6);
+                 (uint64_t)p.bytes, (uint64_t)p.flops, (double)p.timed_ns / 1e6, (uint64_t)p.split_calls,
+                 (double)p.prepass_ns / 1e6);
         s += line;
     }
     snprintf(line, sizeof line, "uploads: count=%" PRIu64 " bytes=%" PRIu64 "\nfailed_calls: %" PRIu64 "\n",

@@ -664,7 +664,7 @@ size_t gemm_scratch_bytes(int fmt, int t, int n_in, const KJob *jobs, int n_jobs
 }
 
 hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_in, const KJob *jobs, int n_jobs,
-                       int cu_count, hipStream_t s, bool glu) {
+                       int cu_count, hipStream_t s, bool glu, hipEvent_t after_prepass) {
     if (t < 1 || n_jobs < 1 || n_jobs > kMaxJobs || n_in % kBlock || cu_count < 1) return hipErrorInvalidValue;
     if (glu && (n_jobs != 2 || jobs[0].n_out != jobs[1].n_out)) return hipErrorInvalidValue;
     // every buffer descriptor (256 rows of x or of a weight) must stay below 2^31 bytes
@@ -679,6 +679,7 @@ hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_i
     hipLaunchKernelGGL(x_to_bf16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x,
                        reinterpret_cast<uint4 *>(xb), n8);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && after_prepass) e = hipEventRecord(after_prepass, s);
     if (e != hipSuccess) return e;
     if (r.verify) {
         // one launch per slice of tokens; slice i's x rows and y rows start

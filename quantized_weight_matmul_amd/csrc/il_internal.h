@@ -126,8 +126,10 @@ size_t gemm_scratch_bytes(int fmt, int t, int n_in, const KJob *jobs, int n_jobs
 // aligned, that nothing else uses until the stream has passed this call (may
 // be null when that size is 0).  Enqueues the x -> bf16 pre-pass and one GEMM
 // launch (or the wide-mode launches of mid-size t).
+// after_prepass: when not null, recorded on s between the pre-pass and the
+// GEMM launch (device timing of the two kernels apart).
 hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_in, const KJob *jobs, int n_jobs,
-                       int cu_count, hipStream_t s, bool glu = false);
+                       int cu_count, hipStream_t s, bool glu = false, hipEvent_t after_prepass = nullptr);
 // The device's static scratch of il_matmul_noalloc (static_scratch_bytes()
 // bytes, 256-byte aligned, shared by every call on that device): its device
 // address, looked up on the first call for the device, which must be current.
