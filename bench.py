@@ -679,6 +679,50 @@ def bench_headline(args) -> int:
     return 0
 
 
+def calibrate_read(sizes_mb) -> int:
+    """The read ceiling: il_read_probe (a plain streaming read, no arithmetic)
+    over buffers of the given sizes, rotated so that one rotation exceeds
+    1 GiB, in a sweep of launch shapes; prints one JSON line with the best
+    shape and rate per size."""
+    import torch
+
+    import quantized_weight_matmul_amd as il
+    stream = torch.cuda.Stream()
+    out = {"metric": "plain streaming read GB/s (il_read_probe), best launch shape per size",
+           "unit": "GB/s", "peak": HBM_PEAK_GBS, "sizes": {}}
+    for mb in sizes_mb:
+        nbytes = int(mb * 1e6) // 16 * 16
+        n_bufs = max(1, -(-ROTATE_BYTES // nbytes))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(k) for k in range(n_bufs)]
+        sink = torch.empty(nbytes // 1024 + 1, dtype=torch.int32, device="cuda")
+        rows = []
+        for waves in (4, 8, 16):
+            for chunk_kib in (16, 32, 64, 128, 256):
+                chunk = chunk_kib * 1024
+                for depth in (2, 4, 8):
+                    if chunk < 64 * waves * 16 * depth:
+                        continue  # fewer bytes than one round of the ring
+                    def launch(i, s):
+                        if il.il_read_probe(bufs[i % n_bufs], nbytes, chunk, waves, depth, sink,
+                                            sink.numel() * 4, s) != 1:
+                            raise RuntimeError(il.il_last_error())
+                    _, dev_ms = time_eager(launch, 40, 8, stream)
+                    gbs = nbytes / (dev_ms * 1e-3) / 1e9
+                    rows.append({"waves": waves, "chunk_kib": chunk_kib, "depth": depth,
+                                 "workgroups": -(-nbytes // chunk), "us": round(dev_ms * 1e3, 2),
+                                 "gbs": round(gbs, 1)})
+        rows.sort(key=lambda r: -r["gbs"])
+        best = rows[0]
+        log(f"[read] {mb} MB: best {best['gbs']:.0f} GB/s ({best['gbs'] / HBM_PEAK_GBS:.3f} of peak) with "
+            f"{best['waves']} waves x {best['chunk_kib']} KiB, depth {best['depth']} ({best['us']} us); "
+            f"next {[(r['waves'], r['chunk_kib'], r['depth'], r['gbs']) for r in rows[1:4]]}")
+        out["sizes"][f"{mb}MB"] = {"bytes": nbytes, "buffers_rotated": n_bufs, "best": best,
+                                   "frac_of_peak": round(best["gbs"] / HBM_PEAK_GBS, 4), "top5": rows[:5]}
+        del bufs
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -692,6 +736,9 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="single workload: time eager launches, not a graph")
     ap.add_argument("--no-decode", action="store_true", help="headline line without the decode object")
     ap.add_argument("--no-clock", action="store_true", help="headline line without sampling the shader clock")
+    ap.add_argument("--calibrate-read", default="", metavar="MB[,MB...]",
+                    help="only time a plain streaming read (il_read_probe) of buffers of these sizes in a "
+                         "sweep of launch shapes: the read ceiling of the decode kernels")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -707,6 +754,9 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"[bench] copied {args.calibrate_copy} MiB five times")
         return 0
+
+    if args.calibrate_read:
+        return calibrate_read([float(v) for v in args.calibrate_read.split(",")])
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "

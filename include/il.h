@@ -215,12 +215,14 @@ IL_API int il_matmul_gelu_mul(const float *x, int64_t t, int64_t n_in, const il_
  *   x          : DEVICE float[t][h], 16-byte aligned; 1 <= t <= 8.
  *   centroids  : bf16 handle [C, h];  embed : bf16 handle [V, h], V % C == 0.
  *   ordering   : DEVICE uint32[V]; entries >= V are skipped (never chosen).
- *   top_k      : 1 <= top_k <= C; (C + h + 2 * next_pow2(top_k)) * 4 bytes
- *                must fit in 152 KiB (one workgroup's LDS less 8 KiB).
+ *   top_k      : >= 1; a value above C means every cluster (k = min(top_k,
+ *                C), as the page's `top_k_centroids.min(num_centroids)`);
+ *                (C + h + 2 * next_pow2(k)) * 4 bytes must fit in 152 KiB
+ *                (one workgroup's LDS less 8 KiB).
  *   token      : DEVICE int32[t]: the chosen token (-1 if every candidate of
  *                the row was skipped).
- *   clusters   : DEVICE int32[t][top_k] or NULL: the chosen clusters in
- *                visiting order.
+ *   clusters   : DEVICE int32[t][k] or NULL: the chosen clusters in
+ *                visiting order (k = min(top_k, C)).
  *   score      : DEVICE float[t] or NULL: the chosen token's score.
  *   workspace  : DEVICE scratch of at least il_centroid_argmax_workspace(t,
  *                C, top_k) bytes, owned by the caller and not used by
@@ -235,7 +237,8 @@ IL_API int il_centroid_argmax(const float *x, int64_t t, int64_t h, const il_wei
                               void *hip_stream);
 
 /* Bytes of workspace il_centroid_argmax needs for t rows, C centroids and
- * top_k clusters (t * (C + 2 * top_k) * 4); -1 for sizes it does not take. */
+ * top_k clusters (t * (C + 2 * k) * 4 with k = min(top_k, C)); -1 for sizes
+ * it does not take. */
 IL_API int64_t il_centroid_argmax_workspace(int64_t t, int64_t n_centroids, int64_t top_k);
 
 /* Backend::wants -- whether a matmul of these dimensions is worth running on
@@ -244,6 +247,24 @@ IL_API int64_t il_centroid_argmax_workspace(int64_t t, int64_t n_centroids, int6
  * the threshold (default 2^18 flops, IL_WANTS_MIN_FLOP in the environment
  * overrides it), else 0.  Advisory only: il_matmul never consults it. */
 IL_API int il_wants(int64_t n_out, int64_t n_in, int64_t t);
+
+/* Measurement aid, not part of the layer: a plain streaming read of
+ * `bytes` bytes of device memory with no arithmetic beside the loads -- the
+ * ceiling the decode kernels' weight bandwidth (the GB/s of
+ * `WeightRef::bytes`) is compared with.
+ *   buf        : DEVICE pointer, `bytes` readable bytes (bytes >= 1).
+ *   chunk      : bytes per workgroup, a multiple of 16 in [1024, 2^31);
+ *                ceil(bytes / chunk) workgroups.
+ *   waves      : waves per workgroup, 1..16.
+ *   depth      : 16-byte loads in flight per lane: 1, 2, 4, 8 or 16.
+ *   sink       : DEVICE buffer of at least 4 * ceil(bytes / chunk) bytes
+ *                (sink_bytes); one word per workgroup is written (an XOR of
+ *                the words it read), so the loads cannot be optimised away.
+ *   hip_stream : as for il_matmul.
+ * Asynchronous; returns 1 after enqueueing, 0 on bad arguments (reason in
+ * il_last_error()). */
+IL_API int il_read_probe(const void *buf, int64_t bytes, int64_t chunk, int waves, int depth, void *sink,
+                         int64_t sink_bytes, void *hip_stream);
 
 /* Backend::name -- a static string naming this backend. */
 IL_API const char *il_name(void);

@@ -250,8 +250,10 @@ class Oracle:
     def centroid_argmax(self, x, centroids, embed, ordering, k: int) -> dict:
         """Centroid-masked LM head per row of x [t, h]: centroids bf16 bits
         [C, h], embed bf16 bits [V, h], ordering uint32 [V], k clusters.
-        Returns token [t], clusters [t, k] (visiting order), score [t] (f32),
-        cl and cl_bound [t, C] (exact f64 logits and sum |x*w|)."""
+        Returns token [t], clusters [t, min(k, C)] (visiting order), score [t]
+        (f32), cl and cl_bound [t, C] (exact f64 logits and sum |x*w|).  A k
+        above C takes every cluster (`top_k_centroids.min(num_centroids)` in
+        Drafter::step, oxinfer 0.0.1 src/drafter.rs page)."""
         x = np.ascontiguousarray(x, dtype=np.float32)
         t, h = x.shape
         cen = np.ascontiguousarray(centroids, dtype=np.uint16)
@@ -260,7 +262,7 @@ class Oracle:
         n_c, vocab = cen.shape[0], emb.shape[0]
         if cen.shape[1] != h or emb.shape[1] != h or order.shape != (vocab,):
             raise ValueError("shape mismatch")
-        out = {"token": np.empty(t, np.int32), "clusters": np.empty((t, k), np.int32),
+        out = {"token": np.empty(t, np.int32), "clusters": np.empty((t, min(int(k), n_c)), np.int32),
                "score": np.empty(t, np.float32), "cl": np.empty((t, n_c), np.float64),
                "cl_bound": np.empty((t, n_c), np.float64)}
         if self.lib.orc_centroid_argmax(_p(x), t, h, _p(cen), n_c, _p(emb), vocab, _p(order), k,

@@ -455,7 +455,8 @@ int orc_centroid_argmax(const float *x, int64_t t, int64_t h, const uint16_t *ce
                         const uint16_t *embed, int64_t vocab, const uint32_t *ordering, int64_t k,
                         int32_t *token, int32_t *clusters, float *score, double *cl, double *cl_bound)
 {
-    if (t < 0 || h <= 0 || n_c <= 0 || k < 1 || k > n_c || vocab < n_c || vocab % n_c) return -1;
+    if (t < 0 || h <= 0 || n_c <= 0 || k < 1 || vocab < n_c || vocab % n_c) return -1;
+    if (k > n_c) k = n_c; /* the page takes top_k_centroids.min(num_centroids) */
     const int64_t per = vocab / n_c;
     for (int64_t v = 0; v < vocab; ++v)
         if (ordering[v] >= (uint64_t)vocab) return -1;

@@ -23,7 +23,7 @@ One decode step over three projections that share x::
 from .il import (  # noqa: F401
     IL_BF16, IL_Q4, IL_Q8, IL_SRC_BF16, IL_SRC_F32, LIB_PATH, Weight, il_centroid_argmax,
     il_centroid_argmax_workspace, il_download, il_free,
-    il_last_error, il_matmul, il_matmul_gelu_mul, il_matmul_noalloc, il_name, il_stats, il_upload, il_upload_quantize, il_wants,
+    il_last_error, il_matmul, il_matmul_gelu_mul, il_matmul_noalloc, il_name, il_read_probe, il_stats, il_upload, il_upload_quantize, il_wants,
     il_weight_bytes,
 )
 
@@ -31,7 +31,7 @@ __all__ = [
     "IL_BF16", "IL_Q8", "IL_Q4", "IL_SRC_F32", "IL_SRC_BF16", "LIB_PATH", "Weight", "il_upload",
     "il_upload_quantize", "il_download", "il_free", "il_matmul", "il_matmul_noalloc", "il_matmul_gelu_mul", "il_centroid_argmax",
     "il_centroid_argmax_workspace",
-    "il_wants", "il_name",
+    "il_wants", "il_name", "il_read_probe",
     "il_stats",
     "il_weight_bytes", "il_last_error",
 ]

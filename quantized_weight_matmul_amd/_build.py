@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libil.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["il_api.cpp", "il_repack.hip", "il_gemv.hip", "il_gemv_mfma.hip", "il_gemm.hip", "il_lmhead.hip"]
+SOURCES = ["il_api.cpp", "il_repack.hip", "il_gemv.hip", "il_gemv_mfma.hip", "il_gemm.hip", "il_lmhead.hip", "il_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -814,8 +814,8 @@ int il_matmul_gelu_mul(const float *x, int64_t t, int64_t n_in, const il_weight 
 }
 
 int64_t il_centroid_argmax_workspace(int64_t t, int64_t n_centroids, int64_t top_k) {
-    if (t < 0 || n_centroids < 1 || top_k < 1 || t > il::kGemvMaxT || n_centroids > INT_MAX || top_k > INT_MAX)
-        return -1;
+    if (t < 0 || n_centroids < 1 || top_k < 1 || t > il::kGemvMaxT || n_centroids > INT_MAX) return -1;
+    if (top_k > n_centroids) top_k = n_centroids;
     return (int64_t)il::lm_head_workspace_bytes((int)t, (int)n_centroids, (int)top_k);
 }
 
@@ -846,10 +846,11 @@ int il_centroid_argmax(const float *x, int64_t t, int64_t h, const il_weight *ce
                 n_c);
         return 0;
     }
-    if (top_k < 1 || top_k > n_c) {
-        set_err("il_centroid_argmax: top_k = %" PRId64 " outside [1, %" PRId64 "]", top_k, n_c);
+    if (top_k < 1) {
+        set_err("il_centroid_argmax: top_k = %" PRId64 " must be at least 1", top_k);
         return 0;
     }
+    if (top_k > n_c) top_k = n_c;  // Drafter::step: k = top_k_centroids.min(num_centroids)
     if (il::lm_head_lds_bytes((int)n_c, (int)h, (int)top_k) > il::kLmHeadMaxLds) {
         set_err("il_centroid_argmax: %" PRId64 " centroids and h = %" PRId64 " exceed the LDS of one workgroup", n_c, h);
         return 0;
@@ -898,6 +899,32 @@ int il_centroid_argmax(const float *x, int64_t t, int64_t h, const il_weight *ce
     st.jobs += 1;
     st.bytes += (uint64_t)(centroids->host_bytes + t * top_k * (vocab / n_c) * h * 2);
     st.flops += 2ull * (uint64_t)t * (uint64_t)h * (uint64_t)(n_c + top_k * (vocab / n_c));
+    return 1;
+}
+
+int il_read_probe(const void *buf, int64_t bytes, int64_t chunk, int waves, int depth, void *sink,
+                  int64_t sink_bytes, void *hip_stream) {
+    g_err.clear();
+    if (!buf || !sink || bytes <= 0 || chunk < 1024 || chunk % 16 || chunk >= (1ll << 31) || waves < 1 ||
+        waves > 16 || (depth != 1 && depth != 2 && depth != 4 && depth != 8 && depth != 16)) {
+        set_err("il_read_probe: bad arguments (chunk a multiple of 16 in [1024, 2^31), waves 1..16, depth 1, 2, 4, "
+                "8 or 16)");
+        return 0;
+    }
+    int dev = -1;
+    if (!context(&dev)) return 0;
+    const int64_t grid = (bytes + chunk - 1) / chunk;
+    if (sink_bytes < grid * 4) {
+        set_err("il_read_probe: sink of %" PRId64 " bytes, %" PRId64 " needed", sink_bytes, grid * 4);
+        return 0;
+    }
+    if (!device_range_ok(buf, bytes, "buf") || !device_range_ok(sink, grid * 4, "sink")) return 0;
+    const hipError_t e = il::launch_read_probe(buf, bytes, chunk, waves, depth, static_cast<uint32_t *>(sink),
+                                               static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) {
+        set_err("il_read_probe: launch failed: %s", hipGetErrorString(e));
+        return 0;
+    }
     return 1;
 }
 

@@ -24,6 +24,7 @@
 //     are bitwise reproducible.
 #include "il_internal.h"
 
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -521,12 +522,18 @@ hipError_t launch_stream(const GemvParams &p, hipStream_t s) {
     const size_t lds = stream_lds_bytes<FMT, P>(T, p.n_in);
     auto kern = gemv_stream_kernel<FMT, T, R, P, GLU>;
     if (lds > 64 * 1024) {
-        static bool raised = false;  // benign race: the attribute is idempotent
-        if (!raised) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, kStreamMaxLds);
+        // the attribute belongs to the kernel on the current device: raised
+        // once per device (bit d of `raised`; a benign race, it is idempotent)
+        static std::atomic<uint64_t> raised{0};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+        if (!bit || !(raised.load(std::memory_order_relaxed) & bit)) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kStreamMaxLds);
             if (e != hipSuccess) return e;
-            raised = true;
+            raised.fetch_or(bit, std::memory_order_relaxed);
         }
     }
     const int rows_per_block = kStreamWaves * (GLU ? R / 2 : R);

@@ -136,6 +136,12 @@ hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_i
 size_t static_scratch_bytes();
 hipError_t static_scratch(int device, void **ptr);
 
+// ---- plain streaming read of device memory (il_probe.hip) ----
+// Workgroups of `waves` waves each read `chunk` bytes (16 per lane per load,
+// `depth` loads in flight per lane); sink gets one word per workgroup.
+hipError_t launch_read_probe(const void *buf, int64_t bytes, int64_t chunk, int waves, int depth, uint32_t *sink,
+                             hipStream_t s);
+
 // ---- centroid-masked LM head (il_lmhead.hip) ----
 // x [t][h] (t <= kGemvMaxT); centroids: a bf16 job [C][h]; embed bf16 [V][h]
 // with V % C == 0; ordering [V] (entries < V); 1 <= k <= C.  Writes token[t]

@@ -58,6 +58,9 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_void_p, ctypes.c_void_p, _i64, ctypes.c_void_p]
             L.il_centroid_argmax_workspace.restype = _i64
             L.il_centroid_argmax_workspace.argtypes = [_i64, _i64, _i64]
+            L.il_read_probe.restype = ctypes.c_int
+            L.il_read_probe.argtypes = [ctypes.c_void_p, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        _i64, ctypes.c_void_p]
             L.il_wants.restype = ctypes.c_int
             L.il_wants.argtypes = [_i64, _i64, _i64]
             L.il_name.restype = ctypes.c_char_p
@@ -235,6 +238,14 @@ def il_centroid_argmax(x, t: int, h: int, centroids: Weight, embed: Weight, orde
 
 def il_centroid_argmax_workspace(t: int, n_centroids: int, top_k: int) -> int:
     return int(lib().il_centroid_argmax_workspace(int(t), int(n_centroids), int(top_k)))
+
+
+def il_read_probe(buf, nbytes: int, chunk: int, waves: int, depth: int, sink, sink_bytes: int, stream=None) -> int:
+    """Plain streaming read of nbytes of device memory (a measurement aid);
+    1 after enqueueing, 0 on bad arguments."""
+    return int(lib().il_read_probe(ctypes.c_void_p(_ptr(buf)), int(nbytes), int(chunk), int(waves), int(depth),
+                                   ctypes.c_void_p(_ptr(sink)), int(sink_bytes),
+                                   ctypes.c_void_p(int(_stream_handle(stream)))))
 
 
 def il_wants(n_out: int, n_in: int, t: int) -> int:

@@ -354,6 +354,24 @@ def pin_lm_head_integers(O):
         assert np.array_equal(r["score"].astype(np.float64), sc), "score"
 
 
+def pin_lm_head_topk_clamp(O):
+    """k above the number of clusters takes all of them: the page's
+    `let k = self.top_k_centroids.min(self.num_centroids)` in Drafter::step
+    (oxinfer 0.0.1 src/drafter.rs), checked against brute force with k = C."""
+    rng = np.random.default_rng(43)
+    h, n_c, per = 16, 6, 3
+    vocab = n_c * per
+    x = rng.integers(-3, 4, (2, h))
+    cen = rng.integers(-2, 3, (n_c, h))
+    emb = rng.integers(-2, 3, (vocab, h))
+    order = rng.permutation(vocab).astype(np.uint32)
+    tok, clus, sc = _lm_head_brute(x, cen, emb, order, n_c)
+    for k in (n_c, n_c + 1, 4 * n_c):
+        r = O.centroid_argmax(x.astype(np.float32), _bf16_of_ints(cen), _bf16_of_ints(emb), order, k)
+        assert r["clusters"].shape == (2, n_c), f"k={k}: clusters shape {r['clusters'].shape}"
+        assert np.array_equal(r["clusters"], clus) and np.array_equal(r["token"], tok), f"k={k}"
+
+
 def pin_lm_head_random(O):
     rng = np.random.default_rng(41)
     t, h, n_c, per, k = 3, 64, 32, 8, 4
@@ -679,7 +697,7 @@ ALL_PINS = [
     pin_numpy_matmul, pin_points_equal_rows, pin_thread_invariance, pin_check_rule,
     pin_f16_rounding, pin_quantize_hand, pin_quantize_roundtrip, pin_quantize_nearest,
     pin_gelu_values, pin_gelu_mul_onehot, pin_gelu_mul_composition,
-    pin_lm_head_integers, pin_lm_head_random, pin_token_score,
+    pin_lm_head_integers, pin_lm_head_random, pin_token_score, pin_lm_head_topk_clamp,
 ]
 
 

@@ -24,7 +24,8 @@ def test_header_declares_the_abi():
     assert header_symbols() == sorted([
         "il_upload", "il_upload_quantize", "il_download", "il_free", "il_matmul", "il_matmul_noalloc",
         "il_matmul_gelu_mul",
-        "il_centroid_argmax", "il_centroid_argmax_workspace", "il_wants", "il_name", "il_stats", "il_weight_bytes", "il_last_error"])
+        "il_centroid_argmax", "il_centroid_argmax_workspace", "il_read_probe", "il_wants", "il_name", "il_stats",
+        "il_weight_bytes", "il_last_error"])
 
 
 def test_library_exports_every_declared_symbol():

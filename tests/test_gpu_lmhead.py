@@ -25,17 +25,19 @@ pytestmark = [pytest.mark.gpu,
 TOL = 4e-3
 
 
-def _run(x, cen, emb, order, k, workspace=False):
+def _run(x, cen, emb, order, k, workspace=False, k_out=None):
+    """k_out: columns of the clusters output (min(k, C), the clusters visited)."""
     import torch
     t, h = x.shape
     n_c, vocab = cen.shape[0], emb.shape[0]
+    k_out = k if k_out is None else k_out
     hc = il.il_upload(cen, il.IL_BF16, n_c, h)
     he = il.il_upload(emb, il.IL_BF16, vocab, h)
     assert hc is not None and he is not None, il.il_last_error()
     xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
     od = torch.from_numpy(order.view(np.int32)).cuda()
     tok = torch.full((t,), -7, dtype=torch.int32, device="cuda")
-    clu = torch.full((t, k), -7, dtype=torch.int32, device="cuda")
+    clu = torch.full((t, k_out), -7, dtype=torch.int32, device="cuda")
     sc = torch.full((t,), np.nan, dtype=torch.float32, device="cuda")
     ws = None
     if workspace:  # caller-owned scratch, filled with junk first
@@ -124,6 +126,25 @@ def test_lm_head_workload_full():
     _check_valid(x, cen, emb, order, k, tok, clu, sc)
 
 
+def test_lm_head_top_k_above_clusters():
+    """top_k above C takes every cluster (Drafter::step: k =
+    top_k_centroids.min(num_centroids)); the result equals top_k = C and the
+    oracle's, exactly (integer inputs)."""
+    rng = np.random.default_rng(11)
+    t, h, n_c, per = 2, 64, 12, 5
+    vocab = n_c * per
+    to_bf = lambda a: wl.f32_to_bf16_bits(a.astype(np.float32))
+    x = _ints(rng, (t, h), -3, 3).astype(np.float32)
+    cen, emb = to_bf(_ints(rng, (n_c, h), -2, 2)), to_bf(_ints(rng, (vocab, h), -2, 2))
+    order = rng.permutation(vocab).astype(np.uint32)
+    ref = oracle.centroid_argmax(x, cen, emb, order, n_c)
+    for k in (n_c, n_c + 1, 100):
+        say(f"[lm_head] top_k={k} C={n_c}")
+        tok, clu, sc = _run(x, cen, emb, order, k, k_out=min(k, n_c), workspace=True)
+        assert np.array_equal(clu, ref["clusters"]) and np.array_equal(tok, ref["token"]), f"top_k={k}"
+        assert np.array_equal(sc, ref["score"]), f"top_k={k}"
+
+
 def test_lm_head_skips_out_of_range_ordering_and_rejects_bad_calls():
     import torch
     rng = np.random.default_rng(3)
@@ -141,7 +162,7 @@ def test_lm_head_skips_out_of_range_ordering_and_rejects_bad_calls():
     xd = torch.from_numpy(x).cuda()
     od = torch.zeros(vocab, dtype=torch.int32, device="cuda")
     out = torch.full((1,), 9, dtype=torch.int32, device="cuda")
-    assert il.il_centroid_argmax(xd, 1, h, hc, he, od, n_c + 1, out) == 0 and "top_k" in il.il_last_error()
+    assert il.il_centroid_argmax(xd, 1, h, hc, he, od, 0, out) == 0 and "top_k" in il.il_last_error()
     assert il.il_centroid_argmax(xd, 1, h, hq, he, od, 1, out) == 0 and "bf16" in il.il_last_error()
     assert il.il_centroid_argmax(xd, 1, h, he, hc, od, 1, out) == 0 and "multiple" in il.il_last_error()
     big = il.il_upload(np.zeros((40000, h), np.uint16), il.IL_BF16, 40000, h)  # (40000 + h + 2) * 4 > 152 KiB

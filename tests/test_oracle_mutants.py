@@ -61,6 +61,7 @@ MUTANTS = {
     "lm_ordering_index": ("const uint32_t tok = ordering[c * per + j];", "const uint32_t tok = ordering[j * n_c + c];"),
     "lm_token_row_offset": ("embed + (size_t)tok * (size_t)h, x, h, bound", "embed + (size_t)tok, x, h, bound"),
     "lm_token_bound_signed": ("        m += fabs(p);", "        m += p;"),
+    "lm_topk_unclamped": ("if (k > n_c) k = n_c;", "if (k > n_c) return -1;"),
     "lm_x_row": ("const float *xi = x + (size_t)i * (size_t)h;", "const float *xi = x;"),
     "gelu_half": ("return 0.5 * v * (1.0 + erf(v / sqrt(2.0)));", "return v * (1.0 + erf(v / sqrt(2.0)));"),
     "gelu_erf_argument": ("erf(v / sqrt(2.0))", "erf(v)"),
