@@ -195,14 +195,30 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], const KJ
     }
 }
 
-// x f32 -> bf16 (RNE) pre-pass: 8 elements per thread.
+// x f32 -> bf16 (RNE) pre-pass: groups of 8 elements (32 bytes in, 16 out);
+// a workgroup covers kPreGroups * 256 consecutive groups, thread i the groups
+// i, i + 256, ..., all of whose loads are issued before the first store.
+constexpr int kPreGroups = 4;
 __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float *__restrict__ x, uint4 *__restrict__ xb,
                                                         int64_t n8) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const float4 a = reinterpret_cast<const float4 *>(x)[2 * i];
-    const float4 b = reinterpret_cast<const float4 *>(x)[2 * i + 1];
-    xb[i] = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
+    const int64_t g0 = (int64_t)blockIdx.x * (256 * kPreGroups) + threadIdx.x;
+    const float4 *x4 = reinterpret_cast<const float4 *>(x);
+    float4 a[kPreGroups], b[kPreGroups];
+#pragma unroll
+    for (int u = 0; u < kPreGroups; ++u) {
+        const int64_t g = g0 + u * 256;
+        if (g < n8) {
+            a[u] = x4[2 * g];
+            b[u] = x4[2 * g + 1];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kPreGroups; ++u) {
+        const int64_t g = g0 + u * 256;
+        if (g < n8)
+            xb[g] = make_uint4(pack_bf16(a[u].x, a[u].y), pack_bf16(a[u].z, a[u].w), pack_bf16(b[u].x, b[u].y),
+                               pack_bf16(b[u].z, b[u].w));
+    }
 }
 
 // ----------------------------------------------------------- Q8 / Q4 units
@@ -676,8 +692,8 @@ hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_i
     // x -> bf16 into the caller's scratch
     const int64_t n8 = (int64_t)t * n_in / 8;
     uint16_t *xb = static_cast<uint16_t *>(xb_scratch);
-    hipLaunchKernelGGL(x_to_bf16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x,
-                       reinterpret_cast<uint4 *>(xb), n8);
+    hipLaunchKernelGGL(x_to_bf16_kernel, dim3((unsigned)((n8 + 256 * kPreGroups - 1) / (256 * kPreGroups))), dim3(256),
+                       0, s, x, reinterpret_cast<uint4 *>(xb), n8);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && after_prepass) e = hipEventRecord(after_prepass, s);
     if (e != hipSuccess) return e;
