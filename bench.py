@@ -93,10 +93,11 @@ def kernel_source_sha(name: str) -> str:
         return ""
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str | None = None):
     """HBM bytes per launch of the workload's kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE runs (profiles/traffic.json), scaled by
-    the same counters on a plain copy of known size; None when absent or when
+    the same counters on a plain copy of known size; with `kernel`, that
+    kernel's own bytes (a call of several kernels); None when absent or when
     a source of the call's kernels changed after the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -108,6 +109,9 @@ def measured_traffic(workload: str):
         return None
     if any(kernel_source_sha(name) != sha for name, sha in rec["kernel_sources"].items()):
         return None
+    if kernel is not None:
+        b = rec.get("hbm_bytes_per_kernel", {}).get(kernel)
+        return int(b) if b is not None else None
     return int(rec["hbm_bytes_per_launch"])
 
 
@@ -612,7 +616,8 @@ def bench_headline(args) -> int:
         cpu = cpu_baseline(sub, x_np, weights, args.cpu_seconds)
 
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(name),
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(name, "gemm_bf16_kernel"),
                 "kernel": "gemm_bf16_kernel", "kernel_ms": round(gemm_ms, 6), "prepass_ms": round(pre_ms, 6),
                 "call_device_ms": round(dev_ms, 6),
                 "call_frac": round(sub.flops / (dev_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -821,7 +826,8 @@ def report(args, sub, per_set, n_sets, ms_per_step, kern_ms, pair_ms, x_np, weig
         unit = "TFLOP/s"
         achieved = sub.flops / launches_per_step / (kern_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "the whole call (x -> bf16 pre-pass and GEMM)"}
     roofline["traffic"] = measured_traffic(sub.name)
     roofline["kernel_ms"] = round(kern_ms, 6)
     roofline["timing"] = "HIP events on the launch stream around the timed region / launches"
