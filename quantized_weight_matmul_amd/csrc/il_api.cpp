@@ -175,7 +175,7 @@ hipError_t grow_scratch(DeviceCtx *ctx, StreamScratch *e, size_t need, bool *fal
 // its scratch from the stream's cache.
 hipError_t run_gemm(DeviceCtx *ctx, int fmt, const float *x, int t, int n_in, const il::KJob *jobs, int n_jobs,
                     hipStream_t s, bool glu, hipEvent_t after_prepass = nullptr) {
-    const size_t need = il::gemm_scratch_bytes(fmt, t, n_in, jobs, n_jobs);
+    const size_t need = il::gemm_scratch_bytes(fmt, t, n_in, jobs, n_jobs, glu);
     if (need == 0) return il::launch_gemm(fmt, x, nullptr, t, n_in, jobs, n_jobs, ctx->cu_count, s, glu);
     StreamScratch *e = nullptr;
     std::unique_lock<std::mutex> lock = stream_scratch(ctx, s, &e);
@@ -649,8 +649,8 @@ int matmul_impl(const char *who, const float *x, int64_t t, int64_t n_in, const 
             if (n > need) need = n;
         }
         if (need > il::static_scratch_bytes()) {
-            set_err("%s: t * n_in = %" PRId64 " needs %zu bytes of scratch for the bf16 copy of x; the static "
-                    "buffer holds %zu (t * n_in <= %zu)",
+            set_err("%s: t * n_in = %" PRId64 " needs %zu bytes of scratch (the bf16 copy of x, and at t <= 128 "
+                    "the K-split partial sums); the static buffer holds %zu (bf16 weights: t * n_in <= %zu)",
                     who, t * n_in, need, il::static_scratch_bytes(), il::static_scratch_bytes() / 2);
             return 0;
         }

@@ -44,6 +44,7 @@
 #include <cstring>
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 namespace il {
 namespace {
@@ -82,6 +83,14 @@ struct GemmParams {
     int small_lo;       // first big unit the small units split
     KJob job[kMaxJobs];
     int tn0[kMaxJobs + 1];  // prefix sums of unit-grid columns per job
+    // mid-size plan (Q8/Q4, 32 < t <= 128; mid_bm = 0 otherwise): units of
+    // mid_bm tokens x 128 weight rows; the big units are run whole, the
+    // n_small small ones are chunk c = u % n_chunks of unit n_big + u / n_chunks
+    int mid_bm;
+    int nk;        // K steps of BK
+    int n_chunks;  // K chunks every mid unit sums separately, in order
+    int chunk_hi[16];  // chunk c = steps [chunk_hi[c - 1], chunk_hi[c]) (chunk_hi[-1] = 0)
+    float *part;   // [unit - n_big][chunk][mid_bm * 128] chunk sums of the split units
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -222,25 +231,33 @@ __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float *__restrict_
 }
 
 // ----------------------------------------------------------- Q8 / Q4 units
-// A BM x 128 unit (BM = 256: a half, 128: a quarter) on 8 waves in a 4 x 2
-// grid of (BM / 4) x 64.  Per K step (64 = two quantisation blocks) each
-// wave's 32x32 tiles get one MFMA chain per block, started from zero, whose
-// f32 result is scaled by the block's scale of the tile's weight row (one
-// per lane: a lane holds one output column) and added to the accumulator.
+// A BM x 128 unit (BM = 256: a half; 128: a quarter, on 8 waves in a 4 x 2
+// grid of (BM / 4) x 64; 64: on a 2 x 4 grid of 32 x 32) over K steps
+// [ks_lo, ks_hi).  Per K step (64 = two quantisation blocks) each wave's
+// 32x32 tiles get one MFMA chain per block, started from zero, whose f32
+// result is scaled by the block's scale of the tile's weight row (one per
+// lane: a lane holds one output column) and added to the accumulator.
+// CHUNKED: the accumulator restarts from zero at each of the n_chunks chunk
+// boundaries of K (chunk c = steps [nk c / n_chunks, nk (c + 1) / n_chunks))
+// and the chunk sums are added, in chunk order, into the total, so that a
+// unit computed whole and one whose chunks ran in separate workgroups give
+// the same bits.  fin(acc, wm, wn, lane) takes the result.
 // GLU: B-tile rows come in groups of 32 alternating between the gate and up
 // projections (virtual row v is row (v / 64) * 32 + v % 32 of the gate if
 // (v / 32) is even, of the up projection if odd), so a wave's two 32-column
 // tiles are the gate and up sums of the same outputs.
-template <int FMT, int BM, bool GLU>
-__device__ __forceinline__ void q_unit(const GemmParams &p, uint16_t *lds, float *scl, int m0, int n0, const KJob &jb) {
-    constexpr int BN = 128, WM = 4, WN = 2;
+template <int FMT, int BM, bool GLU, bool CHUNKED, class Fin>
+__device__ __forceinline__ void q_unit(const GemmParams &p, uint16_t *lds, float *scl, int m0, int n0, const KJob &jb,
+                                       int ks_lo, int ks_hi, Fin &&fin) {
+    constexpr int BN = 128, WM = BM == 64 ? 2 : 4, WN = kWaves / WM;
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
     constexpr int kCols = GLU ? BN / 2 : BN;  // output columns of the unit
     constexpr int kChunksA = BM * BK / 8 / kThreads;  // 16-byte chunks per thread, A tile
     constexpr int TPR = kThreads / BN;                // staging threads per B row
     constexpr int EPT = BK / TPR;                     // codes of a B row per thread and step
     constexpr int kStage = (BM + BN) * BK;            // bf16 elements per LDS stage
-    static_assert(TN == 2 && EPT == 16 && kChunksA >= 1, "unit shape");
+    static_assert(TM >= 1 && TN >= 1 && EPT == 16 && kChunksA >= 1, "unit shape");
+    static_assert(!GLU || TN == 2, "GLU pairs the two 32-column tiles of a wave");
     const int n_in = p.n_in;
     const int nb = n_in / kBlock;
     const int tid = threadIdx.x;
@@ -330,11 +347,20 @@ __device__ __forceinline__ void q_unit(const GemmParams &p, uint16_t *lds, float
         }
     };
 
-    f32x16 acc[TM][TN];
+    f32x16 acc[TM][TN], tot[CHUNKED ? TM : 1][CHUNKED ? TN : 1];
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
         for (int n = 0; n < TN; ++n) acc[a][n] = (f32x16){};
+    if constexpr (CHUNKED) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int n = 0; n < TN; ++n) tot[a][n] = (f32x16){};
+    }
+    int chunk = 0;
+    const auto chunk_end = [&](int c) { return (int)((int64_t)p.nk * (c + 1) / p.n_chunks); };
+    int next_fold = CHUNKED ? chunk_end(0) : 0;
 
     // 32x32x16 fragments: lane reads row (lane & 31) of a 32-row tile, 16-byte
     // chunk 2 kk + lane / 32; every fragment row of this lane shares one
@@ -376,7 +402,7 @@ __device__ __forceinline__ void q_unit(const GemmParams &p, uint16_t *lds, float
         }
     };
 
-    const int nk = (n_in + BK - 1) / BK;
+    const int nk = ks_hi;
     uint32_t offa[kChunksA];
     int ka[kChunksA];
 #pragma unroll
@@ -402,15 +428,17 @@ __device__ __forceinline__ void q_unit(const GemmParams &p, uint16_t *lds, float
     constexpr int kBLoads = 2;
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    issue_a(0, 0);
-    fetch(0, S0{});
-    if (nk > 1) fetch(BK, S1{});
+    const int k0 = ks_lo * BK;
+    issue_a(0, k0);
+    fetch(k0, S0{});
+    if (ks_lo + 1 < nk) fetch(k0 + BK, S1{});
     store(0, S0{});
-    if (nk > 2) fetch(2 * BK, S0{});
+    if (ks_lo + 2 < nk) fetch(k0 + 2 * BK, S0{});
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's LDS writes are done
     lds_barrier();
-    // step ks computes stage ks & 1; the codes of step ks + 1 are in set (ks + 1) & 1
+    // step ks computes stage (ks - ks_lo) & 1; the codes of step ks + 1 are
+    // in set (ks + 1 - ks_lo) & 1
     auto step = [&](int ks, auto cur_c) {
         constexpr int cur = decltype(cur_c)::value;
         using Next = std::integral_constant<int, cur ^ 1>;
@@ -421,16 +449,385 @@ __device__ __forceinline__ void q_unit(const GemmParams &p, uint16_t *lds, float
             if (ks + 3 < nk) fetch((ks + 3) * BK, Next{}), fetched = true;
         }
         compute(cur);
+        if constexpr (CHUNKED) {
+            if (ks + 1 == next_fold) {  // the last step of chunk `chunk`
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+#pragma unroll
+                    for (int n = 0; n < TN; ++n) {
+                        tot[a][n] += acc[a][n];
+                        acc[a][n] = (f32x16){};
+                    }
+                ++chunk;
+                next_fold = chunk < p.n_chunks ? chunk_end(chunk) : -1;
+            }
+        }
         if (fetched) wait_vmcnt<kBLoads>(); else wait_vmcnt<0>();
         __builtin_amdgcn_s_waitcnt(0xC07F);
         lds_barrier();
     };
-    for (int ks = 0; ks < nk; ks += 2) {
+    for (int ks = ks_lo; ks < nk; ks += 2) {
         step(ks, S0{});
         if (ks + 1 < nk) step(ks + 1, S1{});
     }
-    store_tile<TM, TN, GLU>(acc, jb, p.t, m0 + wm * (BM / WM), n0 + wn * (GLU ? 32 : 64), lane);
+    if constexpr (CHUNKED) fin(tot, wm, wn, lane);
+    else fin(acc, wm, wn, lane);
 }
+
+// The same BM x 128 Q8/Q4 unit for mid-size t (BM = 64 or 128 holds every
+// token), with longer K steps and a deeper pipeline: with BM small a K step
+// of 64 has little arithmetic, and its fixed costs (the barrier, the waits,
+// all eight waves reading LDS at once) dominated.  Here a step is kMidBK =
+// 128 (four quantisation blocks; one block's codes per staging thread), every
+// thread keeps kMidDepth steps of its codes in flight in a ring of registers,
+// and x's tile is copied mid_a_stages - 1 steps ahead into a ring of LDS
+// stages; the codes of the next step are converted into one of two B
+// stages.  Every step issues the same loads (past the unit's range they read
+// nothing: out-of-range offsets), so the number of loads behind any given
+// one is fixed and one wait count serves every step.  The loop is unrolled
+// kMidDepth times so that ring indices are constants.  An LDS row holds 128
+// bf16 as 16 chunks of 16 bytes, chunk c of row r at slot c ^ (r & 15).
+// f(integral_constant<int, J>) for J = 0 .. N - 1 in order, while it returns true.
+template <class F, int... J>
+__device__ __forceinline__ void unrolled_while(F &&f, std::integer_sequence<int, J...>) {
+    (void)(f(std::integral_constant<int, J>{}) && ...);
+}
+
+constexpr int kMidBK = 128;   // K per step of a mid unit
+constexpr int kMidDepth = 4;  // steps of codes in flight per thread
+template <int BM>
+constexpr int mid_a_stages() { return BM == 64 ? 4 : 2; }  // LDS stages of x's tile
+template <int BM>
+constexpr int mid_lds_elems() {  // bf16 elements: A ring, two B stages, then the scales
+    return mid_a_stages<BM>() * BM * kMidBK + 2 * 128 * kMidBK + 2 * 128 * 4 * 2;
+}
+
+template <int FMT, int BM, bool GLU, bool CHUNKED, class Fin>
+__device__ __forceinline__ void q_mid_unit(const GemmParams &p, uint16_t *lds, int m0, int n0, const KJob &jb,
+                                           int ks_lo, int ks_hi, Fin &&fin) {
+    constexpr int BN = 128, BKM = kMidBK, WM = BM == 64 ? 2 : 4, WN = kWaves / WM;
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+    constexpr int kCols = GLU ? BN / 2 : BN;
+    constexpr int kRowChunks = BKM / 8;                           // 16-byte chunks per LDS row
+    constexpr int kChunksA = BM * kRowChunks / kThreads;          // A copies per thread and step
+    constexpr int TPR = kThreads / BN, EPT = BKM / TPR;           // staging threads per B row, codes each
+    constexpr int kF = FMT == FMT_Q8 ? 3 : 2;                     // loads per fetch
+    constexpr int D = kMidDepth, NA = mid_a_stages<BM>();
+    static_assert(TM >= 1 && TN >= 1 && EPT == kBlock && kChunksA >= 1 && kRowChunks == 16, "unit shape");
+    static_assert(!GLU || TN == 2, "GLU pairs the two 32-column tiles of a wave");
+    static_assert(D % NA == 0 && D % 2 == 0, "ring sizes divide the unroll");
+    uint16_t *const Aring = lds;
+    uint16_t *const Bst = lds + NA * BM * BKM;
+    float *const scl = reinterpret_cast<float *>(Bst + 2 * BN * BKM);  // [stage][B row][block of the step]
+    const int n_in = p.n_in;
+    const int nb = n_in / kBlock;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+
+    const int a_rows = min(BM, p.t - m0);
+    const int b_rows = min(kCols, jb.n_out - n0);
+    const uint32_t row2 = (uint32_t)n_in * 2u;
+    const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.xb + (int64_t)m0 * n_in, (uint32_t)a_rows * row2);
+    // the codes, and the scales from the tiled plane (rows padded to 16 and
+    // blocks to 4 with zero scales), so that a block past the end of K, or a
+    // row past the job's last, is multiplied by 0; rows past the padding lie
+    // outside the descriptors and read 0
+    const int nb4 = (nb + 3) / 4;
+    constexpr uint32_t kSclBytes = FMT == FMT_Q8 ? 4u : 2u;
+    auto b_rsrc = [&](const KJob &k, __amdgpu_buffer_rsrc_t &c, __amdgpu_buffer_rsrc_t &sc) {
+        if constexpr (FMT == FMT_Q8)
+            c = make_rsrc(static_cast<const int8_t *>(k.codes) + (int64_t)n0 * n_in, (uint32_t)b_rows * (uint32_t)n_in);
+        else
+            c = make_rsrc(static_cast<const uint8_t *>(k.codes) + (n0 >> 4) * q4_plane_bytes(16, nb),
+                          (uint32_t)q4_plane_bytes(b_rows, nb));
+        sc = make_rsrc(static_cast<const uint8_t *>(k.scales_t) + (int64_t)(n0 >> 4) * nb4 * 64 * kSclBytes,
+                       (uint32_t)tiled_scale_count(b_rows, nb) * kSclBytes);
+    };
+    __amdgpu_buffer_rsrc_t brs, bss, brs2, bss2;
+    b_rsrc(jb, brs, bss);
+    if constexpr (GLU) b_rsrc(p.job[1], brs2, bss2);
+    else brs2 = brs, bss2 = bss;
+
+    // staging of the codes: TPR threads per B row, each one quantisation
+    // block (block qh of the step) of row qr
+    const int qr = tid / TPR, qh = tid % TPR;
+    const int qkey = qr & 15;
+    const bool up = GLU && ((qr >> 5) & 1);
+    const int wr = GLU ? (qr >> 6) * 32 + (qr & 31) : qr;
+    const __amdgpu_buffer_rsrc_t crs = up ? brs2 : brs, srs = up ? bss2 : bss;
+    uint4 cq[D][FMT == FMT_Q8 ? 2 : 1];
+    uint32_t cs[D];
+    // this thread's block of step ks is block 4 ks + qh of row wr: its codes
+    // at c_base + ks * c_step, its scale at s_base + ks * s_step.  Past the
+    // end of K (the fetches that run ahead of the last steps) these read
+    // padding, the next tile's codes or nothing; the results are never used.
+    const uint32_t c_base = FMT == FMT_Q8 ? (uint32_t)wr * (uint32_t)n_in + (uint32_t)qh * kBlock
+                                          : (uint32_t)q4_block_offset(wr, qh, nb);
+    constexpr uint32_t c_step = FMT == FMT_Q8 ? BKM : 1024u;  // Q4: one 64-byte segment per row and step
+    const uint32_t s_base = (uint32_t)tiled_scale_index(wr, qh, nb4) * kSclBytes;
+    constexpr uint32_t s_step = 64u * kSclBytes;
+    auto fetch = [&](int ks, auto slot_c) {
+        constexpr int S = decltype(slot_c)::value;
+        const uint32_t co = c_base + (uint32_t)ks * c_step, so = s_base + (uint32_t)ks * s_step;
+        if constexpr (FMT == FMT_Q8) {
+            cq[S][0] = bload16(crs, co);
+            cq[S][1] = bload16(crs, co + 16u);
+            cs[S] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, 0, 0);
+        } else {
+            cq[S][0] = bload16(crs, co);
+            cs[S] = __builtin_amdgcn_raw_buffer_load_b16(srs, so, 0, 0);
+        }
+    };
+    // ring slot S as exact bf16 codes into B stage st, with the block's scale
+    auto store = [&](int st, auto slot_c) {
+        constexpr int S = decltype(slot_c)::value;
+        uint16_t *Bs = Bst + st * BN * BKM;
+        uint32_t o[16];
+        if constexpr (FMT == FMT_Q8) {
+            const uint32_t w[8] = {cq[S][0].x, cq[S][0].y, cq[S][0].z, cq[S][0].w,
+                                   cq[S][1].x, cq[S][1].y, cq[S][1].z, cq[S][1].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                o[2 * i] = pack_bf16((float)(int8_t)(w[i]), (float)(int8_t)(w[i] >> 8));
+                o[2 * i + 1] = pack_bf16((float)(int8_t)(w[i] >> 16), (float)(int8_t)(w[i] >> 24));
+            }
+        } else {
+            const uint32_t w[4] = {cq[S][0].x, cq[S][0].y, cq[S][0].z, cq[S][0].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t lo = (w[i] << 4) & 0xF0F0F0F0u;  // elements 0, 2, 4, 6: 16 (code - 8)
+                const uint32_t hi = w[i] & 0xF0F0F0F0u;         // elements 1, 3, 5, 7
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[4 * i + e] = pack_bf16((float)(int8_t)(lo >> (8 * e)), (float)(int8_t)(hi >> (8 * e)));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4 *>(Bs + qr * BKM + ((4 * qh + i) ^ qkey) * 8) =
+                make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+        scl[(st * BN + qr) * 4 + qh] = FMT == FMT_Q8 ? __builtin_bit_cast(float, cs[S])
+                                                     : (float)__builtin_bit_cast(_Float16, (uint16_t)cs[S]) * 0.0625f;  // Q4 codes carry * 16; exact
+    };
+    uint32_t offa[kChunksA];
+    int ka[kChunksA];
+#pragma unroll
+    for (int i = 0; i < kChunksA; ++i) {
+        const int u = (wave * kChunksA + i) * 64 + lane, r = u / kRowChunks;
+        ka[i] = ((u % kRowChunks) ^ (r & 15)) * 8;
+        offa[i] = (uint32_t)r * row2 + (uint32_t)ka[i] * 2u;
+    }
+    // x's tile of step ks into A stage st; a step that ends past n_in reads
+    // zeros there (not the next row of x).  The copies that run ahead of the
+    // last steps land in stages that are never read.
+    auto issue_a = [&](int st, int ks) {
+        uint16_t *As = Aring + st * BM * BKM;
+        const int k0 = ks * BKM;
+        if (k0 + BKM <= n_in) {
+#pragma unroll
+            for (int i = 0; i < kChunksA; ++i)
+                lds_load16(ars, As + (wave * kChunksA + i) * 64 * 8, offa[i] + (uint32_t)k0 * 2u);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kChunksA; ++i)
+                lds_load16(ars, As + (wave * kChunksA + i) * 64 * 8, k0 + ka[i] < n_in ? offa[i] + (uint32_t)k0 * 2u : kOut);
+        }
+    };
+
+    f32x16 acc[TM][TN], tot[CHUNKED ? TM : 1][CHUNKED ? TN : 1];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) acc[a][n] = (f32x16){};
+    if constexpr (CHUNKED) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int n = 0; n < TN; ++n) tot[a][n] = (f32x16){};
+    }
+    int chunk = 0;
+    int next_fold = CHUNKED ? p.chunk_hi[0] : 0;
+
+    const int frow = lane & 31;
+    const int fkey = frow & 15;
+    const int a_base = (wm * (BM / WM) + frow) * BKM;
+    const int b_base = (wn * (BN / WN) + frow) * BKM;
+    // With one 32x32 tile per wave (BM = 64), a block's scaled sum is added
+    // to the accumulator only after the next block's MFMAs are issued, so
+    // that the FMAs do not wait for the MFMA results they consume: block b's
+    // MFMA results go to buffer b & 1 (four blocks per step, so the last
+    // block of a step is always in buffer 1) and are added while block b + 1
+    // computes into the other.  (Before the first block, buffer 1 holds a
+    // zero product.)  With two tiles per wave (BM = 128) the second buffer
+    // does not fit in registers: each block's sum is added right after its
+    // MFMAs, and the other wave on the SIMD covers the wait.  Either way the
+    // additions into acc come block by block, in order.
+    static_assert((BKM / kBlock) % 2 == 0, "blocks alternate between the two buffers");
+    constexpr bool kDefer = TM * TN == 1;
+    f32x16 part[kDefer ? 2 : 1][TM][TN];
+    float part_s[2][TN];
+    auto clear1 = [&]() {
+        if constexpr (kDefer) {
+#pragma unroll
+            for (int n = 0; n < TN; ++n) {
+                part_s[1][n] = 0.f;
+#pragma unroll
+                for (int a = 0; a < TM; ++a) part[1][a][n] = (f32x16){};
+            }
+        }
+    };
+    clear1();
+    auto flush = [&](auto buf_c) {
+        if constexpr (!kDefer) return;
+        constexpr int B = kDefer ? decltype(buf_c)::value : 0;
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int n = 0; n < TN; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[a][n][i] = fmaf(part_s[B][n], part[B][a][n][i], acc[a][n][i]);
+    };
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    auto compute = [&](int sa, int sb) {
+        const uint16_t *As = Aring + sa * BM * BKM, *Bs = Bst + sb * BN * BKM;
+        f32x4 s[TN];
+#pragma unroll
+        for (int n = 0; n < TN; ++n) s[n] = *reinterpret_cast<const f32x4 *>(scl + (sb * BN + wn * (BN / WN) + n * 32 + frow) * 4);
+        auto block = [&](int blk, auto buf_c) {
+            constexpr int B = kDefer ? decltype(buf_c)::value : 0;
+#pragma unroll
+            for (int kk2 = 0; kk2 < 2; ++kk2) {
+                const int slot = ((2 * blk + kk2) * 2 + (lane >> 5)) ^ fkey;
+                bf16x8 fa[TM], fb[TN];
+#pragma unroll
+                for (int a = 0; a < TM; ++a) fa[a] = *reinterpret_cast<const bf16x8 *>(As + a_base + a * 32 * BKM + slot * 8);
+#pragma unroll
+                for (int n = 0; n < TN; ++n) fb[n] = *reinterpret_cast<const bf16x8 *>(Bs + b_base + n * 32 * BKM + slot * 8);
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+#pragma unroll
+                    for (int n = 0; n < TN; ++n)
+                        part[B][a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[n],
+                                                                                 kk2 ? part[B][a][n] : (f32x16){}, 0, 0, 0);
+            }
+            if constexpr (kDefer) {
+                flush(std::integral_constant<int, B ^ 1>{});  // the previous block
+#pragma unroll
+                for (int n = 0; n < TN; ++n) part_s[B][n] = s[n][blk];
+            } else {
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+#pragma unroll
+                    for (int n = 0; n < TN; ++n)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[a][n][i] = fmaf(s[n][blk], part[0][a][n][i], acc[a][n][i]);
+            }
+        };
+#pragma unroll
+        for (int blk = 0; blk < BKM / kBlock; blk += 2) {
+            block(blk, B0{});
+            block(blk + 1, B1{});
+        }
+    };
+
+    // Loads issued per step: kChunksA copies, then a fetch of kF loads.
+    // Before step ks + 1 the copy of its x tile (issued at step ks + 2 - NA)
+    // and the codes of step ks + 2 (fetched at step ks + 1 - D, stored at step
+    // ks + 1) must have landed: the wait allows what was issued after the
+    // later of them.
+    // (In the first step fewer loads follow the codes of step ks_lo + 2,
+    // fetched in the prologue after the tiles: (D - 2) fetches and one step.)
+    constexpr int kPer = kChunksA + kF;
+    constexpr int kAfterA = kF + (NA - 2) * kPer, kAfterF = (D - 1) * kPer, kFirst = (D - 2) * kF + kPer;
+    constexpr int kWait0 = kAfterA < kAfterF ? kAfterA : kAfterF;
+    constexpr int kWait = kWait0 < kFirst ? kWait0 : kFirst;
+    static_assert(kWait >= 0 && kWait < 64, "vmcnt range");
+    using Z = std::integral_constant<int, 0>;
+    // prologue: the codes of step ks_lo first (they are converted before the
+    // loop), then x's tiles of steps ks_lo .. ks_lo + NA - 2, then the codes
+    // of steps ks_lo + 1 .. ks_lo + D - 1, and once slot 0 is converted, the
+    // codes of step ks_lo + D into it (step j refills the slot it converts,
+    // that of step j + 1, with the codes of step j + 1 + D)
+    fetch(ks_lo, Z{});
+#pragma unroll
+    for (int j = 0; j < NA - 1; ++j) issue_a(j, ks_lo + j);
+    unrolled_while(
+        [&](auto j_c) {
+            constexpr int J = decltype(j_c)::value;
+            fetch(ks_lo + 1 + J, std::integral_constant<int, 1 + J>{});
+            return true;
+        },
+        std::make_integer_sequence<int, D - 1>{});
+    wait_vmcnt<(NA - 1) * kChunksA + (D - 1) * kF>();
+    store(0, Z{});
+    fetch(ks_lo + D, Z{});
+    // x's tile of step ks_lo and the codes of step ks_lo + 1 (converted by
+    // the first step), the later of which was followed by D - 1 fetches
+    wait_vmcnt<(D - 1) * kF>();
+    static_assert((D - 1) * kF <= (NA - 2) * kChunksA + D * kF, "the codes come after the tile");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    lds_barrier();
+    // step ks = ks_lo + i: A stage i % NA, B stage i % 2, its codes were in
+    // ring slot i % D
+    auto step = [&](int ks, auto i_c) {
+        constexpr int I = decltype(i_c)::value;
+        store((I + 1) & 1, std::integral_constant<int, (I + 1) % D>{});  // step ks + 1
+        issue_a((I + NA - 1) % NA, ks + NA - 1);
+        fetch(ks + 1 + D, std::integral_constant<int, (I + 1) % D>{});
+        compute(I % NA, I & 1);
+        if constexpr (CHUNKED) {
+            if (ks + 1 == next_fold) {  // the last step of chunk `chunk`
+                flush(B1{});
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+#pragma unroll
+                    for (int n = 0; n < TN; ++n) {
+                        tot[a][n] += acc[a][n];
+                        acc[a][n] = (f32x16){};
+                    }
+                clear1();
+                ++chunk;
+                next_fold = chunk < p.n_chunks ? p.chunk_hi[chunk] : -1;
+            }
+        }
+        wait_vmcnt<kWait>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        lds_barrier();
+    };
+    for (int ks = ks_lo; ks < ks_hi; ks += D) {
+        unrolled_while(
+            [&](auto i_c) {
+                if (ks + decltype(i_c)::value >= ks_hi) return false;
+                step(ks + decltype(i_c)::value, i_c);
+                return true;
+            },
+            std::make_integer_sequence<int, D>{});
+    }
+    wait_vmcnt<0>();  // the copies past the range write LDS; nothing may be in flight at the end
+    if constexpr (CHUNKED) {
+        fin(tot, wm, wn, lane);  // the last chunk's end flushed the pending block
+    } else {
+        flush(B1{});
+        fin(acc, wm, wn, lane);
+    }
+}
+
+// The finisher that writes a unit's result to y: wave (wm, wn) holds rows
+// m0 + wm * BM / WM and columns n0 + wn * (BN / WN) (GLU: half as many).
+template <int BM, bool GLU>
+struct StoreY {
+    const GemmParams &p;
+    const KJob &jb;
+    int m0, n0;
+    template <int TM, int TN>
+    __device__ __forceinline__ void operator()(const f32x16 (&acc)[TM][TN], int wm, int wn, int lane) const {
+        constexpr int WM = BM == 64 ? 2 : 4, WN = kWaves / WM;
+        store_tile<TM, TN, GLU>(acc, jb, p.t, m0 + wm * (BM / WM), n0 + wn * (128 / WN) / (GLU ? 2 : 1), lane);
+    }
+};
 
 template <int FMT, bool GLU>
 __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(GemmParams p) {
@@ -448,10 +845,122 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_kernel(GemmParams p) {
     Place pl;
     if (kind == 0) {
         if (!place<GLU>(p, u, cols, 0, 0, cols, pl)) return;
-        q_unit<FMT, 256, GLU>(p, lds, scl, pl.m0, pl.n0, p.job[pl.j]);
+        q_unit<FMT, 256, GLU, false>(p, lds, scl, pl.m0, pl.n0, p.job[pl.j], 0, p.nk,
+                                     StoreY<256, GLU>{p, p.job[pl.j], pl.m0, pl.n0});
     } else {
         if (!place<GLU>(p, p.small_lo + (u >> 1), cols, (u & 1) * 128, 0, cols, pl)) return;
-        q_unit<FMT, 128, GLU>(p, lds, scl, pl.m0, pl.n0, p.job[pl.j]);
+        q_unit<FMT, 128, GLU, false>(p, lds, scl, pl.m0, pl.n0, p.job[pl.j], 0, p.nk,
+                                     StoreY<128, GLU>{p, p.job[pl.j], pl.m0, pl.n0});
+    }
+}
+
+// Mid-size t (32 < t <= 128): every unit is BM (64 or 128) tokens -- all of
+// them -- by 128 weight rows, summed over K in p.n_chunks chunks (q_mid_unit,
+// CHUNKED).  The big units run whole, one workgroup each.  When the units
+// are one whole round of the compute units plus a few (272 units of the Q4
+// verify shape on 256 CUs), those few are split: one workgroup per chunk,
+// each writing its chunk sum to p.part in its registers' order; a second,
+// small launch (mid_fixup_kernel) adds each split unit's chunk sums in chunk
+// order and writes y.  The last round is then 1/n_chunks of a unit long
+// instead of a whole unit.  (Completing the units inside the GEMM launch,
+// by whichever workgroup finishes a unit's last chunk, needs a device-wide
+// release and acquire per workgroup, which write back and invalidate the
+// L2: that measured ~50 us per call on the Q4 verify shape.)
+// Layout of a chunk sum: float4 ((wave * kQ + (a * TN + n) * 4 + q) * 64 + lane)
+// holds acc[a][n][4 q .. 4 q + 3] of that wave and lane, kQ = TM * TN * 4.
+template <int BM>
+struct PartFin {
+    const GemmParams &p;
+    int su, chunk;
+    template <int TM, int TN>
+    __device__ __forceinline__ void operator()(const f32x16 (&acc)[TM][TN], int, int, int lane) const {
+        constexpr int kQ = TM * TN * 4;
+        const int wave = threadIdx.x >> 6;
+        float4 *mine = reinterpret_cast<float4 *>(p.part) + ((int64_t)su * p.n_chunks + chunk) * (BM * 128 / 4) +
+                       (wave * kQ) * 64 + lane;
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int n = 0; n < TN; ++n)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    mine[((a * TN + n) * 4 + q) * 64] =
+                        make_float4(acc[a][n][4 * q], acc[a][n][4 * q + 1], acc[a][n][4 * q + 2], acc[a][n][4 * q + 3]);
+    }
+};
+
+// The split units' chunk sums added in chunk order, starting from zero as
+// the whole units' totals do, and stored as the GEMM's wave would have
+// stored them.  One thread per float4 of a chunk sum (GLU: the gate's and
+// the up projection's float4 of the same outputs), its n_chunks loads issued
+// before the additions; 64-thread workgroups, one per (split unit, wave, a,
+// n, q) of the chunk-sum layout.
+template <int BM, bool GLU>
+__global__ __launch_bounds__(64) void mid_fixup_kernel(GemmParams p) {
+    constexpr int WM = BM == 64 ? 2 : 4, WN = kWaves / WM;
+    constexpr int TM = BM / WM / 32, TN = 128 / WN / 32, kQ = TM * TN * 4;
+    constexpr int kGroups = GLU ? kQ / 2 : kQ;  // GLU: n = 0 and n = 1 in one thread
+    constexpr int kMaxChunks = 16;
+    static_assert(!GLU || TN == 2, "GLU pairs the two 32-column tiles of a wave");
+    const int lane = threadIdx.x;
+    int g = blockIdx.x;
+    const int grp = g % kGroups;
+    g /= kGroups;
+    const int wave = g % kWaves, su = g / kWaves;
+    // grp -> (a, n, q) of the layout (GLU: n = 0 here, n = 1 its partner)
+    const int q = grp & 3, an = grp >> 2;
+    const int a = GLU ? an : an / TN, n = GLU ? 0 : an % TN;
+    Place pl;
+    if (!place<GLU>(p, p.n_big + su, big_cols(FMT_Q4, GLU), 0, 0, big_cols(FMT_Q4, GLU), pl)) return;
+    const float4 *src = reinterpret_cast<const float4 *>(p.part) + (int64_t)su * p.n_chunks * (BM * 128 / 4) +
+                        (wave * kQ) * 64 + lane;
+    const int off0 = ((a * TN + n) * 4 + q) * 64, off1 = ((a * TN + 1) * 4 + q) * 64;
+    float4 v0[kMaxChunks], v1[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+        if (c < p.n_chunks) {
+            v0[c] = src[(int64_t)c * (BM * 128 / 4) + off0];
+            if constexpr (GLU) v1[c] = src[(int64_t)c * (BM * 128 / 4) + off1];
+        }
+    float s0[4] = {0.f, 0.f, 0.f, 0.f}, s1[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+        if (c < p.n_chunks) {
+            s0[0] += v0[c].x, s0[1] += v0[c].y, s0[2] += v0[c].z, s0[3] += v0[c].w;
+            if constexpr (GLU) s1[0] += v1[c].x, s1[1] += v1[c].y, s1[2] += v1[c].z, s1[3] += v1[c].w;
+        }
+    // rows and column of accumulator elements 4 q .. 4 q + 3 (see store_tile)
+    const int wm = wave / WN, wn = wave % WN;
+    const KJob &jb = p.job[pl.j];
+    const int row0 = pl.m0 + wm * (BM / WM) + a * 32 + q * 8 + (lane >> 5) * 4;
+    const int col = pl.n0 + wn * (128 / WN) / (GLU ? 2 : 1) + (GLU ? 0 : n * 32) + (lane & 31);
+    if (col >= jb.n_out) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int row = row0 + e;
+        if (row < p.t) jb.y[(int64_t)row * jb.n_out + col] = GLU ? gelu(s0[e]) * s1[e] : s0[e];
+    }
+}
+
+template <int FMT, int BM, bool GLU>
+__global__ __launch_bounds__(kThreads, 1) void gemm_q_mid_kernel(GemmParams p) {
+    static_assert(FMT == FMT_Q8 || FMT == FMT_Q4, "bf16 weights use gemm_bf16_kernel");
+    // one LDS object, as in gemm_q_kernel
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[mid_lds_elems<BM>()];
+    int u;
+    const int kind = unit_of(p, &u);
+    if (kind < 0) return;
+    constexpr int cols = big_cols(FMT, GLU);
+    Place pl;
+    if (kind == 0) {
+        if (!place<GLU>(p, u, cols, 0, 0, cols, pl)) return;
+        q_mid_unit<FMT, BM, GLU, true>(p, lds, pl.m0, pl.n0, p.job[pl.j], 0, p.nk,
+                                       StoreY<BM, GLU>{p, p.job[pl.j], pl.m0, pl.n0});
+    } else {
+        const int su = u / p.n_chunks, c = u - su * p.n_chunks;
+        if (!place<GLU>(p, p.n_big + su, cols, 0, 0, cols, pl)) return;
+        const int lo = c ? p.chunk_hi[c - 1] : 0, hi = p.chunk_hi[c];
+        q_mid_unit<FMT, BM, GLU, false>(p, lds, pl.m0, pl.n0, p.job[pl.j], lo, hi, PartFin<BM>{p, su, c});
     }
 }
 
@@ -623,26 +1132,72 @@ hipError_t launch_plan(GemmParams p, int cu_count, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Mid-size t runs the matrix-core decode kernel's wide mode, which rounds x
-// itself up to kWideF32MaxT tokens and reads the bf16 copy of x beyond.  Q4
-// weights take it up to kVerifySliceMaxT tokens, as even slices of at most
-// kVerifyMaxT (the Q4 GEMM units convert few codes per flop and measured
-// ~220 us per call on 2 x [17408, 5120] from t = 33 to 128).
-// IL_PREFILL=gemm|verify pins the kernel.
+// t <= kVerifyMaxT runs the matrix-core decode kernel's wide mode, which
+// rounds x itself up to kWideF32MaxT tokens and reads the bf16 copy of x
+// beyond.  Q8/Q4 at kVerifyMaxT < t <= kMidMaxT run the mid plan (units that
+// hold every token); larger t and bf16 weights the big/small tile plan.
+// IL_PREFILL pins the kernel: gemm (the GEMM the shape would take: mid plan
+// or tiles), tiles (the big/small tile plan even where the mid plan would
+// run), verify (wide mode; up to kVerifySliceMaxT tokens as even slices of at
+// most kVerifyMaxT).
 struct Route {
     bool verify;
-    int slice;  // tokens per wide-mode launch
+    int slice;   // tokens per wide-mode launch
+    int mid_bm;  // GEMM of mid-size t: tokens per unit (64 or 128), else 0
 };
-Route route(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
-    bool verify = t <= kVerifyMaxT || (fmt == FMT_Q4 && t <= kVerifySliceMaxT);
+Route route(int fmt, int t, int n_in, const KJob *jobs, int n_jobs, bool glu) {
+    bool verify = t <= kVerifyMaxT, tiles = false;
     if (const char *force = getenv("IL_PREFILL")) {
         if (!strcmp(force, "gemm")) verify = false;
+        if (!strcmp(force, "tiles")) verify = false, tiles = true;
         if (!strcmp(force, "verify")) verify = t <= kVerifySliceMaxT;
     }
     const int n_slices = (t + kVerifyMaxT - 1) / kVerifyMaxT;
     const int slice = (t + n_slices - 1) / n_slices;  // > kWideF32MaxT when t > kVerifyMaxT
     verify = verify && verify_mfma_fits(fmt, slice, n_in, jobs, n_jobs);
-    return {verify, slice};
+    int mid_bm = 0;
+    if (!verify && !tiles && fmt != FMT_BF16 && t <= kMidMaxT) mid_bm = t <= 64 && !glu ? 64 : 128;
+    return {verify, slice, mid_bm};
+}
+
+// The mid plan's scratch after the bf16 copy of x: the split units' chunk
+// sums (after 256 bytes kept free).
+constexpr int kMidChunks = 16;   // K chunks of a mid unit (fewer when K has fewer steps)
+constexpr int kMidMaxSplit = 16;  // units split per launch, at most
+size_t mid_extra_bytes(int mid_bm) { return 256 + (size_t)kMidMaxSplit * kMidChunks * mid_bm * 128 * 4; }
+size_t xb_bytes(int t, int n_in) { return ((size_t)t * (size_t)n_in * 2 + 255) / 256 * 256; }
+
+template <int FMT, bool GLU>
+hipError_t launch_mid(GemmParams p, int mid_bm, int cu_count, hipStream_t s) {
+    // units: one 128-row column of a job each (tiles_m == 1); whole rounds of
+    // units run whole, and a last partial round of at most cu_count /
+    // n_chunks units is split into chunks
+    const int units = p.tn0[kMaxJobs];
+    const int left = units % cu_count;
+    const int n_split = left > 0 && left * p.n_chunks <= cu_count && left <= kMidMaxSplit && units >= cu_count ? left : 0;
+    p.mid_bm = mid_bm;
+    p.n_big = units - n_split;
+    p.small_lo = p.n_big;
+    p.n_small = n_split * p.n_chunks;
+    p.big_per_xcd = (p.n_big + kXcds - 1) / kXcds;
+    p.small_per_xcd = (p.n_small + kXcds - 1) / kXcds;
+    const dim3 grid(kXcds * (p.big_per_xcd + p.small_per_xcd));
+    if (grid.x == 0) return hipSuccess;
+    // the fixup's workgroups: (split unit, wave, float4 group of the chunk-sum layout)
+    const int groups = mid_bm == 64 ? 4 : (GLU ? 4 : 8);
+    const dim3 fix((unsigned)(n_split * kWaves * groups));
+    if (mid_bm == 64) {
+        if constexpr (!GLU) {
+            hipLaunchKernelGGL((gemm_q_mid_kernel<FMT, 64, false>), grid, dim3(kThreads), 0, s, p);
+            if (n_split) hipLaunchKernelGGL((mid_fixup_kernel<64, false>), fix, dim3(64), 0, s, p);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else {
+        hipLaunchKernelGGL((gemm_q_mid_kernel<FMT, 128, GLU>), grid, dim3(kThreads), 0, s, p);
+        if (n_split) hipLaunchKernelGGL((mid_fixup_kernel<128, GLU>), fix, dim3(64), 0, s, p);
+    }
+    return hipGetLastError();
 }
 
 // The buffer of il_matmul_noalloc's prefill path: one per device, for
@@ -672,11 +1227,11 @@ hipError_t static_scratch(int device, void **ptr) {
     return st.err;
 }
 
-size_t gemm_scratch_bytes(int fmt, int t, int n_in, const KJob *jobs, int n_jobs) {
+size_t gemm_scratch_bytes(int fmt, int t, int n_in, const KJob *jobs, int n_jobs, bool glu) {
     if (t <= kGemvMaxT || n_jobs < 1) return 0;
-    const Route r = route(fmt, t, n_in, jobs, n_jobs);
+    const Route r = route(fmt, t, n_in, jobs, n_jobs, glu);
     if (r.verify && t <= kWideF32MaxT) return 0;
-    return ((size_t)t * (size_t)n_in * 2 + 255) / 256 * 256;
+    return xb_bytes(t, n_in) + (r.mid_bm ? mid_extra_bytes(r.mid_bm) : 0);
 }
 
 hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_in, const KJob *jobs, int n_jobs,
@@ -685,7 +1240,7 @@ hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_i
     if (glu && (n_jobs != 2 || jobs[0].n_out != jobs[1].n_out)) return hipErrorInvalidValue;
     // every buffer descriptor (256 rows of x or of a weight) must stay below 2^31 bytes
     if ((int64_t)kBigM * n_in * 2 >= (1ll << 31)) return hipErrorInvalidValue;
-    const Route r = route(fmt, t, n_in, jobs, n_jobs);
+    const Route r = route(fmt, t, n_in, jobs, n_jobs, glu);
     if (r.verify && t <= kWideF32MaxT) return launch_verify_mfma(fmt, x, nullptr, t, n_in, jobs, n_jobs, cu_count, s, glu);
     if (!xb_scratch) return hipErrorInvalidValue;
 
@@ -718,6 +1273,10 @@ hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_i
     p.n_in = n_in;
     p.n_jobs = n_jobs;
     p.tiles_m = (t + kBigM - 1) / kBigM;
+    p.nk = r.mid_bm ? (n_in + kMidBK - 1) / kMidBK : (n_in + BK - 1) / BK;
+    p.n_chunks = p.nk < kMidChunks ? p.nk : kMidChunks;
+    for (int c = 0; c < p.n_chunks; ++c) p.chunk_hi[c] = (int)((int64_t)p.nk * (c + 1) / p.n_chunks);
+    if (r.mid_bm) p.part = reinterpret_cast<float *>(static_cast<uint8_t *>(xb_scratch) + xb_bytes(t, n_in) + 256);
     const int cols = big_cols(fmt, glu);
     int tn = 0;
     for (int j = 0; j < n_jobs; ++j) {
@@ -727,6 +1286,13 @@ hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_i
         if (!glu || j == 0) tn += (jobs[j].n_out + cols - 1) / cols;
     }
     for (int j = glu ? 1 : n_jobs; j <= kMaxJobs; ++j) p.tn0[j] = tn;
+    if (r.mid_bm) {
+        switch (fmt) {
+            case FMT_Q8: return glu ? launch_mid<FMT_Q8, true>(p, r.mid_bm, cu_count, s) : launch_mid<FMT_Q8, false>(p, r.mid_bm, cu_count, s);
+            case FMT_Q4: return glu ? launch_mid<FMT_Q4, true>(p, r.mid_bm, cu_count, s) : launch_mid<FMT_Q4, false>(p, r.mid_bm, cu_count, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (fmt) {
         case FMT_BF16: return glu ? launch_plan<FMT_BF16, true>(p, cu_count, s) : launch_plan<FMT_BF16, false>(p, cu_count, s);
         case FMT_Q8: return glu ? launch_plan<FMT_Q8, true>(p, cu_count, s) : launch_plan<FMT_Q8, false>(p, cu_count, s);

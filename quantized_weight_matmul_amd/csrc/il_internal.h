@@ -34,7 +34,8 @@ constexpr int kBlock = 32;     // quantisation block (elements)
 constexpr int kMaxJobs = 8;    // jobs per kernel launch (kernarg table)
 constexpr int kGemvMaxT = 8;   // t <= kGemvMaxT runs the decode kernels
 constexpr int kVerifyMaxT = 32;  // largest t the matrix-core decode kernel takes in wide mode
-constexpr int kVerifySliceMaxT = 128;  // Q4: wide mode in slices of <= kVerifyMaxT tokens up to here
+constexpr int kVerifySliceMaxT = 128;  // Q4 under IL_PREFILL=verify: wide mode in slices of <= kVerifyMaxT tokens up to here
+constexpr int kMidMaxT = 128;  // Q8/Q4 GEMM with all tokens in one unit (the mid-size plan) up to here
 
 struct Weight {
     int fmt;
@@ -120,8 +121,10 @@ hipError_t launch_verify_mfma(int fmt, const float *x, const uint16_t *xb, int t
 
 // ---- prefill GEMM, t > kGemvMaxT (il_gemm.hip) ----
 // Bytes of device scratch launch_gemm needs for this call (the bf16 copy of
-// x its units read), 0 when the call takes a path that rounds x itself.
-size_t gemm_scratch_bytes(int fmt, int t, int n_in, const KJob *jobs, int n_jobs);
+// x its units read; for Q8/Q4 at kVerifyMaxT < t <= kMidMaxT also the
+// counters and chunk sums of the units it splits over K), 0 when the call
+// takes a path that rounds x itself.
+size_t gemm_scratch_bytes(int fmt, int t, int n_in, const KJob *jobs, int n_jobs, bool glu = false);
 // xb_scratch: gemm_scratch_bytes(...) bytes of device memory, 256-byte
 // aligned, that nothing else uses until the stream has passed this call (may
 // be null when that size is 0).  Enqueues the x -> bf16 pre-pass and one GEMM
