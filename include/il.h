@@ -80,7 +80,7 @@ typedef struct {
  * return.  Returns NULL on failure ("declined", the page's `None`): bad
  * fmt or shape, null pointer, no HIP device, out of device memory; the
  * reason is in il_last_error(). */
-IL_API il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in);
+IL_API il_weight *il_upload(const void *weight, il_fmt fmt, int64_t n_out, int64_t n_in);
 
 /* Element type of the full-precision weights given to il_upload_quantize. */
 typedef enum {
@@ -113,7 +113,7 @@ typedef enum {
  * the host-format blocks of the rule above, and il_matmul uses it like any
  * other.  Synchronous.  Returns NULL on failure (bad arguments, no device,
  * out of memory); the reason is in il_last_error(). */
-IL_API il_weight *il_upload_quantize(const void *weight, int src, int fmt, int64_t n_out, int64_t n_in);
+IL_API il_weight *il_upload_quantize(const void *weight, il_src src, il_fmt fmt, int64_t n_out, int64_t n_in);
 
 /* Export -- writes the weight of a handle back in its host format (see
  * il_fmt: bf16 words, or the Q8 / Q4 blocks), bit for bit what il_upload

@@ -340,7 +340,7 @@ auto on_device(int device, F f) {
 // ===================================================================== ABI
 extern "C" {
 
-il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in) {
+il_weight *il_upload(const void *weight, il_fmt fmt, int64_t n_out, int64_t n_in) {
     g_err.clear();
     if (!weight) {
         set_err("il_upload: weight is NULL");
@@ -396,7 +396,7 @@ il_weight *il_upload(const void *weight, int fmt, int64_t n_out, int64_t n_in) {
     return make_handle(fmt, dev, n_out, n_in, pl);
 }
 
-il_weight *il_upload_quantize(const void *weight, int src, int fmt, int64_t n_out, int64_t n_in) {
+il_weight *il_upload_quantize(const void *weight, il_src src, il_fmt fmt, int64_t n_out, int64_t n_in) {
     g_err.clear();
     if (!weight) {
         set_err("il_upload_quantize: weight is NULL");
