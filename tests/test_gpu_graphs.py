@@ -59,7 +59,8 @@ def _replay_and_compare(graph, outs, eager, between):
 # (id, fmt, t, n_in, n_outs, env pins): both decode families, the two-rows-
 # per-wave long rows, the matrix-core mid-size kernel without and with the
 # x pre-pass and in slices, GEMM halves, whole rounds of big tiles plus
-# quarters
+# quarters, and the mid-size plan with its last round split over K (272
+# units: three launches, chunk sums in the stream's scratch)
 CASES = [
     ("bf16-valu-t1", BF16, 1, 1024, [512, 300], {"IL_DECODE": "valu"}),
     ("q8-valu-t3-long-rows", Q8, 3, 8192, [40, 17], {"IL_DECODE": "valu"}),
@@ -68,7 +69,9 @@ CASES = [
     ("q4-verify-t16", Q4, 16, 1024, [500], {"IL_PREFILL": "verify"}),
     ("bf16-verify-t24", BF16, 24, 512, [300, 65], {"IL_PREFILL": "verify"}),
     ("q4-verify-slices-t70", Q4, 70, 512, [300], {"IL_PREFILL": "verify"}),
-    ("q8-gemm-halves-t40", Q8, 40, 512, [700], {"IL_PREFILL": "gemm"}),
+    ("q8-gemm-halves-t40", Q8, 40, 512, [700], {"IL_PREFILL": "tiles"}),
+    ("q4-mid-split-t100", Q4, 100, 256, [17408, 17408], {}),
+    ("q8-mid-split-t64", Q8, 64, 288, [17408, 17408], {}),
     ("q4-gemm-t300", Q4, 300, 256, [1000, 129], {}),
     ("bf16-gemm-rounds-t600", BF16, 600, 256, [22016], {}),
 ]

@@ -14,7 +14,7 @@ import pytest
 import quantized_weight_matmul_amd as il
 from quantized_weight_matmul_amd import workloads as wl
 from conftest import gpu_available
-from gpu_util import check_full, say, upload_all
+from gpu_util import check_full, check_sampled, say, upload_all
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
@@ -64,6 +64,25 @@ def test_noalloc_equals_il_matmul(fmt):
         for w, n, a, b in zip(ws, n_outs, got, ref):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"t {t} n_out {n}: differs from il_matmul"
             check_full(a, x, w, fmt, n, what=f"noalloc fmt {fmt} t {t} n_out {n}")
+
+
+@pytest.mark.parametrize("fmt", [Q8, Q4], ids=lambda f: FMT_NAME[f])
+def test_noalloc_mid_split(fmt):
+    """The mid-size plan whose last round is split over K keeps its chunk
+    sums in the static scratch too: two calls in a row (the second smaller),
+    each bitwise equal to il_matmul."""
+    g = np.random.default_rng(4300 + fmt)
+    n_in, n_outs = 256, [17408, 17408]
+    ws = [_weight(fmt, g, n, n_in) for n in n_outs]
+    hs = upload_all(ws, [fmt] * len(n_outs), n_outs, n_in)
+    for t in (100, 40):
+        say(f"[noalloc mid] fmt={FMT_NAME[fmt]} t={t} n_in={n_in} n_outs={n_outs}")
+        x = g.standard_normal((t, n_in)).astype(np.float32)
+        got = _call(il.il_matmul_noalloc, x, hs, n_outs)
+        ref = _call(il.il_matmul, x, hs, n_outs)
+        for w, n, a, b in zip(ws, n_outs, got, ref):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"t {t} n_out {n}: differs from il_matmul"
+            check_sampled(a, x, w, fmt, n, what=f"noalloc mid fmt {fmt} t {t} n_out {n}")
 
 
 def test_noalloc_size_limit():
