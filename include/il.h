@@ -140,20 +140,22 @@ IL_API void il_free(il_weight *w);
  * Validates every job first; any invalid job fails the whole call before
  * anything is enqueued (all or nothing).  Paths by t: t <= 8 the decode
  * GEMV kernels (f32 streaming or matrix-core, by format and t), one launch
- * per weight format present; 8 < t <= 32 (Q4 weights: <= 128, in even
- * slices of at most 32 tokens, one launch each) the matrix-core kernel's
- * wide mode; beyond, the MFMA GEMM: an x -> bf16 pre-pass, then one launch
- * per format (bf16: whole rounds of 256 x 256 tiles and the rest as
- * 128 x 128 quarters; Q8/Q4: 256 x 128 halves and 128 x 128 quarters, the
- * codes exact and each block's scale applied to its f32 partial sum).  All
- * jobs of one format share each launch.  The bf16 copy of x lives in a
- * buffer the library keeps per stream (grown when a call needs more, kept
- * until the process ends; while the stream is being captured into a graph
- * and that buffer is too small, the call allocates stream-ordered memory
- * instead).  A graph that captured a prefill call reads the buffer of the
- * stream it was captured on: do not replay it concurrently with other
- * prefill calls on that stream.  Asynchronous: returns after enqueueing,
- * results are valid once the stream has reached that point.
+ * per weight format present; 8 < t <= 32 the matrix-core kernel's wide
+ * mode; beyond, the MFMA GEMM: an x -> bf16 pre-pass, then one launch per
+ * format (bf16: whole rounds of 256 x 256 tiles and the rest as 128 x 128
+ * quarters; Q8/Q4: 256 x 128 halves and 128 x 128 quarters, the codes exact
+ * and each block's scale applied to its f32 partial sum; Q8/Q4 with
+ * t <= 128: units holding every token, whose last partial round is split
+ * over K and completed by a third, small launch).  All jobs of one format
+ * share each launch.  The bf16 copy of x (and the split units' partial
+ * sums) live in a buffer the library keeps per stream (grown when a call
+ * needs more, kept until the process ends; while the stream is being
+ * captured into a graph and that buffer is too small, the call allocates
+ * stream-ordered memory instead).  A graph that captured a prefill call
+ * reads the buffer of the stream it was captured on: do not replay it
+ * concurrently with other prefill calls on that stream.  Asynchronous:
+ * returns after enqueueing, results are valid once the stream has reached
+ * that point.
  * Returns 1 on success, 0 if nothing was computed (the page's `false`: the
  * caller then runs the whole batch elsewhere).  On a validation failure the
  * y buffers are untouched; if a launch itself fails their contents are
@@ -166,13 +168,16 @@ IL_API int il_matmul(const float *x, int64_t t, int64_t n_in, const il_job *jobs
  * that may not call hipMalloc, harnesses that forbid it.  Same arguments,
  * validation, kernels, results and 1 / 0 return as il_matmul, but the call
  * allocates nothing (no device memory, no events): the bf16 copy of x that
- * the prefill path (t > 8) reads lives in a static buffer of 32 MiB per
- * device, built into the library and held until the process ends.
- *   - Limit: a prefill call that needs that copy needs t * n_in * 2 bytes
- *     (rounded up to 256); when that exceeds 32 MiB (t * n_in > 16777216)
- *     the call fails before enqueueing anything, y untouched, with the sizes
- *     in il_last_error().  Decode calls (t <= 8) and the mid-size calls that
- *     round x themselves (t <= 16) use no scratch.
+ * the prefill path (t > 8) reads, and the partial sums of units split over
+ * K, live in a static buffer of 32 MiB per device, built into the library
+ * and held until the process ends.
+ *   - Limit: a prefill call needs t * n_in * 2 bytes (rounded up to 256) for
+ *     that copy, plus, for Q8/Q4 at 32 < t <= 128, 8 MiB (t <= 64) or
+ *     16 MiB of partial sums and 256 bytes; when that exceeds 32 MiB (bf16
+ *     weights: t * n_in > 16777216) the call fails before enqueueing
+ *     anything, y untouched, with the sizes in il_last_error().  Decode
+ *     calls (t <= 8) and the mid-size calls that round x themselves
+ *     (t <= 16) use no scratch.
  *   - Every call on a device shares that device's buffer: calls that overlap
  *     on one device (from several streams, or a replayed graph next to other
  *     work) race on it; order them on one stream or synchronize between them.
