@@ -13,7 +13,9 @@ around each of the call's two kernels) against 2.5 PFLOP/s dense bf16; the
 same line carries the call's device time, the graph-replay time per call,
 the eager per-call cost beside the pages' ~0.15 ms dispatch figure, the
 inputs' SHA-256, the host CPU (the shader clock is not read live: the note
-says where the counter bound on it stands), a `cpu_baseline` (the oracle on the host cores, on the first 16 rows of x)
+says where the counter bound on it stands), the il_wants threshold
+calibrated from the cost of a launch-bound call and the oracle's rate, a
+`cpu_baseline` (the oracle on the host cores, on the first 16 rows of x)
 and a `decode` object: weight GB/s against 8 TB/s of the decode workloads
 (fused bf16 t = 1, Q8 gate/up and down t = 1, Q4 t = 1, 2, 4, 8), each timed
 in a HIP graph of calls, with its eager per-call cost.
@@ -552,6 +554,40 @@ def decode_entry(il, name: str, args, stream, cache) -> dict:
     return e
 
 
+def wants_calibration(il, stream, cpu) -> dict:
+    """The il_wants threshold from measurements: the work the host oracle
+    does in the time one launch-bound call takes (eager calls of the smallest
+    configuration, bf16 [1024, 256] at t = 1, host validation and launch
+    included).  A call of fewer flops than that would finish sooner on the
+    host; il_wants should say yes above it.  Also whether the calibrated
+    threshold says yes to every configuration."""
+    sub = wl.SUBMISSIONS["c1"]
+    rig = Rig(il, sub, wl.make_x(sub), wl.make_weights(sub), 1)
+    wall_ms, _ = time_eager(rig.step, 2000, 200, stream)
+    del rig
+    out = {"tiny_call_us": round(wall_ms * 1e3, 3), "default_min_flop": 262144}
+    if cpu is None:
+        return out
+    flops_per_s = cpu["value"] * 1e12  # the oracle on every host core (prefill sample)
+    min_flop = wall_ms * 1e-3 * flops_per_s
+    old = os.environ.get("IL_WANTS_MIN_FLOP")
+    os.environ["IL_WANTS_MIN_FLOP"] = repr(min_flop)
+    try:
+        says = {n: all(il.il_wants(j.n_out, s.n_in, s.t) == 1 for j in s.jobs) for n, s in wl.SUBMISSIONS.items()}
+    finally:
+        if old is None:
+            del os.environ["IL_WANTS_MIN_FLOP"]
+        else:
+            os.environ["IL_WANTS_MIN_FLOP"] = old
+    out.update({"oracle_tflops_all_cores": cpu["value"], "calibrated_min_flop": round(min_flop),
+                "calibrated_over_default": round(min_flop / 262144, 3),
+                "yes_for_every_config": all(says.values()),
+                "no_for": sorted(n for n, v in says.items() if not v)})
+    log(f"[bench] il_wants: a launch-bound call takes {out['tiny_call_us']} us, in which the oracle does "
+        f"{min_flop:.3g} flop (default threshold 2^18 = 262144); yes for every config: {out['yes_for_every_config']}")
+    return out
+
+
 def bench_headline(args) -> int:
     """The default line: the bf16 prefill (2048 tokens through [4096 | 14336]
     x 4096, the largest configuration that fits one GPU) as TFLOP/s, with the
@@ -614,6 +650,7 @@ def bench_headline(args) -> int:
     if args.cpu_seconds > 0:
         log(f"[bench] oracle on the host cores for ~{args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(sub, x_np, weights, args.cpu_seconds)
+    wants = wants_calibration(il, stream, cpu)
 
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -636,7 +673,8 @@ def bench_headline(args) -> int:
                    "eager_us_per_call": round(ms_per_step * 1e3, 3),
                    "graph_us_per_call": round(wall_g * 1e3, 3),
                    "pages_dispatch_cost_us": PAGES_DISPATCH_US,
-                   "input_sha256_16": digests, "host": host_info(), "shader_clock": clock},
+                   "input_sha256_16": digests, "host": host_info(), "shader_clock": clock,
+                   "il_wants": wants},
         "roofline": roofline, "cpu_baseline": cpu, "decode": decode,
     }
     print(json.dumps(out), flush=True)
