@@ -23,11 +23,12 @@
 //     byte-to-address step is a single v_perm.  No
 //     offset is folded out of a sum, so every product of A and B is exact
 //     and the rounding of a result is relative to the sum of |x * w|.
-//   * A = x as 16 rows: row i < 8 holds bf16(x_i) ("hi"), row 8 + i holds
-//     bf16(x_i - hi) ("lo"), so hi + lo carries 16 significant bits of x and
-//     each product of A and B is exact in f32.  Rows of tokens >= t read
-//     zeros.  Each wave builds these operands itself from x (f32, a few KiB
-//     that stay in L2), one step ahead, in the per-lane order of the MFMA.
+//   * A = x as 16 rows: row i < t holds bf16(x_i), rounded to nearest even
+//     as on the GEMM path (relative error <= 2^-9 per element, inside the
+//     4e-3 * sum |x * w| bound), and every product of A and B is exact in
+//     f32.  Rows of tokens >= t read zeros.  Each wave builds these operands
+//     itself from x (f32, a few KiB that stay in L2), one step ahead, in the
+//     per-lane order of the MFMA.
 //   * The per-block scale multiplies the 16 x 16 f32 result (one FMA per
 //     accumulator element), so no rounding of a dequantised weight occurs.
 //   * Wide mode (8 < t <= 32): A rows are 16 tokens of bf16(x) per group
@@ -78,6 +79,11 @@ constexpr int kTile = 16;                    // weight rows per MFMA tile
 constexpr int chunk_tiles(int ng, bool glu) { return ng >= 2 ? (glu ? 4 : 6) : (glu ? 8 : 9); }
 constexpr uint32_t kBufFlags = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
 constexpr uint32_t kOut = 0x7FFFFFF0u;       // a buffer offset past every range: reads 0
+// A uniform offset base past every range: every plane and every per-lane
+// offset is below 2^31, so base + lane offset stays past the plane and below
+// 2^32 (no wrap).  The choice between a tile's base and this one is a scalar
+// select, and the load's address costs one vector add.
+constexpr uint32_t kOutBase = 0x80000000u;
 
 // Blocks of one row covered by a wave's 16-byte-per-lane step (64 bytes/row).
 template <int FMT>
@@ -131,8 +137,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));  // RNE
 }
 
-__device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
 // Dword d of lane group m -> dword m of lane group d (lanes keep l % 16).
 __device__ __forceinline__ void xpose4(uint32_t &d0, uint32_t &d1, uint32_t &d2, uint32_t &d3) {
@@ -185,24 +189,9 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f3
 }
 
 
-// A operand of one block for this lane from its 8 x values (two 16-byte
-// loads): hi lanes (lo_mask 0) take bf16(x), lo lanes (lo_mask ~0) take
-// bf16(x - bf16(x)).  Whole-vector bit casts (see bload16).
-__device__ __forceinline__ bf16x8 x_frag(const uint4 &p, const uint4 &q, uint32_t lo_mask) {
-    const f32x4 a = __builtin_bit_cast(f32x4, p);
-    const f32x4 b = __builtin_bit_cast(f32x4, q);
-    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t hm = pack_bf16(v[2 * k], v[2 * k + 1]) & lo_mask;
-        w[k] = pack_bf16(v[2 * k] - bf16_lo_f32(hm), v[2 * k + 1] - bf16_hi_f32(hm));
-    }
-    return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-}
-
-// A operand of one block in wide mode: the lane's 8 x values rounded to
-// bf16 (round-to-nearest-even, as on the GEMM path).
+// A operand of one block: the lane's 8 x values (two 16-byte loads) rounded
+// to bf16 (round-to-nearest-even, as on the GEMM path).  Whole-vector bit
+// casts (see bload16).
 __device__ __forceinline__ bf16x8 x_bf16(const uint4 &p, const uint4 &q) {
     const f32x4 a = __builtin_bit_cast(f32x4, p);
     const f32x4 b = __builtin_bit_cast(f32x4, q);
@@ -211,7 +200,7 @@ __device__ __forceinline__ bf16x8 x_bf16(const uint4 &p, const uint4 &q) {
 }
 
 struct MfmaParams {
-    const float *x;      // [t][n_in] (split mode, wide mode with one group)
+    const float *x;      // [t][n_in] (narrow mode, wide mode with one group)
     const uint16_t *xb;  // bf16(x) [t][n_in] (wide mode with two groups)
     int t;
     int n_in;
@@ -232,7 +221,8 @@ struct Chunk {
     int lrow0;  // job-local row of the chunk's first row
 };
 
-// NG = 0: "split" mode, t <= 8, A rows = bf16 hi / lo of x (f32 in memory).
+// NG = 0: "narrow" mode, t <= 8, A rows 0..t-1 = bf16(x) (f32 in memory),
+// rows 8..15 zero, so the outputs sit in lanes 0..31 (rows 0..7).
 // NG >= 1: "wide" mode, t <= 16 NG, NG groups of 16 tokens per B operand,
 // A rows = bf16(x): rounded from the f32 x as it is loaded (NG = 1) or read
 // from the pre-pass's bf16 copy (NG = 2).
@@ -240,7 +230,11 @@ struct Chunk {
 // holds TC / 2 tiles of each, slot r < TC / 2 gate tile r and slot TC / 2 + r
 // the up tile with the same rows, and the reduction writes
 // GELU(gate) * up to job 0's y.
-template <int FMT, int TC, int NG, bool GLU>
+// TE: accumulator elements per lane that hold a token (lane group g, element
+// e holds A row 4g + e): all 4 in wide mode; in narrow mode row i of token
+// i < t, so min(t, 4) -- the block scale is applied to those only (the
+// others stay 0 and are never read).
+template <int FMT, int TC, int NG, bool GLU, int TE>
 __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     constexpr int BPS = Mfma<FMT>::BPS;
     constexpr int TCh = GLU ? TC / 2 : TC;  // tiles of one job in a chunk
@@ -259,11 +253,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
     const int nb4 = (nb + 3) / 4;
     const int64_t row_bytes = mfma_row_bytes<FMT>(n_in);
 
-    // Split mode: A operand row n is the hi part of token n (n < 8) or the
-    // lo part of token n - 8.  Wide mode: row n of group q is token 16 q + n.
-    // Rows of tokens >= t read zeros.
-    const int tok = kWide ? n : (n & 7);
-    const uint32_t lo_mask = (!kWide && n >= 8) ? 0xFFFFFFFFu : 0u;
+    // A operand row n of group q is token 16 q + n; rows of tokens >= t read
+    // zeros (narrow mode: t <= 8, so rows 8..15 always do).
+    const int tok = n;
     constexpr bool kXb16 = NG >= 2;  // x given as bf16
     constexpr int esz = kXb16 ? 2 : 4;
     const __amdgpu_buffer_rsrc_t xrs =
@@ -366,9 +358,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
             // scales (16 rows x 4 blocks x 2 bytes).
             const bool ok = rt < ic.cnt;
             const uint32_t seg = (uint32_t)((ic.lrow0 >> 4) + rt) * (uint32_t)nb4 + (uint32_t)is;
-            wc[r] = bload16(wrs, ok ? (seg << 10) + q4_code_lane : kOut);
+            wc[r] = bload16(wrs, (ok ? seg << 10 : kOutBase) + q4_code_lane);
             ws[r] = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_raw_buffer_load_b64(qrs, ok ? (seg << 7) + q4_scale_lane : kOut, 0, 0));
+                uint2, __builtin_amdgcn_raw_buffer_load_b64(qrs, (ok ? seg << 7 : kOutBase) + q4_scale_lane, 0, 0));
             return;
         }
         // bf16 / Q8, row-major planes: no per-lane checks either.  A row past
@@ -378,12 +370,12 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
         // (x past n_in reads zeros) and the zero padded scale, so it adds 0.
         const bool ok = rt < ic.cnt;
         const uint32_t row0 = (uint32_t)(ic.lrow0 + kTile * rt);
-        wc[r] = bload16(wrs, ok ? row0 * (uint32_t)row_bytes + ((uint32_t)is << 6) + rm_code_lane : kOut);
+        wc[r] = bload16(wrs, (ok ? row0 * (uint32_t)row_bytes + ((uint32_t)is << 6) : kOutBase) + rm_code_lane);
         if constexpr (FMT == FMT_Q8) {
             // this lane's 16 bytes are half of block 2s + g/2: scale index
             // ((tile * nb4 + s/2) * 64) + 4 n + 2 (s % 2) + g/2 in the tiled plane
             const uint32_t tq = ((row0 >> 4) * (uint32_t)nb4 + ((uint32_t)is >> 1)) * 64u + (((uint32_t)is & 1u) << 1);
-            ws[r] = __builtin_amdgcn_raw_buffer_load_b32(qrs, ok ? (tq + q8_scale_lane) * 4u : kOut, 0, 0);
+            ws[r] = __builtin_amdgcn_raw_buffer_load_b32(qrs, (ok ? tq * 4u : kOutBase) + q8_scale_lane * 4u, 0, 0);
         }
     };
     auto advance = [&](Chunk &c, int &s) {
@@ -410,22 +402,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
 #pragma unroll
             for (int r = 0; r < TC; ++r) {
                 if (r % TCh < c.cnt) {
-                    if constexpr (kWide) {
-                        red[wave][r][lane] = acc[r][q];
-                    } else {
-                        // rows 8..15 (lo) of lanes 32..63 onto rows 0..7 of lanes 0..31
-                        // (whole-vector bit casts only, see bload16)
-                        const uint4 ai = __builtin_bit_cast(uint4, acc[r][q]);
-                        const uint32_t av[4] = {ai.x, ai.y, ai.z, ai.w};
-                        f32x4 v;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const auto h = __builtin_amdgcn_permlane32_swap(av[e], av[e], false, false);
-                            const f32x2 hf = __builtin_bit_cast(f32x2, h);
-                            v[e] = hf[0] + hf[1];
-                        }
-                        if (lane < 32) red[wave][r][lane] = v;
-                    }
+                    // narrow mode: rows 0..7 are lanes 0..31
+                    if (kWide || lane < 32) red[wave][r][lane] = acc[r][q];
                 }
                 acc[r][q] = (f32x4){0.f, 0.f, 0.f, 0.f};
             }
@@ -481,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
 #pragma unroll
             for (int q = 0; q < NA; ++q)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[r][q][e] = fmaf(scf[1], p1[q][e], fmaf(scf[0], p0[q][e], acc[r][q][e]));
+                for (int e = 0; e < TE; ++e) acc[r][q][e] = fmaf(scf[1], p1[q][e], fmaf(scf[0], p0[q][e], acc[r][q][e]));
         } else {
             uint32_t d[4] = {wc[r].x, wc[r].y, wc[r].z, wc[r].w};
             xpose4(d[0], d[1], d[2], d[3]);
@@ -502,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
 #pragma unroll
                 for (int q = 0; q < NA; ++q)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[r][q][e] = fmaf(sf, pj[q][jb][e], acc[r][q][e]);
+                    for (int e = 0; e < TE; ++e) acc[r][q][e] = fmaf(sf, pj[q][jb][e], acc[r][q][e]);
             }
         }
     };
@@ -545,10 +523,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
             if constexpr (kXb16) {
 #pragma unroll
                 for (int q = 0; q < NA; ++q) a[q][jb] = __builtin_bit_cast(bf16x8, xw[q][jb]);
-            } else if constexpr (kWide) {
-                a[0][jb] = x_bf16(xr[0][jb][0], xr[0][jb][1]);
             } else {
-                a[0][jb] = x_frag(xr[0][jb][0], xr[0][jb][1], lo_mask);
+                a[0][jb] = x_bf16(xr[0][jb][0], xr[0][jb][1]);
             }
         }
         issue_x();
@@ -570,16 +546,19 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(MfmaParams p) {
 
 namespace {
 
-// every buffer offset a lane forms stays below 2^31
+// every buffer offset a lane forms stays below 2^31: with row-major planes
+// that includes the rows of a job's last tile past n_out (16-row padding) and
+// the 32 bytes a Q8 row's last step reads past its end
 bool mfma_fits(int fmt, int64_t x_bytes, int n_in, const KJob *jobs, int n_jobs) {
     if (n_in <= 0 || n_in % kBlock || x_bytes >= (1ll << 31) || n_jobs < 1 || n_jobs > kMaxJobs) return false;
     const int64_t rb = fmt == FMT_BF16 ? 2ll * n_in : (int64_t)n_in;
     const int64_t sb = fmt == FMT_Q8 ? 4 : 2;
-    for (int j = 0; j < n_jobs; ++j)
-        if ((fmt == FMT_Q4 ? q4_plane_bytes(jobs[j].n_out, n_in / kBlock) : (int64_t)jobs[j].n_out * rb) >=
-                (1ll << 31) ||
+    for (int j = 0; j < n_jobs; ++j) {
+        const int64_t rows16 = (jobs[j].n_out + kTile - 1) / kTile * kTile;
+        if ((fmt == FMT_Q4 ? q4_plane_bytes(jobs[j].n_out, n_in / kBlock) : rows16 * rb + 64) >= (1ll << 31) ||
             tiled_scale_count(jobs[j].n_out, n_in / kBlock) * sb >= (1ll << 31))
             return false;
+    }
     return true;
 }
 
@@ -603,13 +582,22 @@ bool fill_params(MfmaParams &p, int fmt, int t, int n_in, const KJob *jobs, int 
     return tiles > 0;
 }
 
+template <int FMT, int NG, bool GLU, int TE>
+hipError_t launch_te(const MfmaParams &p, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((gemv_mfma_kernel<FMT, chunk_tiles(NG, GLU), NG, GLU, TE>), dim3(grid), dim3(kThreads), 0,
+                       s, p);
+    return hipGetLastError();
+}
+
 template <int FMT, int NG, bool GLU>
 hipError_t launch_mode(const MfmaParams &p, int cu_count, hipStream_t s) {
     // one workgroup per compute unit at most, each an equal share of the tiles
     const int grid = p.tiles_total < cu_count ? p.tiles_total : cu_count;
-    hipLaunchKernelGGL((gemv_mfma_kernel<FMT, chunk_tiles(NG, GLU), NG, GLU>), dim3(grid), dim3(kThreads), 0, s,
-                       p);
-    return hipGetLastError();
+    if constexpr (NG == 0) {
+        if (p.t == 1) return launch_te<FMT, NG, GLU, 1>(p, grid, s);
+        if (p.t == 2) return launch_te<FMT, NG, GLU, 2>(p, grid, s);
+    }
+    return launch_te<FMT, NG, GLU, 4>(p, grid, s);
 }
 
 template <int NG>

@@ -35,12 +35,6 @@ def _bf16_rne(a):
     return bits.view(np.float32)
 
 
-def _hi_lo(a):
-    """The x the matrix-core decode kernel multiplies: bf16(x) + bf16(x - bf16(x)), in f32."""
-    hi = _bf16_rne(a)
-    return (hi + _bf16_rne((a - hi).astype(np.float32))).astype(np.float32)
-
-
 def _paths(t):
     if t <= 8:
         return ("valu", "mfma")
@@ -64,7 +58,7 @@ def _selected(x, path):
     """What a one-hot weight row returns for x on each path."""
     if path == "valu":
         return x
-    return _hi_lo(x) if path == "mfma" else _bf16_rne(x)  # verify and gemm: bf16(x)
+    return _bf16_rne(x)  # matrix-core decode, verify and gemm: bf16(x)
 
 
 # ------------------------------------------------------------- workloads
@@ -387,9 +381,9 @@ def _onehot(fmt, n_out, n_in, cols):
 @pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
 @pytest.mark.parametrize("t,path", _decode_cases([1, 3, 8, 9, 20, 200]))
 def test_onehot_selects_columns(fmt, t, path, monkeypatch):
-    """One-hot W: y[:, r] = x[:, c_r] exactly on the f32 decode path, the
-    bf16 hi + lo split of it on the matrix-core decode path, and bf16(x)
-    on the GEMM path."""
+    """One-hot W: y[:, r] = x[:, c_r] exactly on the f32 decode path and
+    bf16(x) (round to nearest even) on the matrix-core paths (decode, verify
+    and GEMM)."""
     _pin(monkeypatch, path)
     g = np.random.default_rng(20 + t)
     n_in, n_out = 320, 300
