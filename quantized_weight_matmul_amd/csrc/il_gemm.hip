@@ -40,6 +40,7 @@
 // slices its workgroups share.
 #include "il_internal.h"
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -204,14 +205,20 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], const KJ
     }
 }
 
-// x f32 -> bf16 (RNE) pre-pass: groups of 8 elements (32 bytes in, 16 out);
-// a workgroup covers kPreGroups * 256 consecutive groups, thread i the groups
-// i, i + 256, ..., all of whose loads are issued before the first store.
-constexpr int kPreGroups = 4;
+// x f32 -> bf16 (RNE) pre-pass: groups of 8 elements (32 bytes in, 16 out).
+// A grid of at most kPreWgPerCu workgroups per compute unit strides over the
+// groups, kPreGroups * 256 consecutive ones per workgroup and round (thread i
+// the groups i, i + 256, ...); each thread loads its next round's groups
+// before it stores this round's, so reads and writes overlap (50 MB on the
+// 2048-token prefill: 14.1 against 15.8-16.0 us with one round per
+// workgroup, by HIP events).
+constexpr int kPreGroups = 2;
+constexpr int kPreWgPerCu = 8;
 __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float *__restrict__ x, uint4 *__restrict__ xb,
                                                         int64_t n8) {
-    const int64_t g0 = (int64_t)blockIdx.x * (256 * kPreGroups) + threadIdx.x;
     const float4 *x4 = reinterpret_cast<const float4 *>(x);
+    const int64_t stride = (int64_t)gridDim.x * (256 * kPreGroups);
+    int64_t g0 = (int64_t)blockIdx.x * (256 * kPreGroups) + threadIdx.x;
     float4 a[kPreGroups], b[kPreGroups];
 #pragma unroll
     for (int u = 0; u < kPreGroups; ++u) {
@@ -221,12 +228,30 @@ __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float *__restrict_
             b[u] = x4[2 * g + 1];
         }
     }
+    while (g0 < n8) {
+        const int64_t gn = g0 + stride;
+        float4 a2[kPreGroups], b2[kPreGroups];
 #pragma unroll
-    for (int u = 0; u < kPreGroups; ++u) {
-        const int64_t g = g0 + u * 256;
-        if (g < n8)
-            xb[g] = make_uint4(pack_bf16(a[u].x, a[u].y), pack_bf16(a[u].z, a[u].w), pack_bf16(b[u].x, b[u].y),
-                               pack_bf16(b[u].z, b[u].w));
+        for (int u = 0; u < kPreGroups; ++u) {
+            const int64_t g = gn + u * 256;
+            if (g < n8) {
+                a2[u] = x4[2 * g];
+                b2[u] = x4[2 * g + 1];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kPreGroups; ++u) {
+            const int64_t g = g0 + u * 256;
+            if (g < n8)
+                xb[g] = make_uint4(pack_bf16(a[u].x, a[u].y), pack_bf16(a[u].z, a[u].w), pack_bf16(b[u].x, b[u].y),
+                                   pack_bf16(b[u].z, b[u].w));
+        }
+#pragma unroll
+        for (int u = 0; u < kPreGroups; ++u) {
+            a[u] = a2[u];
+            b[u] = b2[u];
+        }
+        g0 = gn;
     }
 }
 
@@ -1247,8 +1272,9 @@ hipError_t launch_gemm(int fmt, const float *x, void *xb_scratch, int t, int n_i
     // x -> bf16 into the caller's scratch
     const int64_t n8 = (int64_t)t * n_in / 8;
     uint16_t *xb = static_cast<uint16_t *>(xb_scratch);
-    hipLaunchKernelGGL(x_to_bf16_kernel, dim3((unsigned)((n8 + 256 * kPreGroups - 1) / (256 * kPreGroups))), dim3(256),
-                       0, s, x, reinterpret_cast<uint4 *>(xb), n8);
+    const int64_t pre_wgs = std::min<int64_t>((n8 + 256 * kPreGroups - 1) / (256 * kPreGroups),
+                                              (int64_t)cu_count * kPreWgPerCu);
+    hipLaunchKernelGGL(x_to_bf16_kernel, dim3((unsigned)pre_wgs), dim3(256), 0, s, x, reinterpret_cast<uint4 *>(xb), n8);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && after_prepass) e = hipEventRecord(after_prepass, s);
     if (e != hipSuccess) return e;
