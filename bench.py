@@ -420,14 +420,14 @@ def smi_sample() -> dict:
     graphics clock of each XCD, the memory clock and the power figures."""
     exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
     try:
-        r = subprocess.run([exe, "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True,
-                           text=True, timeout=30)
+        r = subprocess.run([exe, "metric", "-g", "0", "--clock", "--power", "--usage", "--json"],
+                           capture_output=True, text=True, timeout=30)
         text = r.stdout
         d = json.loads(text[text.index("{"):])
     except (OSError, ValueError, subprocess.SubprocessError) as e:
         return {"error": f"{type(e).__name__}: {str(e)[:160]}"}
     g = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else (d[0] if isinstance(d, list) else d)
-    out = {"gfx_mhz": [], "mem_mhz": None, "power": {}}
+    out = {"gfx_mhz": [], "mem_mhz": None, "power": {}, "usage": {}}
     for k, v in (g.get("clock") or {}).items():
         clk = v.get("clk", {}) if isinstance(v, dict) else {}
         val = clk.get("value") if isinstance(clk, dict) else None
@@ -435,9 +435,10 @@ def smi_sample() -> dict:
             out["gfx_mhz"].append(val)
         elif k.startswith("mem") and isinstance(val, (int, float)):
             out["mem_mhz"] = val
-    for k, v in (g.get("power") or {}).items():
-        if isinstance(v, dict) and isinstance(v.get("value"), (int, float)):
-            out["power"][k] = [v["value"], v.get("unit")]
+    for part in ("power", "usage"):
+        for k, v in (g.get(part) or {}).items():
+            if isinstance(v, dict) and isinstance(v.get("value"), (int, float)):
+                out[part][k] = [v["value"], v.get("unit")]
     return out
 
 
@@ -656,8 +657,8 @@ def bench_headline(args) -> int:
     clock = {"live_mhz": None, "max_engine_mhz": 2400,
              "note": "not read in the kernels; SQ_BUSY_CYCLES / 32 shader arrays over the GEMM's duration bounds "
                      "it, profiles/gemm_bf16_prefill_2048x18432x4096.txt; smi_under_load: one amd-smi reading "
-                     "taken while bursts of these calls run (the tool's own averaging: its gfx clock has read "
-                     "~1 GHz here, below that counter bound, so no figure uses it)"}
+                     "taken while bursts of these calls run (the tool's own sampling: its gfx clock has read "
+                     "150 MHz to 1 GHz here, below that counter bound, so no figure uses it)"}
     smi = {}
     sampler = threading.Thread(target=lambda: smi.update(smi_sample()), daemon=True)
     sampler.start()
