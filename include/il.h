@@ -147,7 +147,11 @@ IL_API void il_free(il_weight *w);
  * and each block's scale applied to its f32 partial sum; Q8/Q4 with
  * t <= 128: units holding every token, whose last partial round is split
  * over K and completed by a third, small launch).  All jobs of one format
- * share each launch.  The bf16 copy of x (and the split units' partial
+ * share each launch.  Accuracy: every y element is within 4e-3 of the sum
+ * of |x_k * w_k| over its reduction of the exact result; the f32 streaming
+ * decode kernel keeps x in f32, the matrix-core paths (decode, wide mode
+ * and GEMM) round x to bf16 (nearest even, < 3.9e-3 relative) and nothing
+ * else: codes, scales and products are exact, sums in f32.  The bf16 copy of x (and the split units' partial
  * sums) live in a buffer the library keeps per stream (grown when a call
  * needs more, kept until the process ends; while the stream is being
  * captured into a graph and that buffer is too small, the call allocates

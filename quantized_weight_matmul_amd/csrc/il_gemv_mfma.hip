@@ -1,4 +1,4 @@
-// il_gemv_mfma.hip -- decode GEMV on the bf16 matrix cores (small t > 1),
+// il_gemv_mfma.hip -- decode GEMV on the bf16 matrix cores (t <= 8),
 // and its "wide" mode for mid-size t (speculative-verify batches, 8 < t <= 32
 // per launch; the prefill dispatch runs Q4 weights in slices of up to 32
 // tokens to t = 128).
@@ -24,9 +24,10 @@
 //     offset is folded out of a sum, so every product of A and B is exact
 //     and the rounding of a result is relative to the sum of |x * w|.
 //   * A = x as 16 rows: row i < t holds bf16(x_i), rounded to nearest even
-//     as on the GEMM path (relative error <= 2^-9 per element, inside the
-//     4e-3 * sum |x * w| bound), and every product of A and B is exact in
-//     f32.  Rows of tokens >= t read zeros.  Each wave builds these operands
+//     as on the GEMM path (relative error at most 2^-8 / (1 + 2^-8), about
+//     3.89e-3, per element; with the f32 sums, whose tree is a few hundred
+//     additions deep, inside the 4e-3 * sum |x * w| bound), and every product
+//     of A and B is exact in f32.  Rows of tokens >= t read zeros.  Each wave builds these operands
 //     itself from x (f32, a few KiB that stay in L2), one step ahead, in the
 //     per-lane order of the MFMA.
 //   * The per-block scale multiplies the 16 x 16 f32 result (one FMA per
