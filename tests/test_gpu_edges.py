@@ -145,3 +145,32 @@ def test_onehot_off_grid_values(fmt, t, path, monkeypatch):
     (y,) = run(x, [h], [n_out])
     r = check_full(y, x, w, fmt, n_out, what=f"one-hot off grid fmt {fmt} t {t} {path}")
     say(f"  worst |err|/bound = {r['worst']:.2e}")
+
+
+@pytest.mark.parametrize("fmt", [BF16, Q8, Q4], ids=lambda f: FMT_NAME[f])
+@pytest.mark.parametrize("t,path", _cases())
+def test_dense_midpoint_bias(fmt, t, path, monkeypatch):
+    """Every x at a bf16 rounding midpoint ((1 + 2^-8) * 2^k, which rounds to
+    2^k: each term loses 2^-8 / (1 + 2^-8) of itself) and every weight of
+    the same sign, over 5120 inputs: on the paths that round x to bf16 the
+    error of each output is that whole bias, ~0.973 of the 4e-3 tolerance,
+    plus the f32 sums of every kernel -- the margin the bound leaves."""
+    _pin(monkeypatch, path)
+    g = np.random.default_rng(3400 + 11 * t + fmt)
+    n_in, n_out = 5120, 272
+    nb = n_in // 32
+    say(f"[edge dense midpoint] fmt={FMT_NAME[fmt]} t={t} path={path}")
+    x = (np.float32(1 + 2 ** -8) * np.float32(2.0) ** g.integers(-3, 4, (t, n_in))).astype(np.float32)
+    x *= np.where(np.arange(t) % 2 == 0, 1, -1).astype(np.float32)[:, None]  # one sign per token
+    if fmt == BF16:
+        w = wl.f32_to_bf16_bits(g.uniform(0.5, 2.0, (n_out, n_in)).astype(np.float32))
+    elif fmt == Q8:
+        w = wl.encode_q8(g.integers(1, 128, (n_out, n_in)).astype(np.int8),
+                         g.uniform(1e-3, 1e-2, (n_out, nb)).astype(np.float32))
+    else:
+        w = wl.encode_q4(g.integers(9, 16, (n_out, n_in)).astype(np.uint8),
+                         g.uniform(1e-3, 1e-2, (n_out, nb)).astype(np.float16).view(np.uint16))
+    (h,) = upload_all([w], [fmt], [n_out], n_in)
+    (y,) = run(x, [h], [n_out])
+    r = check_full(y, x, w, fmt, n_out, what=f"dense midpoint fmt {fmt} t {t} {path}")
+    say(f"  worst |err|/bound = {r['worst']:.6f} ({r['worst'] / 4e-3:.4f} of the tolerance)")
