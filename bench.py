@@ -13,7 +13,8 @@ around each of the call's two kernels) against 2.5 PFLOP/s dense bf16; the
 same line carries the call's device time, the graph-replay time per call,
 the eager per-call cost beside the pages' ~0.15 ms dispatch figure, the
 inputs' SHA-256, the host CPU (the shader clock is not read live: the note
-says where the counter bound on it stands), the il_wants threshold
+says where the counter bound on it stands, beside one amd-smi clock and
+power reading taken under the calls), the il_wants threshold
 calibrated from the cost of a launch-bound call and the oracle's rate, a
 `cpu_baseline` (the oracle on the host cores, on the first 16 rows of x)
 and a `decode` object: weight GB/s against 8 TB/s of the decode workloads
@@ -21,7 +22,10 @@ and a `decode` object: weight GB/s against 8 TB/s of the decode workloads
 in a HIP graph of calls, with its eager per-call cost.
 
 --workload NAME times one workload alone (graph replay, or eager with
---no-graph) and prints its own line in the same form.
+--no-graph) and prints its own line in the same form.  --decode-sweep times
+both decode kernel families and the library's choice between them over
+model-like shapes; --calibrate-read / --calibrate-copy time a plain read and
+a plain copy (the read ceiling and the counter scaling).
 """
 from __future__ import annotations
 
@@ -723,6 +727,59 @@ def bench_headline(args) -> int:
     return 0
 
 
+# Decode shapes of model-like layers for the dispatch sweep: (format, n_out
+# of each job, n_in).
+SWEEP_SHAPES = [(wl.Q4, [17408, 17408], 5120), (wl.Q4, [4096, 1024, 1024], 4096), (wl.Q4, [4096], 14336),
+                (wl.Q4, [1024], 4096), (wl.Q8, [14336, 14336], 4096), (wl.Q8, [4096], 14336),
+                (wl.Q8, [1024, 1024], 4096)]
+
+
+def decode_sweep(args) -> int:
+    """Both decode kernel families (IL_DECODE=valu / mfma) and the library's
+    own choice over model-like shapes at t = 1, 2, 4, 8: device us per call
+    (HIP events around a burst of eager calls, weights rotated past the
+    last-level cache); one JSON line."""
+    import torch
+
+    import quantized_weight_matmul_amd as il
+    stream = torch.cuda.Stream()  # default priority
+    rows = []
+    for fmt, n_outs, n_in in SWEEP_SHAPES:
+        ws = [wl.gen_weight(fmt, 90, j, n, n_in) for j, n in enumerate(n_outs)]
+        bytes_set = sum(int(w.nbytes) for w in ws)
+        n_sets = max(1, -(-ROTATE_BYTES // bytes_set))
+        sets = [[il.il_upload(w, fmt, n, n_in) for w, n in zip(ws, n_outs)] for _ in range(n_sets)]
+        if any(h is None for hs in sets for h in hs):
+            raise RuntimeError(il.il_last_error())
+        for t in (1, 2, 4, 8):
+            x = torch.from_numpy(np.random.default_rng(t).standard_normal((t, n_in)).astype(np.float32)).cuda()
+            ys = [torch.empty(t, n, device="cuda") for n in n_outs]
+
+            def step(i, s):
+                hs = sets[i % n_sets]
+                if il.il_matmul(x, t, n_in, [(h, n, y) for h, n, y in zip(hs, n_outs, ys)], stream=s) != 1:
+                    raise RuntimeError(il.il_last_error())
+            row = {"fmt": wl.FMT_NAMES[fmt], "n_outs": n_outs, "n_in": n_in, "t": t}
+            for mode in ("valu", "mfma", "auto"):
+                if mode == "auto":
+                    os.environ.pop("IL_DECODE", None)
+                else:
+                    os.environ["IL_DECODE"] = mode
+                _, dev_ms = time_eager(step, args.steps, args.warmup, stream)
+                row[f"{mode}_us"] = round(dev_ms * 1e3, 2)
+            os.environ.pop("IL_DECODE", None)
+            row["auto_is_faster_family"] = row["auto_us"] <= 1.05 * min(row["valu_us"], row["mfma_us"])
+            log(f"[sweep] {row['fmt']} {n_outs} x {n_in} t={t}: streaming {row['valu_us']} us, matrix-core "
+                f"{row['mfma_us']} us, dispatch {row['auto_us']} us")
+            rows.append(row)
+        for hs in sets:
+            for h in hs:
+                il.il_free(h)
+    print(json.dumps({"metric": "decode kernel dispatch sweep", "unit": "device us per call", "steps": args.steps,
+                      "rows": rows}), flush=True)
+    return 0
+
+
 def calibrate_read(sizes_mb) -> int:
     """The read ceiling: il_read_probe (a plain streaming read, no arithmetic)
     over buffers of the given sizes, rotated so that one rotation exceeds
@@ -784,6 +841,8 @@ def main() -> int:
     ap.add_argument("--calibrate-read", default="", metavar="MB[,MB...]",
                     help="only time a plain streaming read (il_read_probe) of buffers of these sizes in a "
                          "sweep of launch shapes: the read ceiling of the decode kernels")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="only time both decode kernel families and the dispatch's choice over model-like shapes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -802,6 +861,8 @@ def main() -> int:
 
     if args.calibrate_read:
         return calibrate_read([float(v) for v in args.calibrate_read.split(",")])
+    if args.decode_sweep:
+        return decode_sweep(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "

@@ -656,20 +656,35 @@ hipError_t launch_fmt(GemvParams &p, int cu_count, hipStream_t s) {
 
 }  // namespace
 
-// Smallest t at which the matrix-core decode kernel beats the streaming
-// kernel for a format: where the f32 vector work per weight byte (2t flops
-// per element plus the dequantisation) stops fitting under the HBM time.
-// Q4 takes the matrix cores from t = 1: its table-driven code conversion
-// costs fewer vector instructions per byte than the streaming kernel's
-// per-element convert and FMA (measured: 29.5 vs 35.1 us on 2 x [17408, 5120]).
-static int mfma_min_t(int fmt) { return fmt == FMT_Q4 ? 1 : fmt == FMT_Q8 ? 4 : kGemvMaxT + 1; }
+// Which decode kernel a call takes.  The streaming kernel's f32 vector work
+// per weight byte (2t flops per element plus the dequantisation) grows with
+// t; the matrix-core kernel's does not, but it keeps a whole step of loads in
+// flight only across the 16-row tiles a workgroup owns, so with few tiles
+// per compute unit (short or few jobs) it streams slowly.  Measured per call
+// (us, streaming / matrix-core, one box):
+//   Q4 2 x [17408, 5120] (136 rows per CU): t = 1 36.5 / 25.4, t = 8 337 / 26.0
+//   Q4 [4096 + 1024 + 1024, 4096] (24):     t = 1 8.7 / 20.0, t = 8 19.7 / 22.9
+//   Q4 [4096, 14336] (16):                   t = 2 22.0 / 31.7, t = 4 38.2 / 33.5
+//   Q4 [1024, 4096] (4):                     t = 4 11.6 / 13.2, t = 8 18.6 / 14.1
+//   Q8 2 x [14336, 4096] (112):              t = 2 31.3 / 32.8, t = 4 44.3 / 32.9
+//   Q8 [4096, 14336] (16):                   t = 4 41.8 / 55.0, t = 8 65.9 / 57.8
+//   Q8 2 x [1024, 4096] (8):                 t = 8 10.7 / 19.5
+// bf16 always streams (its vector work is a shift and an FMA per element).
+static bool decode_on_matrix_cores(int fmt, int t, int n_in, const KJob *jobs, int n_jobs, int cu_count) {
+    int64_t rows = 0;
+    for (int j = 0; j < n_jobs; ++j) rows += jobs[j].n_out;
+    const int64_t per_cu = rows / (cu_count > 0 ? cu_count : 1);
+    if (fmt == FMT_Q4) return per_cu >= 64 || (t >= 4 && n_in >= 8192) || (t >= 8 && per_cu <= 8);
+    if (fmt == FMT_Q8) return (per_cu >= 64 && t >= 4) || (t >= 8 && n_in >= 8192);
+    return false;
+}
 
 hipError_t launch_gemv(int fmt, const float *x, int t, int n_in, const KJob *jobs, int n_jobs,
                        int cu_count, hipStream_t s, bool glu) {
     if (t < 1 || t > kGemvMaxT || n_jobs < 1 || n_jobs > kMaxJobs) return hipErrorInvalidValue;
     if (glu && (n_jobs != 2 || jobs[0].n_out != jobs[1].n_out)) return hipErrorInvalidValue;
     // IL_DECODE=valu|mfma pins the kernel family (both compute the same sums)
-    bool use_mfma = t >= mfma_min_t(fmt);
+    bool use_mfma = decode_on_matrix_cores(fmt, t, n_in, jobs, n_jobs, cu_count);
     if (const char *force = getenv("IL_DECODE")) {
         if (!strcmp(force, "mfma")) use_mfma = true;
         if (!strcmp(force, "valu")) use_mfma = false;
