@@ -418,20 +418,44 @@ def host_info() -> dict:
     return {"cpu_model": model, "nproc": os.cpu_count(), "oracle_threads": threads}
 
 
-def smi_sample() -> dict:
-    """One `amd-smi metric --clock --power` reading of GPU 0 (the tool's own
-    sampling window; a child process, so nothing here touches the GPU): the
-    graphics clock of each XCD, the memory clock and the power figures."""
+def hip_bus_id() -> str:
+    """PCI bus id ("dddd:bb:dd.f") of the HIP device this process uses."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL("libamdhip64.so")
+    buf = ctypes.create_string_buffer(64)
+    if lib.hipDeviceGetPCIBusId(buf, 64, torch.cuda.current_device()) != 0:
+        raise RuntimeError("hipDeviceGetPCIBusId failed")
+    return buf.value.decode().lower()
+
+
+def _json_of(text: str):
+    starts = [i for i in (text.find("{"), text.find("[")) if i >= 0]
+    return json.loads(text[min(starts):])
+
+
+def smi_sample(bus_id: str) -> dict:
+    """One `amd-smi metric --clock --power --usage` reading of the GPU with
+    this PCI bus id (amd-smi numbers every GPU of the host, not only the ones
+    this process sees; the tool's own sampling window; child processes, so
+    nothing here touches the GPU): the graphics clock of each XCD, the
+    memory clock, power and activity."""
     exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
     try:
-        r = subprocess.run([exe, "metric", "-g", "0", "--clock", "--power", "--usage", "--json"],
+        lst = _json_of(subprocess.run([exe, "list", "--json"], capture_output=True, text=True, timeout=30).stdout)
+        idx = None
+        for e in (lst if isinstance(lst, list) else lst.get("gpu_data", [])):
+            if str(e.get("bdf", "")).lower() == bus_id:
+                idx = e.get("gpu")
+        if idx is None:
+            return {"error": f"no amd-smi GPU with bus id {bus_id}", "bus_id": bus_id}
+        r = subprocess.run([exe, "metric", "-g", str(idx), "--clock", "--power", "--usage", "--json"],
                            capture_output=True, text=True, timeout=30)
-        text = r.stdout
-        d = json.loads(text[text.index("{"):])
-    except (OSError, ValueError, subprocess.SubprocessError) as e:
-        return {"error": f"{type(e).__name__}: {str(e)[:160]}"}
+        d = _json_of(r.stdout)
+    except (OSError, ValueError, KeyError, AttributeError, subprocess.SubprocessError) as e:
+        return {"error": f"{type(e).__name__}: {str(e)[:160]}", "bus_id": bus_id}
     g = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else (d[0] if isinstance(d, list) else d)
-    out = {"gfx_mhz": [], "mem_mhz": None, "power": {}, "usage": {}}
+    out = {"bus_id": bus_id, "amd_smi_gpu": idx, "gfx_mhz": [], "mem_mhz": None, "power": {}, "usage": {}}
     for k, v in (g.get("clock") or {}).items():
         clk = v.get("clk", {}) if isinstance(v, dict) else {}
         val = clk.get("value") if isinstance(clk, dict) else None
@@ -443,6 +467,28 @@ def smi_sample() -> dict:
         for k, v in (g.get(part) or {}).items():
             if isinstance(v, dict) and isinstance(v.get("value"), (int, float)):
                 out[part][k] = [v["value"], v.get("unit")]
+    return out
+
+
+def smi_under_load(bus_id: str, first_after_s: float = 1.5, n: int = 3, gap_s: float = 0.5) -> dict:
+    """amd-smi readings taken while the caller keeps the GPU busy: its
+    metrics lag the load by about a second, so the first is taken
+    first_after_s into the burst, then n - 1 more gap_s apart.  Summary over
+    the readings that show the GPU busy (gfx activity >= 90 %): the median
+    of their mean XCD clock and of their socket power."""
+    time.sleep(first_after_s)
+    reads = []
+    for i in range(n):
+        if i:
+            time.sleep(gap_s)
+        reads.append(smi_sample(bus_id))
+    busy = [r for r in reads if (r.get("usage", {}).get("gfx_activity") or [0])[0] >= 90 and r.get("gfx_mhz")]
+    out = {"readings": reads, "busy_readings": len(busy)}
+    if busy:
+        out["gfx_mhz_median"] = float(np.median([sum(r["gfx_mhz"]) / len(r["gfx_mhz"]) for r in busy]))
+        watts = [r["power"]["socket_power"][0] for r in busy if "socket_power" in r.get("power", {})]
+        if watts:
+            out["socket_power_w_median"] = float(np.median(watts))
     return out
 
 
@@ -661,17 +707,23 @@ def bench_headline(args) -> int:
     clock = {"live_mhz": None, "max_engine_mhz": 2400,
              "note": "not read in the kernels; SQ_BUSY_CYCLES / 32 shader arrays over the GEMM's duration bounds "
                      "it, profiles/gemm_bf16_prefill_2048x18432x4096.txt; smi_under_load: one amd-smi reading "
-                     "taken while bursts of these calls run (the tool's own sampling: its gfx clock has read "
-                     "150 MHz to 1 GHz here, below that counter bound, so no figure uses it)"}
+                     "series of this process's GPU (matched by PCI bus id) taken while bursts of these calls run "
+                     "(its metrics lag the load by about a second); the roofline keeps the published peak"}
     smi = {}
-    sampler = threading.Thread(target=lambda: smi.update(smi_sample()), daemon=True)
+    try:
+        bus = hip_bus_id()
+    except (OSError, RuntimeError, AttributeError) as e:
+        bus = f"unknown ({type(e).__name__})"
+    sampler = threading.Thread(target=lambda: smi.update(smi_under_load(bus)), daemon=True)
     sampler.start()
     t_end = time.perf_counter() + 30.0
     while sampler.is_alive() and time.perf_counter() < t_end:
         burst(0.5)()  # keep the GPU on this workload while the tool samples
     sampler.join(timeout=1.0)
     clock["smi_under_load"] = smi or {"error": "no reading within 30 s"}
-    log(f"[bench] amd-smi during the calls: {clock['smi_under_load']}")
+    log(f"[bench] amd-smi during the calls: {clock['smi_under_load'].get('busy_readings')} busy readings, "
+        f"gfx {clock['smi_under_load'].get('gfx_mhz_median')} MHz, "
+        f"{clock['smi_under_load'].get('socket_power_w_median')} W")
     burst(args.settle)()
     # ---- timed region: K eager calls (host validation and launches included) ----
     ms_per_step, dev_ms = time_eager(rig.step, args.steps, args.warmup, stream)
