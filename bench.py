@@ -8,8 +8,9 @@ timed steps are eager calls bracketed by synchronisations (host validation
 and launches included); weight copies are rotated so that one rotation
 exceeds 1 GiB and every step reads its weights from HBM, not from the
 256 MiB last-level cache.  value = TFLOP/s of whole calls.  `roofline` takes
-the GEMM kernel alone (HIP events the library records on the launch stream
-around each of the call's two kernels) against 2.5 PFLOP/s dense bf16; the
+the GEMM kernel alone (median over calls of the HIP events the library
+records on the launch stream around each of the call's two kernels, a
+512 MiB scratch write before each call) against 2.5 PFLOP/s dense bf16; the
 same line carries the call's device time, the graph-replay time per call,
 the eager per-call cost beside the pages' ~0.15 ms dispatch figure, the
 inputs' SHA-256, the host CPU (the shader clock is not read live: the note
@@ -19,7 +20,8 @@ calibrated from the cost of a launch-bound call and the oracle's rate, a
 `cpu_baseline` (the oracle on the host cores, on the first 16 rows of x)
 and a `decode` object: weight GB/s against 8 TB/s of the decode workloads
 (fused bf16 t = 1, Q8 gate/up and down t = 1, Q4 t = 1, 2, 4, 8), each timed
-in a HIP graph of calls, with its eager per-call cost.
+in a HIP graph of calls, with its eager per-call cost and the oracle's
+time over the same submission (median of 3, on one host core and on all).
 
 --workload NAME times one workload alone (graph replay, or eager with
 --no-graph) and prints its own line in the same form.  --decode-sweep times
@@ -33,6 +35,7 @@ import argparse
 import json
 import os
 import shutil
+import statistics
 import subprocess
 import sys
 import threading
@@ -128,7 +131,7 @@ def cpu_baseline(sub: wl.Submission, x, weights, budget_s: float) -> dict:
     same workload (whole submissions for decode; a slice of x's rows for
     prefill), scaled to the metric's unit, on every core and on one."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    threads = oracle_threads()
     streaming = sub.t <= STREAMING_MAX_T
     xs = x if streaming else x[:16]
 
@@ -161,6 +164,28 @@ def cpu_baseline(sub: wl.Submission, x, weights, budget_s: float) -> dict:
             "sample": f"{reps} {what}", "seconds": round(el, 2),
             "single_core": {"value": round(rate(reps1, el1), 4), "unit": unit, "cores": 1,
                             "sample": f"{reps1} {what}", "seconds": round(el1, 2)}}
+
+
+def oracle_threads() -> int:
+    return int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+
+
+def decode_oracle(sub: wl.Submission, x, weights) -> dict:
+    """The oracle, as it stands, over one whole decode submission on the host
+    cores: the median of 3 passes on one thread and on every core, as weight
+    GB/s (a baseline beside the kernel, not a target)."""
+    import oracle
+    out = {"kind": "oracle", "passes": 3}
+    for key, n in (("all_cores", oracle_threads()), ("single_core", 1)):
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for j, w in zip(sub.jobs, weights):
+                oracle.matmul(x, w, j.fmt, j.n_out, threads=n)
+            times.append(time.perf_counter() - t0)
+        med = statistics.median(times)
+        out[key] = {"cores": n, "ms_median": round(med * 1e3, 4), "gbs": round(sub.weight_bytes / med / 1e9, 4)}
+    return out
 
 
 def stats_device_ms(il, path: str) -> float:
@@ -414,8 +439,7 @@ def host_info() -> dict:
                 model = line.split(":", 1)[1].strip()
     except (OSError, subprocess.SubprocessError):
         pass
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
-    return {"cpu_model": model, "nproc": os.cpu_count(), "oracle_threads": threads}
+    return {"cpu_model": model, "nproc": os.cpu_count(), "oracle_threads": oracle_threads()}
 
 
 def hip_bus_id() -> str:
@@ -571,11 +595,18 @@ def time_graph(step, steps: int, warmup: int, stream, settle=None):
     return wall * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
+FLUSH_BYTES = 512 << 20  # > the 256 MiB last-level cache
+
+
 def prefill_kernel_split(il, step, calls: int, stream):
-    """Device time per call of the x -> bf16 pre-pass and of the GEMM launch,
-    from HIP events the library records on the launch stream around each of
-    them (IL_TIMING=1, eager calls)."""
+    """Device time of the x -> bf16 pre-pass and of the GEMM launch in each of
+    `calls` eager calls, from HIP events the library records on the launch
+    stream around each of them (IL_TIMING=1, which waits for every call).  A
+    512 MiB write (a fill kernel, outside the timed kernels) runs before each
+    call, so neither kernel finds the previous call's x, bf16 x or y in the
+    last-level cache.  Returns (GEMM ms, pre-pass ms) lists, one entry a call."""
     import torch
+    scratch = torch.empty((FLUSH_BYTES,), dtype=torch.uint8, device="cuda")
 
     def read():
         for line in il.il_stats().splitlines():
@@ -584,21 +615,31 @@ def prefill_kernel_split(il, step, calls: int, stream):
                 return float(f["device_ms"]), float(f["prepass_ms"]), int(f["split_calls"])
         raise RuntimeError("no prefill_gemm line in il_stats")
 
+    gemm, pre = [], []
     os.environ["IL_TIMING"] = "1"
     try:
-        d0, p0, n0 = read()
         with torch.cuda.stream(stream):
             for i in range(calls):
+                scratch.fill_(i & 0xFF)
+                d0, p0, n0 = read()
                 step(i, stream)
+                d1, p1, n1 = read()
+                if n1 - n0 != 1:
+                    raise RuntimeError("a timed prefill call was not split into pre-pass and GEMM")
+                pre.append(p1 - p0)
+                gemm.append(d1 - d0 - (p1 - p0))
         torch.cuda.synchronize()
-        d1, p1, n1 = read()
     finally:
         del os.environ["IL_TIMING"]
-    n = n1 - n0
-    if n != calls:
-        raise RuntimeError(f"{n} of {calls} timed prefill calls were split")
-    pre = (p1 - p0) / n
-    return (d1 - d0) / n - pre, pre
+    return gemm, pre
+
+
+def spread(v) -> dict:
+    """median / p10 / p90 / mean (ms) of per-call times."""
+    q = sorted(v)
+    at = lambda f: q[min(len(q) - 1, int(f * len(q)))]
+    return {"median": round(statistics.median(q), 6), "p10": round(at(0.1), 6), "p90": round(at(0.9), 6),
+            "mean": round(sum(q) / len(q), 6), "calls": len(q)}
 
 
 def input_digests(sub, x_np, weights) -> dict:
@@ -631,6 +672,9 @@ def decode_entry(il, name: str, args, stream, cache) -> dict:
     log(f"[bench] {name}: kernel {e['kernel_ms'] * 1e3:.2f} us ({achieved:.0f} GB/s, {e['frac']:.3f} of HBM), "
         f"graph {e['graph_us_per_call']:.2f} us/call, eager {e['eager_us_per_call']:.2f} us/call")
     del rig
+    if args.cpu_seconds > 0:
+        e["oracle"] = decode_oracle(sub, x_np, weights)
+        e["oracle"]["kernel_over_all_cores"] = round(achieved / e["oracle"]["all_cores"]["gbs"], 1)
     return e
 
 
@@ -642,12 +686,14 @@ def wants_calibration(il, stream, cpu) -> dict:
     host; il_wants should say yes above it.  Also whether the calibrated
     threshold says yes to every configuration."""
     sub = wl.SUBMISSIONS["c1"]
-    rig = Rig(il, sub, wl.make_x(sub), wl.make_weights(sub), 1)
+    x_np, weights = wl.make_x(sub), wl.make_weights(sub)
+    rig = Rig(il, sub, x_np, weights, 1)
     wall_ms, _ = time_eager(rig.step, 2000, 200, stream)
     del rig
     out = {"tiny_call_us": round(wall_ms * 1e3, 3), "default_min_flop": 262144}
     if cpu is None:
         return out
+    out["c1_oracle"] = decode_oracle(sub, x_np, weights)
     flops_per_s = cpu["value"] * 1e12  # the oracle on every host core (prefill sample)
     min_flop = wall_ms * 1e-3 * flops_per_s
     old = os.environ.get("IL_WANTS_MIN_FLOP")
@@ -728,7 +774,8 @@ def bench_headline(args) -> int:
     # ---- timed region: K eager calls (host validation and launches included) ----
     ms_per_step, dev_ms = time_eager(rig.step, args.steps, args.warmup, stream)
     burst(args.settle / 3)()
-    gemm_ms, pre_ms = prefill_kernel_split(il, rig.step, max(20, min(args.steps, 100)), stream)
+    gemm_calls, pre_calls = prefill_kernel_split(il, rig.step, max(20, min(args.steps, 100)), stream)
+    gemm_ms, pre_ms = statistics.median(gemm_calls), statistics.median(pre_calls)
     wall_g, dev_g = time_graph(rig.step, args.steps, args.warmup, stream, settle=burst(args.settle / 3))
     value = sub.flops / (ms_per_step * 1e-3) / 1e12
     achieved = sub.flops / (gemm_ms * 1e-3) / 1e12
@@ -754,11 +801,13 @@ def bench_headline(args) -> int:
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(name, "gemm_bf16_kernel"),
                 "kernel": "gemm_bf16_kernel", "kernel_ms": round(gemm_ms, 6), "prepass_ms": round(pre_ms, 6),
+                "kernel_ms_per_call": spread(gemm_calls), "prepass_ms_per_call": spread(pre_calls),
                 "call_device_ms": round(dev_ms, 6),
                 "call_frac": round(sub.flops / (dev_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                "timing": "kernel_ms / prepass_ms: HIP events the library records on the launch stream around "
-                          "each of the call's two kernels (IL_TIMING=1, eager); call_device_ms: HIP events on "
-                          "the launch stream around the timed burst / calls"}
+                "timing": "kernel_ms / prepass_ms: medians over eager calls of the HIP events the library "
+                          "records on the launch stream around each of the call's two kernels (IL_TIMING=1), "
+                          "with a 512 MiB scratch write before each call; call_device_ms: HIP events on the "
+                          "launch stream around the timed burst / calls"}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,

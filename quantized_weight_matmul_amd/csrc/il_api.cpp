@@ -949,7 +949,7 @@ int64_t il_stats(char *buf, int64_t cap) {
         const PathStats &p = g_stats[i];
         snprintf(line, sizeof line,
                  "%s: calls=%" PRIu64 " launches=%" PRIu64 " jobs=%" PRIu64 " weight_bytes=%" PRIu64
-                 " flops=%" PRIu64 " device_ms=%.3f split_calls=%" PRIu64 " prepass_ms=%.3f\n",
+                 " flops=%" PRIu64 " device_ms=%.6f split_calls=%" PRIu64 " prepass_ms=%.6f\n",
                  names[i], (uint64_t)p.calls, (uint64_t)p.launches, (uint64_t)p.jobs,
                  (uint64_t)p.bytes, (uint64_t)p.flops, (double)p.timed_ns / 1e6, (uint64_t)p.split_calls,
                  (double)p.prepass_ns / 1e6);
