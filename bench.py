@@ -79,8 +79,8 @@ DESCRIPTIONS = {
     "c4_t8": "Q4 verify, t=8, 2 jobs [17408, 5120]",
     "c4_t16": "Q4 verify, t=16, 2 jobs [17408, 5120]",
     "c4_t32": "Q4 verify, t=32, 2 jobs [17408, 5120]",
-    "c4_t64": "Q4 verify, t=64, 2 jobs [17408, 5120] (2 slices of 32 tokens on the matrix-core wide mode)",
-    "c4_t128": "Q4 verify, t=128, 2 jobs [17408, 5120] (4 slices of 32 tokens on the matrix-core wide mode)",
+    "c4_t64": "Q4 verify, t=64, 2 jobs [17408, 5120] (mid-size plan: 64-token units on 4 waves)",
+    "c4_t128": "Q4 verify, t=128, 2 jobs [17408, 5120] (mid-size plan: 128-token units)",
     "c5a": "bf16 prefill, t=2048, 2 jobs [4096|14336] x 4096",
     "c5b": "Q4 prefill, t=512, 1 job [14336, 4096]",
     "f4_lmhead_t1": "centroid-masked LM head, t=1: h=256, 2048 centroids, top 32, vocabulary 2^18 (bf16)",

@@ -32,6 +32,9 @@
 //   Q8/Q4 tiles: x's tile is copied into LDS the same way; the weight codes
 //     are fetched into registers two steps ahead, converted to bf16 there and
 //     written to the idle stage with the step's block scales.
+// Q8/Q4 weights at 32 < t <= 128 run the mid-size plan instead: units of
+// all t tokens by 128 weight rows, so that every weight is read and
+// converted once (Q4 at t <= 64 on 4-wave units, below).
 // Rows of 64 bf16 (8 chunks of 16 bytes) are stored with the chunk index
 // XOR-swizzled by the row, so that the fragment reads (and the staging
 // writes) are free of LDS bank conflicts.  Workgroups are mapped to units
@@ -500,7 +503,8 @@ __device__ __forceinline__ void q_unit(const GemmParams &p, uint16_t *lds, float
 }
 
 // The same BM x 128 Q8/Q4 unit for mid-size t (BM = 64 or 128 holds every
-// token), with longer K steps and a deeper pipeline: with BM small a K step
+// token; Q4 with 64 tokens and no gate/up pair runs the 4-wave unit further
+// down instead), with longer K steps and a deeper pipeline: with BM small a K step
 // of 64 has little arithmetic, and its fixed costs (the barrier, the waits,
 // all eight waves reading LDS at once) dominated.  Here a step is kMidBK =
 // 128 (four quantisation blocks; one block's codes per staging thread), every
@@ -989,6 +993,332 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_q_mid_kernel(GemmParams p) {
     }
 }
 
+// ------------------------------------------------ Q4 mid units on 4 waves
+// The Q4 mid unit of 64 tokens x 128 weight rows, laid out like the
+// matrix-core decode kernel's operands: four waves, wave w the unit's rows
+// 32 w .. 32 w + 31 as two 16-row weight tiles, 16x16x32 MFMAs (K = 32 = one
+// quantisation block).  Every K step (128 elements: one 1 KiB segment of the
+// tile-major code plane per weight tile) goes into LDS by buffer-load DMA
+// only -- x's tile, the wave's two code segments and their tiled scales --
+// so no global load returns into registers and every wait for a copy is
+// the explicit one before the step's barrier; the copies run two steps
+// ahead through three stages.  A wave reads its codes back (lane 16 g + n:
+// row n, block g of the segment), transposes dwords across the lane groups
+// so that group g holds elements 8 g .. 8 g + 7 of every block, converts
+// them to exact bf16 (16 (code - 8)) and issues one MFMA per (16-token tile,
+// weight tile, block); each block's f32 result is multiplied by its scale
+// (f16 / 16, exact) into the accumulators.  A wave reads each x fragment
+// once per step and uses it for both of its weight tiles: the LDS reads per
+// MFMA are half those of the 8-wave unit above, whose fragment reads kept
+// the LDS busy over half of the kernel's cycles; and at 75 KiB of LDS two
+// workgroups share a CU.  Like the 8-wave unit, a whole unit sums K in
+// p.n_chunks chunks and adds them in order, which is what the fixup does
+// for the split units, so a unit's result does not depend on the split.
+constexpr int kM2Waves = 4;  // waves across a unit's 128 weight rows (32 each)
+constexpr int kM2Threads = 64 * kM2Waves;
+constexpr int kM2Stages = 3;  // LDS stages: the copies of step ks + 2 land while step ks computes
+constexpr int kM2CodeBytes = kM2Waves * 2 * 1024;  // per stage: each wave's two code segments
+constexpr int kM2SclBytes = kM2Waves * 2 * 128;    // per stage: their 16 x 4 tiled scales
+// The stages are six LDS objects: x's tile of stage i, and the codes then
+// the scales of stage i.  Separate objects give each access an alias scope,
+// so the compiler waits before a read of one stage only for the copies into
+// that stage (which the step's own wait has covered), not for the copies in
+// flight into the others.
+template <int BM>
+struct M2Lds {
+    uint8_t *a[kM2Stages];  // BM x kMidBK bf16
+    uint8_t *c[kM2Stages];  // kM2CodeBytes of codes, then kM2SclBytes of scales
+};
+
+// Dword d of lane group m -> dword m of lane group d (lanes keep l % 16).
+__device__ __forceinline__ void xpose4(uint32_t &d0, uint32_t &d1, uint32_t &d2, uint32_t &d3) {
+    // lanes 32..63 of the first operand trade places with lanes 0..31 of the second
+    const auto a = __builtin_amdgcn_permlane32_swap(d0, d2, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(d1, d3, false, false);
+    // odd 16-lane rows of the first operand trade places with even rows of the second
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    d0 = c[0];
+    d1 = c[1];
+    d2 = e[0];
+    d3 = e[1];
+}
+
+// 8 Q4 codes of one dword (element 2 e in the low nibble of byte e, stored
+// as the 4-bit two's complement of code - 8) -> bf16 16 (code - 8), in order.
+__device__ __forceinline__ bf16x8 q4_dword_bf16(uint32_t d) {
+    const uint32_t lo = (d << 4) & 0xF0F0F0F0u;  // byte e: 16 (code 2 e - 8) as an int8
+    const uint32_t hi = d & 0xF0F0F0F0u;         // byte e: 16 (code 2 e + 1 - 8)
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16((float)(int8_t)(lo >> (8 * e)), (float)(int8_t)(hi >> (8 * e)));
+    return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// 16 / 4 bytes per lane from a buffer straight into LDS: lane l's bytes land
+// at dst + 16 l / 4 l (dst wave-uniform); reads past the buffer write zeros.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 4, off, 0, 0, 0);
+}
+
+template <int BM, bool CHUNKED, class Fin>
+__device__ __forceinline__ void q4_mid2_unit(const GemmParams &p, const M2Lds<BM> &lds, int m0, int n0,
+                                             const KJob &jb, int ks_lo, int ks_hi, Fin &&fin) {
+    constexpr int BKM = kMidBK;
+    constexpr int TMT = BM / 16;                                 // 16-token tiles
+    constexpr int kChunksA = BM * (BKM / 8) / kM2Threads;        // x copies per thread and step
+    constexpr int kPer = kChunksA + 3;                           // copies per thread and step
+    static_assert(BM == 64 && kChunksA >= 1 && BKM == 128 && kPer < 64, "unit shape");
+    const int n_in = p.n_in;
+    const int nb = n_in / kBlock, nb4 = (nb + 3) / 4;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // weight rows 32 wave ..
+    const int ln = lane & 15, lg = lane >> 4;
+
+    const int a_rows = min(BM, p.t - m0);
+    const int b_rows = min(128, jb.n_out - n0);
+    const uint32_t row2 = (uint32_t)n_in * 2u;
+    const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.xb + (int64_t)m0 * n_in, (uint32_t)a_rows * row2);
+    // the unit's 8 weight tiles of codes and of tiled scales (past the job's
+    // last tile, and past the last segment of the last tile, the copies read 0)
+    const __amdgpu_buffer_rsrc_t crs =
+        make_rsrc(static_cast<const uint8_t *>(jb.codes) + (n0 >> 4) * q4_plane_bytes(16, nb),
+                  (uint32_t)q4_plane_bytes(b_rows, nb));
+    const __amdgpu_buffer_rsrc_t srs =
+        make_rsrc(static_cast<const uint8_t *>(jb.scales_t) + (int64_t)(n0 >> 4) * nb4 * 64 * 2,
+                  (uint32_t)tiled_scale_count(b_rows, nb) * 2u);
+    // this wave's segment of tile j and step ks: (2 wave + j) nb4 + ks; lane
+    // 16 g + n copies row n, block g (16 bytes) of it
+    const uint32_t code_lane = ((uint32_t)ln << 6) + ((uint32_t)lg << 4);
+    const uint32_t seg0 = (uint32_t)(2 * wave) * (uint32_t)nb4;
+    // scales: lanes 0..31 copy tile 0's 128 bytes, lanes 32..63 tile 1's
+    const uint32_t scl_lane = ((seg0 + (uint32_t)(lane >> 5) * (uint32_t)nb4) << 7) + ((uint32_t)(lane & 31) << 2);
+    // x's tile: copy i of this thread is 16-byte chunk u = (wave kChunksA +
+    // i) 64 + lane of the stage, row u / 16, holding chunk (u % 16) ^ (row % 16)
+    uint32_t offa[kChunksA];
+    int ka[kChunksA];
+#pragma unroll
+    for (int i = 0; i < kChunksA; ++i) {
+        const int u = (wave * kChunksA + i) * 64 + lane, r = u >> 4;
+        ka[i] = ((u & 15) ^ (r & 15)) * 8;
+        offa[i] = (uint32_t)r * row2 + (uint32_t)ka[i] * 2u;
+    }
+    auto issue = [&](int ks, auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        uint8_t *sa = lds.a[ST];
+        const int k0 = ks * BKM;
+        // (a select, not a branch around two sets of copies: copies issued on
+        // two paths make the compiler's wait counts after the join conservative)
+#pragma unroll
+        for (int i = 0; i < kChunksA; ++i)
+            lds_dma16(ars, sa + (wave * kChunksA + i) * 1024, k0 + ka[i] < n_in ? offa[i] + (uint32_t)k0 * 2u : kOut);
+        uint8_t *cb = lds.c[ST] + wave * 2048;
+        lds_dma16(crs, cb, ((seg0 + (uint32_t)ks) << 10) + code_lane);
+        lds_dma16(crs, cb + 1024, ((seg0 + (uint32_t)nb4 + (uint32_t)ks) << 10) + code_lane);
+        lds_dma4(srs, lds.c[ST] + kM2CodeBytes + wave * 256, scl_lane + ((uint32_t)ks << 7));
+    };
+
+    f32x4 acc[TMT][2], tot[CHUNKED ? TMT : 1][CHUNKED ? 2 : 1];
+#pragma unroll
+    for (int i = 0; i < TMT; ++i) acc[i][0] = acc[i][1] = (f32x4){};
+    if constexpr (CHUNKED) {
+#pragma unroll
+        for (int i = 0; i < TMT; ++i) tot[i][0] = tot[i][1] = (f32x4){};
+    }
+    int chunk = 0;
+    int next_fold = CHUNKED ? p.chunk_hi[0] : 0;
+
+    auto compute = [&](auto st_c) {
+        constexpr int ST = decltype(st_c)::value;
+        const uint16_t *As = reinterpret_cast<const uint16_t *>(lds.a[ST]);
+        const uint4 *cw = reinterpret_cast<const uint4 *>(lds.c[ST] + wave * 2048);
+        uint4 c0 = cw[lane], c1 = cw[64 + lane];
+        const uint2 *sw = reinterpret_cast<const uint2 *>(lds.c[ST] + kM2CodeBytes + wave * 256);
+        const uint2 h0 = sw[ln], h1 = sw[16 + ln];  // row n's four block scales of each tile (f16)
+        xpose4(c0.x, c0.y, c0.z, c0.w);
+        xpose4(c1.x, c1.y, c1.z, c1.w);
+        const uint32_t cd[2][4] = {{c0.x, c0.y, c0.z, c0.w}, {c1.x, c1.y, c1.z, c1.w}};
+        const uint32_t hd[2][2] = {{h0.x, h0.y}, {h1.x, h1.y}};
+        f32x4 part[2][TMT][2];
+        float sc[2][2];
+        // block b: the MFMAs into part[b & 1], then block b - 1's scaling,
+        // whose MFMA results are ready by then
+        auto scale_in = [&](int pb) {
+#pragma unroll
+            for (int i = 0; i < TMT; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(sc[pb][j], part[pb][i][j][e], acc[i][j][e]);
+        };
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const bf16x8 bq0 = q4_dword_bf16(cd[0][b]), bq1 = q4_dword_bf16(cd[1][b]);
+#pragma unroll
+            for (int i = 0; i < TMT; ++i) {
+                const int r = 16 * i + ln;
+                const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(As + r * BKM + (((4 * b + lg) ^ ln) << 3));
+                part[b & 1][i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, bq0, (f32x4){}, 0, 0, 0);
+                part[b & 1][i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, bq1, (f32x4){}, 0, 0, 0);
+            }
+            if (b > 0) scale_in((b - 1) & 1);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t h = hd[j][b >> 1] >> ((b & 1) * 16);
+                sc[b & 1][j] = (float)__builtin_bit_cast(_Float16, (uint16_t)h) * 0.0625f;  // codes carry * 16; exact
+            }
+        }
+        scale_in(1);
+    };
+
+    // step ks = ks_lo + 3 q + I uses stage I; the loop is unrolled three
+    // times so that every stage offset is a constant (with run-time offsets
+    // the compiler cannot tell the copies' LDS range from the one a step
+    // reads, and waits for every copy in flight before the first read)
+    auto step = [&](int ks, auto i_c) {
+        constexpr int I = decltype(i_c)::value;
+        wait_vmcnt<kPer>();  // this step's copies have landed (the next step's may not)
+        lds_barrier();       // ... every wave's; and every wave is done with step ks - 1
+        issue(ks + 2, std::integral_constant<int, (I + 2) % kM2Stages>{});  // into step ks - 1's stage
+        compute(i_c);
+        if constexpr (CHUNKED) {
+            if (ks + 1 == next_fold) {  // the last step of chunk `chunk`
+#pragma unroll
+                for (int i = 0; i < TMT; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        tot[i][j] += acc[i][j];
+                        acc[i][j] = (f32x4){};
+                    }
+                ++chunk;
+                next_fold = chunk < p.n_chunks ? p.chunk_hi[chunk] : -1;
+            }
+        }
+    };
+    issue(ks_lo, std::integral_constant<int, 0>{});
+    issue(ks_lo + 1, std::integral_constant<int, 1>{});
+    // (a partial last round leaves the loop rather than going round to its
+    // head, so that the head is reached from one place in the loop only)
+    for (int ks = ks_lo;; ks += kM2Stages) {
+        bool more = true;
+        unrolled_while(
+            [&](auto i_c) {
+                if (ks + decltype(i_c)::value >= ks_hi) return more = false;
+                step(ks + decltype(i_c)::value, i_c);
+                return true;
+            },
+            std::make_integer_sequence<int, kM2Stages>{});
+        if (!more) break;
+    }
+    wait_vmcnt<0>();  // the copies past the range write LDS; nothing may be in flight at the end
+    if constexpr (CHUNKED) fin(tot, wave, lane);
+    else fin(acc, wave, lane);
+}
+
+// y from a 4-wave unit: tile (i, j) of wave w, lane l holds rows
+// m0 + 16 i + 4 (l / 16) + e of column n0 + 32 w + 16 j + l % 16.
+template <int BM>
+struct StoreY2 {
+    const GemmParams &p;
+    const KJob &jb;
+    int m0, n0;
+    template <int TMT>
+    __device__ __forceinline__ void operator()(const f32x4 (&acc)[TMT][2], int wave, int lane) const {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + 32 * wave + 16 * j + (lane & 15);
+            if (col >= jb.n_out) continue;
+#pragma unroll
+            for (int i = 0; i < TMT; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = m0 + 16 * i + 4 * (lane >> 4) + e;
+                    if (row < p.t) jb.y[(int64_t)row * jb.n_out + col] = acc[i][j][e];
+                }
+        }
+    }
+};
+
+// A split 4-wave unit's chunk sum: float4 ((wave * TMT + i) * 2 + j) * 64 + lane
+// of the chunk's BM * 128 floats holds acc[i][j] of that wave and lane.
+template <int BM>
+struct PartFin2 {
+    const GemmParams &p;
+    int su, chunk;
+    template <int TMT>
+    __device__ __forceinline__ void operator()(const f32x4 (&acc)[TMT][2], int wave, int lane) const {
+        float4 *mine = reinterpret_cast<float4 *>(p.part) + ((int64_t)su * p.n_chunks + chunk) * (BM * 128 / 4) +
+                       (wave * TMT * 2) * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < TMT; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                mine[(i * 2 + j) * 64] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    }
+};
+
+// The split 4-wave units' chunk sums added in chunk order from zero, as a
+// whole unit adds its chunks, and stored as StoreY2 would have.  One thread
+// per float4 of a chunk sum; one 64-thread workgroup per (split unit, wave,
+// i, j).
+template <int BM>
+__global__ __launch_bounds__(64) void mid2_fixup_kernel(GemmParams p) {
+    constexpr int TMT = BM / 16, kGroups = TMT * 2, kMaxChunks = 16;
+    const int lane = threadIdx.x;
+    int g = blockIdx.x;
+    const int grp = g % kGroups;
+    g /= kGroups;
+    const int wave = g % kM2Waves, su = g / kM2Waves;
+    const int i = grp >> 1, j = grp & 1;
+    Place pl;
+    if (!place<false>(p, p.n_big + su, big_cols(FMT_Q4, false), 0, 0, big_cols(FMT_Q4, false), pl)) return;
+    const float4 *src = reinterpret_cast<const float4 *>(p.part) + (int64_t)su * p.n_chunks * (BM * 128 / 4) +
+                        (wave * kGroups + grp) * 64 + lane;
+    float4 v[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+        if (c < p.n_chunks) v[c] = src[(int64_t)c * (BM * 128 / 4)];
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+        if (c < p.n_chunks) sum[0] += v[c].x, sum[1] += v[c].y, sum[2] += v[c].z, sum[3] += v[c].w;
+    const KJob &jb = p.job[pl.j];
+    const int col = pl.n0 + 32 * wave + 16 * j + (lane & 15);
+    if (col >= jb.n_out) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int row = pl.m0 + 16 * i + 4 * (lane >> 4) + e;
+        if (row < p.t) jb.y[(int64_t)row * jb.n_out + col] = sum[e];
+    }
+}
+
+template <int BM>
+__global__ __launch_bounds__(kM2Threads, 2) void gemm_q4_mid2_kernel(GemmParams p) {
+    constexpr int kA = BM * kMidBK * 2, kC = kM2CodeBytes + kM2SclBytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t a0[kA], a1[kA], a2[kA];
+    __shared__ __attribute__((aligned(1024))) uint8_t c0[kC], c1[kC], c2[kC];
+    static_assert(kM2Stages == 3, "three stages");
+    const M2Lds<BM> lds{{a0, a1, a2}, {c0, c1, c2}};
+    int u;
+    const int kind = unit_of(p, &u);
+    if (kind < 0) return;
+    constexpr int cols = big_cols(FMT_Q4, false);
+    Place pl;
+    if (kind == 0) {
+        if (!place<false>(p, u, cols, 0, 0, cols, pl)) return;
+        q4_mid2_unit<BM, true>(p, lds, pl.m0, pl.n0, p.job[pl.j], 0, p.nk, StoreY2<BM>{p, p.job[pl.j], pl.m0, pl.n0});
+    } else {
+        const int su = u / p.n_chunks, c = u - su * p.n_chunks;
+        if (!place<false>(p, p.n_big + su, cols, 0, 0, cols, pl)) return;
+        const int lo = c ? p.chunk_hi[c - 1] : 0, hi = p.chunk_hi[c];
+        q4_mid2_unit<BM, false>(p, lds, pl.m0, pl.n0, p.job[pl.j], lo, hi, PartFin2<BM>{p, su, c});
+    }
+}
+
 // --------------------------------------------------------------- bf16 units
 // A BM x BN tile of bf16 weights on 8 waves (WM x WN grid); both operand
 // tiles copied from L2 into LDS by the load unit.  A stage holds the A tile
@@ -1212,7 +1542,12 @@ hipError_t launch_mid(GemmParams p, int mid_bm, int cu_count, hipStream_t s) {
     const int groups = mid_bm == 64 ? 4 : (GLU ? 4 : 8);
     const dim3 fix((unsigned)(n_split * kWaves * groups));
     if (mid_bm == 64) {
-        if constexpr (!GLU) {
+        if constexpr (FMT == FMT_Q4 && !GLU) {
+            // the 4-wave units; their fixup: (split unit, wave, tile pair)
+            hipLaunchKernelGGL((gemm_q4_mid2_kernel<64>), grid, dim3(kM2Threads), 0, s, p);
+            if (n_split)
+                hipLaunchKernelGGL((mid2_fixup_kernel<64>), dim3((unsigned)(n_split * kM2Waves * 8)), dim3(64), 0, s, p);
+        } else if constexpr (!GLU) {
             hipLaunchKernelGGL((gemm_q_mid_kernel<FMT, 64, false>), grid, dim3(kThreads), 0, s, p);
             if (n_split) hipLaunchKernelGGL((mid_fixup_kernel<64, false>), fix, dim3(64), 0, s, p);
         } else {
