@@ -87,6 +87,8 @@ DESCRIPTIONS = {
     "f3_q8_t1": "fused gate/up + GELU, Q8, t=1, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T)",
     "f3_q4_t1": "fused gate/up + GELU, Q4, t=1, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T)",
     "f3_bf16_t1": "fused gate/up + GELU, bf16, t=1, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T)",
+    "f3_q8_t512": "fused gate/up + GELU, Q8, t=512, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T) (prefill GEMM)",
+    "f3_q4_t512": "fused gate/up + GELU, Q4, t=512, 2 x [14336, 4096] -> y = GELU(x G^T) * (x U^T) (prefill GEMM)",
 }
 
 

@@ -320,7 +320,11 @@ __device__ __forceinline__ void q_unit(const GemmParams &p, uint16_t *lds, float
     // codes EPT qh .. EPT qh + EPT - 1 of the step (half of block qh / 2)
     const int qr = tid / TPR, qh = tid % TPR;
     const int qkey = swz_key(qr);
-    const bool up = GLU && ((qr >> 5) & 1);
+    // a wave stages 16 B rows, inside one 32-row group: whether they are
+    // gate or up rows is the same for the whole wave (taken from the wave
+    // index, so that the descriptor choice is scalar)
+    static_assert(64 / TPR == 16, "a wave stages 16 rows");
+    const bool up = GLU && ((wave >> 1) & 1);
     const int wr = GLU ? (qr >> 6) * 32 + (qr & 31) : qr;
     const __amdgpu_buffer_rsrc_t crs = up ? brs2 : brs, srs = up ? bss2 : bss;
     // two register sets: the codes of step k are fetched into set k & 1 two
@@ -583,7 +587,10 @@ __device__ __forceinline__ void q_mid_unit(const GemmParams &p, uint16_t *lds, i
     // block (block qh of the step) of row qr
     const int qr = tid / TPR, qh = tid % TPR;
     const int qkey = qr & 15;
-    const bool up = GLU && ((qr >> 5) & 1);
+    // gate or up rows: the same for the whole wave (16 rows of one 32-row
+    // group), taken from the wave index so that the descriptor choice is scalar
+    static_assert(64 / TPR == 16, "a wave stages 16 rows");
+    const bool up = GLU && ((wave >> 1) & 1);
     const int wr = GLU ? (qr >> 6) * 32 + (qr & 31) : qr;
     const __amdgpu_buffer_rsrc_t crs = up ? brs2 : brs, srs = up ? bss2 : bss;
     uint4 cq[D][FMT == FMT_Q8 ? 2 : 1];

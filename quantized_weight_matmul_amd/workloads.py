@@ -115,11 +115,14 @@ QUANTIZE = {
 
 
 # Fused gate/up + GELU workloads (il_matmul_gelu_mul): the gate/up pair of the
-# Q8 decode shape, and the same pair as Q4 and bf16; t = 1 (one drafted token).
+# Q8 decode shape, and the same pair as Q4 and bf16; t = 1 (one drafted token),
+# and the Q8 / Q4 pair at t = 512 (the prefill GEMM's gate/up mode).
 GELU_MUL = {
     "f3_q8_t1": (Q8, 14336, 4096, 1, 7),  # fmt, n_out, n_in, t, cfg
     "f3_q4_t1": (Q4, 14336, 4096, 1, 7),
     "f3_bf16_t1": (BF16, 14336, 4096, 1, 7),
+    "f3_q8_t512": (Q8, 14336, 4096, 512, 7),
+    "f3_q4_t512": (Q4, 14336, 4096, 512, 7),
 }
 
 

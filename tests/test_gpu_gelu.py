@@ -79,7 +79,7 @@ def test_gelu_mul_matches_oracle(fmt, t, path, monkeypatch):
         f"fused differs from GELU(g) * u of the unfused kernels: worst {np.max(err / (allow + 1e-300)):.3g} x allowed"
 
 
-@pytest.mark.parametrize("name", ["f3_q8_t1", "f3_q4_t1", "f3_bf16_t1"])
+@pytest.mark.parametrize("name", ["f3_q8_t1", "f3_q4_t1", "f3_bf16_t1", "f3_q8_t512", "f3_q4_t512"])
 def test_gelu_mul_workload_sampled(name):
     """The measured workloads at full size: a band of rows at the start, the
     middle and the end checked against the oracle."""
