@@ -968,7 +968,7 @@ def main() -> int:
         return decode_sweep(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run it with --gpus 1.", file=sys.stderr)
         return 2
     import torch
